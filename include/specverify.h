@@ -1,0 +1,163 @@
+/*
+ * specverify.h - C ABI of the MI355X (gfx950) batched speculative-sampling
+ * verifier, the verify half of one speculative-decoding round.
+ *
+ * What it computes (sources cited by page title and section):
+ *  - bloss0m.com, "Speculative Decoding：用小模型打草稿、大模型一次驗…",
+ *    section "技術機制 / Technical mechanism": speculative sampling (paper
+ *    §2.3) and Algorithm 1 - each drafted token x_i is kept when
+ *    r_i <= p_i(x_i) / q_i(x_i); the scan stops at the first rejection; a
+ *    replacement is drawn from norm(max(0, p - q)) at that position, or a bonus
+ *    token from p_{gamma+1} when every draft was kept.
+ *  - blog.vllbc.top, "Speculative Decoding：draft 先猜，target 一次验证":
+ *    the same Algorithm 1 steps; the vLLM verification path, which scans a
+ *    flattened batch through cu_num_draft_tokens and returns accepted +
+ *    recovered + bonus tokens; the note on paper §2.2 (temperature folds into
+ *    p and q, a greedy draft is a one-hot q).
+ *  - timinsight.com, "Speculative Decoding 實作指南：基準、驗證與取捨",
+ *    section "Step 2": target probabilities are a softmax of the target
+ *    logits; when the residual mass is not above 1e-8 the replacement is drawn
+ *    from p instead.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller. The library
+ *    keeps no state, never allocates, never synchronises; work is enqueued on
+ *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
+ *    outputs are valid once that stream has completed the work.
+ *  - Target temperature: p = softmax(logits / T) for T > 0; T == 0 means
+ *    argmax decoding (p one-hot at the argmax, lowest index on ties).
+ *  - Accept test, in product form: x is kept iff p(x) > 0 and u * q(x) <= p(x).
+ *  - Uniforms: a request with g drafts owns g + 1 uniforms in (0, 1]: entries
+ *    0..g-1 are the accept uniforms, entry g is the single sample uniform,
+ *    used for the emitted replacement or bonus token.
+ *  - Sampling is by inverse CDF in ascending token order: the emitted token is
+ *    the smallest k with C[k] >= u * C[V-1], C the running sum of the
+ *    (unnormalised) weights.
+ *  - Results equal exact-arithmetic results. Every decision taken in fp32 is
+ *    checked against a rigorous error bound; rows where a decision is within
+ *    the bound are recomputed in fp64 before anything is written.
+ *  - Device-side preconditions (not checked, cannot be reported without a
+ *    sync; violating them never makes a kernel read or write out of bounds):
+ *    draft tokens in [0, V) (an out-of-range token is rejected with p(x) = 0);
+ *    uniforms in (0, 1]; logits finite or -inf with at least one finite value
+ *    per row (no NaN); q finite and >= 0; cu_num_draft_tokens non-decreasing
+ *    from 0 to num_draft_tokens.
+ *  - Errors found on the host return a negative status and launch nothing.
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the target logits. Draft probabilities are always fp32. */
+enum sv_dtype { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 };
+
+/* Status codes. */
+enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad temperature or flags */
+  SV_ERR_UNSUPPORTED = -2,      /* unknown dtype, vocab_size above SV_MAX_VOCAB */
+  SV_ERR_LAUNCH = -3,           /* a kernel launch failed (hipGetLastError) */
+  SV_ERR_WORKSPACE = -4         /* workspace missing or smaller than required */
+};
+
+/* Largest supported vocabulary. */
+#define SV_MAX_VOCAB (1 << 21)
+
+/* flags for spec_verify_probs / spec_verify_ragged */
+#define SV_FLAG_EXACT 0x1u         /* take every row through the fp64 path (reference / testing) */
+#define SV_FLAG_ALL_RESIDUALS 0x2u /* draw the replacement token of every draft row, accepted or not */
+
+/* Workspace layout (documented for diagnostics): one 8-byte record per target
+ * row, {int32 token, uint32 row_flags}, at offset 0. row_flags bits: */
+#define SV_ROW_ACCEPTED 0x1u  /* the row's own accept test passed */
+#define SV_ROW_EXACT 0x2u     /* the row was recomputed on the fp64 path */
+#define SV_ROW_RESIDUAL 0x4u  /* the row's replacement token was drawn (q read in full) */
+#define SV_ROW_FALLBACK 0x8u  /* residual mass <= 1e-8: the replacement was drawn from p */
+
+/* Bytes of workspace needed for `num_target_rows` target rows (dense:
+ * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests).
+ * Returns 0 for a negative argument. */
+size_t spec_verify_workspace_size(int64_t num_target_rows);
+
+/* Static, human-readable text for a status code. */
+const char* spec_verify_status_string(int status);
+
+/* Library ABI version (currently 1). */
+int spec_verify_version(void);
+
+/*
+ * spec_verify_probs - dense batch, rejection-sampling verification.
+ *
+ *  target_logits  [B, gamma+1, V] contiguous, dtype `logits_dtype`; row
+ *                 gamma of each request is its bonus row.
+ *  draft_probs    [B, gamma, V] fp32 contiguous, or NULL for one-hot drafts
+ *                 (q = onehot(x): accept with probability p(x), residual = p
+ *                 without x).
+ *  draft_tokens   [B, gamma] int64.
+ *  uniforms       [B, gamma+1] fp32 (see the uniform convention above).
+ *  num_requests B >= 0, gamma >= 0, 1 <= vocab_size V <= SV_MAX_VOCAB.
+ *  temperature    T >= 0 and finite; T == 0 runs the greedy kernel
+ *                 (draft_probs and uniforms are then not read).
+ *  flags          SV_FLAG_* bits.
+ *  out_tokens     [B, gamma+1] int64: x_1..x_n, then the drawn token, then -1.
+ *  num_accepted   [B] int32: n, the number of accepted drafts.
+ *  row_stats      [B, gamma+1, 4] fp32 or NULL: per target row
+ *                 {max(l/T), ln sum exp(l/T - max), p(x), R}; R = sum
+ *                 max(0, p - q) for draft rows; p(x) = NaN and R = 1 for bonus
+ *                 rows. Requires T > 0. Implies SV_FLAG_ALL_RESIDUALS.
+ *  workspace      device scratch of at least
+ *                 spec_verify_workspace_size(B * (gamma + 1)) bytes, 8-byte
+ *                 aligned; contents on entry are ignored.
+ */
+int spec_verify_probs(const void* target_logits, int logits_dtype, const float* draft_probs,
+                      const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
+                      int32_t gamma, int32_t vocab_size, float temperature, uint32_t flags,
+                      int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_greedy - dense batch, argmax verification (temperature 0; the
+ * pages' temp=0 decoding, bloss0m.com Table 2). A draft is kept while it
+ * equals the argmax of its target row (lowest index on ties); the emitted
+ * token is the argmax of the first mismatching row, or of the bonus row.
+ * Shapes and outputs as in spec_verify_probs; no q, no uniforms.
+ */
+int spec_verify_greedy(const void* target_logits, int logits_dtype, const int64_t* draft_tokens,
+                       int32_t num_requests, int32_t gamma, int32_t vocab_size,
+                       int64_t* out_tokens, int32_t* num_accepted, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_ragged - flattened batch with per-request draft counts (the
+ * vLLM verification path on blog.vllbc.top scans requests through
+ * cu_num_draft_tokens; the layout below is this library's own).
+ *
+ *  cu_num_draft_tokens [B+1] int32 device: cu[0] = 0, request b owns draft
+ *                 rows cu[b]..cu[b+1]-1 and target rows cu[b]+b..cu[b+1]+b
+ *                 (the last is its bonus row); g_b = cu[b+1]-cu[b] >= 0.
+ *  target_logits  [num_draft_tokens + B, V].
+ *  draft_probs    [num_draft_tokens, V] fp32, or NULL (one-hot drafts).
+ *  draft_tokens   [num_draft_tokens] int64.
+ *  uniforms       [num_draft_tokens + B] fp32 in target-row layout.
+ *  out_tokens     [num_draft_tokens + B] int64, target-row layout, -1 padded.
+ *  num_accepted   [B] int32.  row_stats [num_draft_tokens + B, 4] or NULL.
+ *  Temperature 0 runs the greedy kernel on the same layout.
+ */
+int spec_verify_ragged(const void* target_logits, int logits_dtype, const float* draft_probs,
+                       const int64_t* draft_tokens, const int32_t* cu_num_draft_tokens,
+                       const float* uniforms, int32_t num_requests, int32_t num_draft_tokens,
+                       int32_t vocab_size, float temperature, uint32_t flags,
+                       int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

@@ -1,0 +1,200 @@
+"""ctypes binding of ``libspecverify.so`` (C ABI in include/specverify.h).
+
+Argument marshalling only: tensors are checked for device, dtype and
+contiguity, their data pointers and the current HIP stream are handed to the
+library, and a nonzero status raises. Every step of the verification runs in
+the library's kernels; there is no other path. PyTorch supplies device memory
+(outputs, workspace) and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+SV_FLAG_EXACT = 0x1
+SV_FLAG_ALL_RESIDUALS = 0x2
+SV_ROW_ACCEPTED = 0x1
+SV_ROW_EXACT = 0x2
+SV_ROW_RESIDUAL = 0x4
+SV_ROW_FALLBACK = 0x8
+
+EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
+           "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged")
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed with status {status}: {status_string(status)}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
+                                  ctypes.c_float, ctypes.c_size_t)
+    lib.spec_verify_workspace_size.argtypes = [i64]
+    lib.spec_verify_workspace_size.restype = sz
+    lib.spec_verify_status_string.argtypes = [ctypes.c_int]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_version.argtypes = []
+    lib.spec_verify_version.restype = ctypes.c_int
+    lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f32, u32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_probs.restype = ctypes.c_int
+    lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.restype = ctypes.c_int
+    lib.spec_verify_ragged.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, u32, vp, vp, vp, vp,
+                                       sz, vp]
+    lib.spec_verify_ragged.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().spec_verify_status_string(int(status)).decode()
+
+
+def workspace_size(num_target_rows: int) -> int:
+    return int(load().spec_verify_workspace_size(int(num_target_rows)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    raise TypeError(f"target logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(rows, device, workspace):
+    need = workspace_size(rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, flags=0, row_stats=False,
+                 workspace=None, stream=None):
+    """logits [B, g+1, V] f32/bf16; draft_probs [B, g, V] f32 or None (one-hot);
+    draft_tokens [B, g] int64; uniforms [B, g+1] f32. Returns
+    (out_tokens [B, g+1] int64, num_accepted [B] int32, row_stats or None, workspace)."""
+    lib = load()
+    dev = logits.device
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, g1, V = logits.shape
+    g = g1 - 1
+    _check(logits, "logits", device=dev)
+    _check(draft_probs, "draft_probs", torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    _check(uniforms, "uniforms", torch.float32, dev)
+    if draft_probs is not None and tuple(draft_probs.shape) != (B, g, V):
+        raise ValueError("draft_probs must be [B, gamma, V]")
+    if tuple(draft_tokens.shape) != (B, g) or tuple(uniforms.shape) != (B, g1):
+        raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
+    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
+    workspace, need = _workspace(B * g1, dev, workspace)
+    rc = lib.spec_verify_probs(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                               _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(out), _ptr(nacc),
+                               _ptr(stats), _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_probs")
+    return out, nacc, stats, workspace
+
+
+def verify_greedy(logits, draft_tokens, workspace=None, stream=None):
+    """Argmax verification. Returns (out_tokens, num_accepted, workspace)."""
+    lib = load()
+    dev = logits.device
+    B, g1, V = logits.shape
+    g = g1 - 1
+    _check(logits, "logits", device=dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    if tuple(draft_tokens.shape) != (B, g):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    workspace, need = _workspace(B * g1, dev, workspace)
+    rc = lib.spec_verify_greedy(_ptr(logits), _dtype_code(logits), _ptr(draft_tokens), B, g, V, _ptr(out),
+                                _ptr(nacc), _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_greedy")
+    return out, nacc, workspace
+
+
+def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms, temperature, flags=0,
+                  row_stats=False, workspace=None, stream=None):
+    """logits [T+B, V]; draft_probs [T, V] or None; draft_tokens [T] int64;
+    cu_num_draft_tokens [B+1] int32; uniforms [T+B] f32. Returns
+    (out_tokens [T+B], num_accepted [B], row_stats or None, workspace)."""
+    lib = load()
+    dev = logits.device
+    nb = cu_num_draft_tokens.numel() - 1
+    T = draft_tokens.numel()
+    V = logits.shape[-1]
+    _check(logits, "logits", device=dev)
+    _check(draft_probs, "draft_probs", torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    _check(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, dev)
+    _check(uniforms, "uniforms", torch.float32, dev)
+    if tuple(logits.shape) != (T + nb, V) or uniforms.numel() != T + nb:
+        raise ValueError("logits must be [T+B, V] and uniforms [T+B]")
+    if draft_probs is not None and tuple(draft_probs.shape) != (T, V):
+        raise ValueError("draft_probs must be [T, V]")
+    out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
+    nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
+    stats = torch.empty((T + nb, 4), dtype=torch.float32, device=dev) if row_stats else None
+    workspace, need = _workspace(T + nb, dev, workspace)
+    rc = lib.spec_verify_ragged(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature), int(flags),
+                                _ptr(out), _ptr(nacc), _ptr(stats), _ptr(workspace), workspace.numel(),
+                                _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_ragged")
+    return out, nacc, stats, workspace
+
+
+def row_records(workspace, num_target_rows):
+    """Diagnostics: the per-row {token, row_flags} records the last call left
+    in `workspace` (int32 [rows, 2])."""
+    return workspace[: num_target_rows * 8].view(torch.int32).view(num_target_rows, 2)

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/specverify.h declares,
+and reject bad arguments with the documented status before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rejection_sampling_verifier_spec_amd import api
+from rejection_sampling_verifier_spec_amd.build import LIB, build_library
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        build_library()
+    return api.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_workspace_size",
+              "spec_verify_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(declared_functions()) == sorted(api.EXPORTS)
+    assert lib.spec_verify_version() == 1
+
+
+def test_status_strings(lib):
+    assert api.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert api.status_string(s) != "unknown status"
+    assert api.status_string(7) == "unknown status"
+
+
+def test_workspace_size(lib):
+    assert api.workspace_size(0) == 0
+    assert api.workspace_size(1) == 256
+    assert api.workspace_size(2048) == 2048 * 8
+    assert lib.spec_verify_workspace_size(-1) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation or has B == 0
+
+
+def probs(lib, **kw):
+    a = dict(logits=FAKE, dtype=1, q=FAKE, x=FAKE, u=FAKE, B=2, g=3, V=100, T=1.0, flags=0, out=FAKE, nacc=FAKE,
+             stats=None, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.spec_verify_probs(a["logits"], a["dtype"], a["q"], a["x"], a["u"], a["B"], a["g"], a["V"], a["T"],
+                                 a["flags"], a["out"], a["nacc"], a["stats"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1),
+    (dict(g=-1), -1),
+    (dict(V=0), -1),
+    (dict(V=(1 << 21) + 1), -2),
+    (dict(dtype=7), -2),
+    (dict(T=-0.5), -1),
+    (dict(T=float("nan")), -1),
+    (dict(T=float("inf")), -1),
+    (dict(flags=0x10), -1),
+    (dict(logits=None), -1),
+    (dict(out=None), -1),
+    (dict(nacc=None), -1),
+    (dict(x=None), -1),
+    (dict(u=None), -1),
+    (dict(stats=FAKE, T=0.0), -1),
+    (dict(ws=None), -4),
+    (dict(wsb=8 * 7), -4),
+    (dict(ws=ctypes.c_void_p(0x1004)), -4),
+    (dict(B=0), 0),
+])
+def test_probs_argument_validation(lib, kw, status):
+    assert probs(lib, **kw) == status
+
+
+def test_greedy_and_ragged_validation(lib):
+    g = lib.spec_verify_greedy
+    assert g(FAKE, 1, FAKE, -1, 2, 10, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert g(FAKE, 3, FAKE, 1, 2, 10, FAKE, FAKE, FAKE, 1 << 20, None) == -2
+    assert g(FAKE, 1, FAKE, 4, 2, 10, FAKE, FAKE, FAKE, 8, None) == -4
+    assert g(FAKE, 1, FAKE, 0, 2, 10, FAKE, FAKE, FAKE, 0, None) == 0
+    r = lib.spec_verify_ragged
+    # missing cu offsets
+    assert r(FAKE, 1, FAKE, FAKE, None, FAKE, 2, 5, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, -1, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "LIB_PATH", "/nonexistent/libspecverify.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        api.load()

@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs. See tests/gpu_helpers.py for the comparison rule."""
+
+import numpy as np
+import pytest
+import torch
+
+from rejection_sampling_verifier_spec_amd import api
+from rejection_sampling_verifier_spec_amd.workloads import (RECIPES, dense_as_ragged, lattice_uniforms,
+                                                            make_dense_custom, make_workload)
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = range(5)
+
+
+def _gh():
+    import gpu_helpers  # noqa: E402  (imported lazily: needs torch.cuda)
+    return gpu_helpers
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    api.load()
+
+
+def sampled(n_total, k):
+    return sorted(set(np.linspace(0, n_total - 1, k).round().astype(int).tolist()))
+
+
+# ------------------------------------------------------------ recipe workloads
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_tiny(seed):
+    gh = _gh()
+    w = make_workload("tiny", seed)
+    gh.compare(w, gh.run_gpu(w), label=f"tiny s{seed}")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"tiny stats s{seed}")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_dense_f32_small(seed):
+    gh = _gh()
+    w = make_workload("dense_f32", seed, B=8)
+    gh.compare(w, gh.run_gpu(w), label=f"dense_f32 B8 s{seed}")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"dense_f32 B8 stats s{seed}")
+
+
+def test_dense_f32_full():
+    gh = _gh()
+    w = make_workload("dense_f32", 0)
+    gh.compare(w, gh.run_gpu(w), label="dense_f32 full")
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_peaked_bf16_small(seed):
+    gh = _gh()
+    w = make_workload("peaked_bf16", seed, B=6)
+    gh.compare(w, gh.run_gpu(w), label=f"peaked B6 s{seed}")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"peaked B6 stats s{seed}")
+
+
+def test_peaked_bf16_full_sampled():
+    gh = _gh()
+    w = make_workload("peaked_bf16", 0)
+    gpu = gh.run_gpu(w)
+    gh.compare(w, gpu, reqs=sampled(w["B"], 24), label="peaked full")
+    # properties at full size: accepted prefix equals the drafts, padding, ranges
+    out, nacc, _, _ = gpu
+    g = w["gamma"]
+    for b in range(w["B"]):
+        n = int(nacc[b])
+        assert 0 <= n <= g
+        assert np.array_equal(out[b, :n], w["draft_tokens"][b, :n])
+        assert 0 <= out[b, n] < w["V"] and np.all(out[b, n + 1:] == -1)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_ragged_small(seed):
+    gh = _gh()
+    w = make_workload("ragged_bf16", seed, B=12)
+    gh.compare(w, gh.run_gpu(w), label=f"ragged B12 s{seed}")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"ragged B12 stats s{seed}")
+
+
+def test_ragged_full_sampled():
+    gh = _gh()
+    w = make_workload("ragged_bf16", 0)
+    gpu = gh.run_gpu(w)
+    gh.compare(w, gpu, reqs=sampled(w["B"], 24), label="ragged full")
+    out, nacc, _, _ = gpu
+    cu = w["cu"]
+    for b in range(w["B"]):
+        g, n, t0 = int(cu[b + 1] - cu[b]), int(nacc[b]), int(cu[b]) + b
+        assert 0 <= n <= g
+        assert np.array_equal(out[t0:t0 + n], w["draft_tokens"][cu[b]:cu[b] + n])
+        assert 0 <= out[t0 + n] < w["V"] and np.all(out[t0 + n + 1:t0 + g + 1] == -1)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_greedy_small(seed):
+    gh = _gh()
+    w = make_workload("greedy_bf16", seed, B=16)
+    gh.compare(w, gh.run_gpu(w), label=f"greedy B16 s{seed}")
+
+
+def test_greedy_full_all_requests():
+    gh = _gh()
+    w = make_workload("greedy_bf16", 0)
+    out, nacc, _, _ = gh.run_gpu(w)
+    import oracle
+    ro, rn = oracle.verify_greedy(w["logits"], w["draft_tokens"])
+    assert np.array_equal(out, ro) and np.array_equal(nacc, rn)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_onehot_small(seed):
+    gh = _gh()
+    w = make_workload("onehot_bf16", seed, B=16)
+    gh.compare(w, gh.run_gpu(w), label=f"onehot B16 s{seed}")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"onehot B16 stats s{seed}")
+
+
+def test_onehot_full_sampled():
+    gh = _gh()
+    w = make_workload("onehot_bf16", 0)
+    gh.compare(w, gh.run_gpu(w), reqs=sampled(w["B"], 24), label="onehot full")
+
+
+# ------------------------------------------------------------ modes and flags
+
+
+@pytest.mark.parametrize("name", ["dense_f32", "peaked_bf16", "onehot_bf16"])
+def test_exact_flag_gives_same_results(name):
+    """SV_FLAG_EXACT takes every row through the fp64 path."""
+    gh = _gh()
+    w = make_workload(name, 1, B=6, V=20000)
+    g1 = gh.run_gpu(w, flags=api.SV_FLAG_EXACT)
+    assert np.all(g1[3][:, 1] & api.SV_ROW_EXACT)
+    gh.compare(w, g1, label=f"{name} exact")
+    g2 = gh.run_gpu(w)
+    assert np.array_equal(g1[0], g2[0]) and np.array_equal(g1[1], g2[1])
+
+
+def test_all_residuals_same_outputs_and_determinism():
+    gh = _gh()
+    w = make_workload("peaked_bf16", 2, B=16)
+    a = gh.run_gpu(w)
+    b = gh.run_gpu(w, flags=api.SV_FLAG_ALL_RESIDUALS)
+    c = gh.run_gpu(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[3], c[3])
+    # in the default mode an accepted draft row skips its residual
+    rec = b[3].reshape(w["B"], -1, 2)
+    assert np.all(rec[:, :-1, 1] & api.SV_ROW_RESIDUAL)
+
+
+def test_ragged_equals_dense():
+    gh = _gh()
+    w = make_workload("peaked_bf16", 3, B=10, V=9000)
+    d = gh.run_gpu(w)
+    r = gh.run_gpu(dense_as_ragged(w))
+    assert np.array_equal(d[0].reshape(-1), r[0]) and np.array_equal(d[1], r[1])
+
+
+def test_temperature_zero_probs_equals_greedy():
+    gh = _gh()
+    w = make_dense_custom(4, B=24, gamma=3, V=4099, dtype="bf16", temperature=1.0)
+    t = gh.dev_inputs(w)
+    o1, n1, _, _ = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], 0.0)
+    o2, n2, _ = api.verify_greedy(t["logits"], t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(n1, n2)
+    w0 = dict(w, temperature=0.0)
+    gh.compare(w0, gh.run_gpu(w0), label="T=0 via probs")
+
+
+# ------------------------------------------------------------ shapes and edges
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 7, 1023, 1025, 5003, 8192])
+def test_vocab_sizes(dtype, V):
+    """Unaligned vocabularies take the scalar-load path; tiny ones a single tile."""
+    gh = _gh()
+    for q_kind in ("noisy", "onehot"):
+        w = make_dense_custom(V + (dtype == "bf16"), B=5, gamma=3, V=V, dtype=dtype, temperature=0.9,
+                              q_kind=q_kind)
+        gh.compare(w, gh.run_gpu(w), label=f"V{V} {dtype} {q_kind}")
+        gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"V{V} {dtype} {q_kind} stats")
+
+
+def test_gamma_zero_dense():
+    gh = _gh()
+    w = make_dense_custom(5, B=9, gamma=0, V=3000, dtype="bf16", temperature=1.2)
+    gh.compare(w, gh.run_gpu(w), label="gamma 0")
+
+
+def test_ragged_with_empty_requests():
+    gh = _gh()
+    rng = np.random.default_rng(6)
+    V, nb = 3001, 9
+    gb = np.array([0, 3, 0, 0, 5, 1, 0, 2, 0])
+    cu = np.concatenate([[0], np.cumsum(gb)]).astype(np.int32)
+    T = int(cu[-1])
+    l = rng.normal(0, 2, (T + nb, V)).astype(np.float32)
+    z = rng.normal(0, 2, (T, V))
+    q = np.exp(z - z.max(1, keepdims=True))
+    q = (q / q.sum(1, keepdims=True)).astype(np.float32)
+    x = np.array([rng.choice(V, p=qq / qq.sum()) for qq in q.astype(np.float64)], dtype=np.int64)
+    w = dict(kind="ragged", B=nb, V=V, dtype="f32", temperature=1.0, logits=l, logits_bits=None,
+             draft_probs=q, draft_tokens=x, uniforms=lattice_uniforms(rng, T + nb), cu=cu)
+    gh.compare(w, gh.run_gpu(w), label="ragged empties")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label="ragged empties stats")
+
+
+def test_draft_equals_target_distribution():
+    """q = fp32(p): nearly every draft is accepted; with accept uniforms of 1
+    the rejections that remain have residual mass around 1e-8, which takes the
+    rows through the fp64 path and the 1e-8 fallback."""
+    gh = _gh()
+    rng = np.random.default_rng(7)
+    B, g, V, T = 16, 3, 2048, 0.8
+    l = rng.normal(0, 2, (B, g + 1, V)).astype(np.float32)
+    s = l[:, :g].astype(np.float64) / T
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    q = p.astype(np.float32)
+    x = np.array([[rng.choice(V, p=p[b, i]) for i in range(g)] for b in range(B)], dtype=np.int64)
+    u = lattice_uniforms(rng, (B, g + 1))
+    u[:, :g] = 1.0
+    w = dict(kind="dense", B=B, gamma=g, V=V, dtype="f32", temperature=T, logits=l, logits_bits=None,
+             draft_probs=q, draft_tokens=x, uniforms=u)
+    gpu = gh.run_gpu(w)
+    gh.compare(w, gpu, label="q = p")
+    gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label="q = p stats")
+
+
+def test_disjoint_support():
+    """Target logits -inf on the draft's support: every draft is rejected."""
+    gh = _gh()
+    rng = np.random.default_rng(8)
+    B, g, V = 12, 4, 4096
+    l = rng.normal(0, 2, (B, g + 1, V)).astype(np.float32)
+    l[:, :, : V // 2] = -np.inf
+    q = np.zeros((B, g, V), dtype=np.float32)
+    z = np.exp(rng.normal(0, 1, (B, g, V // 2)))
+    q[:, :, : V // 2] = (z / z.sum(-1, keepdims=True)).astype(np.float32)
+    x = rng.integers(0, V // 2, (B, g)).astype(np.int64)
+    w = dict(kind="dense", B=B, gamma=g, V=V, dtype="f32", temperature=1.0, logits=l, logits_bits=None,
+             draft_probs=q, draft_tokens=x, uniforms=lattice_uniforms(rng, (B, g + 1)))
+    out, nacc, _, _ = gpu = gh.run_gpu(w)
+    assert np.all(nacc == 0) and np.all(out[:, 0] >= V // 2)
+    gh.compare(w, gpu, label="disjoint")
+
+
+def test_extreme_uniforms_and_ties():
+    gh = _gh()
+    w = make_dense_custom(9, B=32, gamma=4, V=6000, dtype="bf16", temperature=1.0, logit_sigma=0.05)
+    # logits with sigma 0.05 in bf16 have many exact ties; uniforms at both ends
+    u = w["uniforms"].copy()
+    u[::2, -1] = 1.0
+    u[1::2, -1] = 2.0 ** -24
+    u[::3, 0] = 1.0
+    w["uniforms"] = u
+    gh.compare(w, gh.run_gpu(w), label="extreme uniforms")
+    wg = dict(w, temperature=0.0, draft_probs=None)
+    wg["draft_tokens"] = np.argmax(w["logits"][:, :-1], axis=-1)
+    gh.compare(wg, gh.run_gpu(wg), label="greedy ties")
+
+
+def test_out_of_range_draft_token_is_rejected():
+    gh = _gh()
+    w = make_dense_custom(10, B=4, gamma=2, V=1000, dtype="f32", temperature=1.0)
+    t = gh.dev_inputs(w)
+    t["x"][:, 0] = 5000  # outside the vocabulary: p(x) = 0, never accepted, never read out of bounds
+    out, nacc, _, _ = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], 1.0)
+    torch.cuda.synchronize()
+    assert torch.all(nacc == 0)
+    assert torch.all((out[:, 0] >= 0) & (out[:, 0] < 1000))
