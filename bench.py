@@ -1,0 +1,178 @@
+"""Benchmark of the speculative-sampling verifier on one MI355X.
+
+One step = one call of spec_verify_probs on the headline workload: B=256
+requests, gamma=7 drafts each, V=128256, bf16 target logits (N(0, 4^2) with
+1% of each row boosted by 8), fp32 draft probabilities, T=0.7 — the whole hot
+path (temperature softmax, accept test, residual and bonus sampling, first
+rejection select). Inputs are synthetic and seeded, already resident in HBM
+when the timed region starts.
+
+Prints one JSON line. `value` is verified draft positions per second
+(B * gamma per call). The roofline object prices the row kernel against HBM:
+algorithmic bytes = every target logit row once + the q rows the call had to
+read in full (rows whose replacement token was drawn) + one q(x) gather per
+accepted draft row. The oracle (float64 numpy) is timed on the host cores on
+the same inputs as the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=256 γ=7 V=128k"
+
+
+def _oracle_chunk(args):
+    import numpy as np
+
+    import oracle
+
+    logits, q, x, u, T = args
+    n = 0
+    out = []
+    for b in range(len(x)):
+        p_rows = [oracle.target_probs(logits[b, i], T) for i in range(logits.shape[1])]
+        toks, nb = oracle.verify_request(p_rows, [q[b, i] for i in range(q.shape[1])], x[b], u[b])
+        out.append((toks, nb))
+        n += 1
+    return out
+
+
+def cpu_baseline(w, max_requests: int):
+    """Time the oracle over the first `max_requests` requests with one worker
+    per host core; returns (dict, oracle results)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    nb = min(max_requests, w["B"])
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, nb))
+    chunks = np.array_split(np.arange(nb), workers)
+    jobs = [(w["logits"][c], w["draft_probs"][c], w["draft_tokens"][c], w["uniforms"][c], w["temperature"])
+            for c in chunks if len(c)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(jobs)) as pool:
+        res = pool.map(_oracle_chunk, jobs)
+    dt = time.perf_counter() - t0
+    flat = [r for part in res for r in part]
+    positions = nb * w["gamma"]
+    return dict(value=positions / dt, unit="positions/s", cores=len(jobs), kind="oracle",
+                sample=f"first {nb} of {w['B']} requests of the same inputs, float64 numpy, "
+                       f"{len(jobs)} worker processes, {dt:.2f} s wall"), flat
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="peaked_bf16")
+    ap.add_argument("--flags", type=int, default=0, help="SV_FLAG_* bits passed to the library")
+    ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verifier_spec_amd import api
+    from rejection_sampling_verifier_spec_amd.workloads import make_workload
+
+    api.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = make_workload(args.workload, 0)
+    B, g, V, T = w["B"], w["gamma"], w["V"], w["temperature"]
+    if w["dtype"] == "bf16":
+        logits = torch.from_numpy(w["logits_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        logits = torch.from_numpy(w["logits"]).to(dev)
+    q = None if w["draft_probs"] is None else torch.from_numpy(w["draft_probs"]).to(dev)
+    x = torch.from_numpy(w["draft_tokens"]).to(dev)
+    u = torch.from_numpy(w["uniforms"]).to(dev)
+    rows = B * (g + 1)
+    ws = torch.zeros(api.workspace_size(rows), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return api.verify_probs(logits, q, x, u, T, flags=args.flags, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        out, nacc, _, _ = step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall / args.steps * 1e3
+    positions = B * g
+
+    rec = api.row_records(ws, rows).cpu().numpy().reshape(B, g + 1, 2)
+    flags = rec[..., 1]
+    esz = 2 if w["dtype"] == "bf16" else 4
+    residual_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_RESIDUAL))
+    accepted_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_ACCEPTED))
+    exact_rows = int(np.count_nonzero(flags & api.SV_ROW_EXACT))
+    q_bytes = 0 if q is None else residual_rows * V * 4 + (positions - residual_rows) * 4
+    alg_bytes = rows * V * esz + q_bytes
+    full_bytes = rows * V * esz + (0 if q is None else positions * V * 4)
+    call_s = float(np.mean(ev_ms)) * 1e-3
+    achieved = alg_bytes / call_s / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": positions / (wall / args.steps),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 logits, fp32 q, fp32 arithmetic with fp64 accumulation" if esz == 2 else "fp32",
+        "data": "synthetic, seeded (numpy PCG64), same recipe as the parity tests",
+        "config": {"workload": f"{args.workload}: B={B} gamma={g} V={V} T={T} {w['dtype']} logits",
+                   "global_batch": B, "gamma": g, "vocab": V, "flags": args.flags},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_call": alg_bytes,
+                     "kernel_ms_mean": float(np.mean(ev_ms)), "kernel_ms_p10": float(np.percentile(ev_ms, 10)),
+                     "kernel_ms_p90": float(np.percentile(ev_ms, 90)),
+                     "note": "time = hipEvents around each call (row kernel + select kernel) on the launch stream"},
+        "rows": {"draft": positions, "accepted_own_test": accepted_rows, "residual_drawn": residual_rows,
+                 "fp64_recomputed": exact_rows, "mean_accepted": float(nacc.float().mean().item())},
+        "speculative_full_bytes_per_call": full_bytes,
+        "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
+    }
+    if args.cpu_requests > 0 and q is not None:
+        base, ref = cpu_baseline(w, args.cpu_requests)
+        o = out.cpu().numpy()
+        na = nacc.cpu().numpy()
+        mism = sum(1 for b, (toks, n) in enumerate(ref) if n != na[b] or list(o[b, :n + 1]) != toks)
+        base["parity_mismatches_in_sample"] = mism
+        result["cpu_baseline"] = base
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -102,8 +102,9 @@ int spec_verify_version(void);
  *  draft_tokens   [B, gamma] int64.
  *  uniforms       [B, gamma+1] fp32 (see the uniform convention above).
  *  num_requests B >= 0, gamma >= 0, 1 <= vocab_size V <= SV_MAX_VOCAB.
- *  temperature    T >= 0 and finite; T == 0 runs the greedy kernel
- *                 (draft_probs and uniforms are then not read).
+ *  temperature    T >= 0 and finite (double, so that callers, kernels and
+ *                 references agree on the exact value); T == 0 runs the
+ *                 greedy kernel (draft_probs and uniforms are then not read).
  *  flags          SV_FLAG_* bits.
  *  out_tokens     [B, gamma+1] int64: x_1..x_n, then the drawn token, then -1.
  *  num_accepted   [B] int32: n, the number of accepted drafts.
@@ -117,7 +118,7 @@ int spec_verify_version(void);
  */
 int spec_verify_probs(const void* target_logits, int logits_dtype, const float* draft_probs,
                       const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
-                      int32_t gamma, int32_t vocab_size, float temperature, uint32_t flags,
+                      int32_t gamma, int32_t vocab_size, double temperature, uint32_t flags,
                       int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -152,7 +153,7 @@ int spec_verify_greedy(const void* target_logits, int logits_dtype, const int64_
 int spec_verify_ragged(const void* target_logits, int logits_dtype, const float* draft_probs,
                        const int64_t* draft_tokens, const int32_t* cu_num_draft_tokens,
                        const float* uniforms, int32_t num_requests, int32_t num_draft_tokens,
-                       int32_t vocab_size, float temperature, uint32_t flags,
+                       int32_t vocab_size, double temperature, uint32_t flags,
                        int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
                        void* workspace, size_t workspace_bytes, void* stream);
 

@@ -47,19 +47,19 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                            "(there is no fallback path)")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, u32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
-                                  ctypes.c_float, ctypes.c_size_t)
+    vp, i32, u32, i64, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
+                                  ctypes.c_double, ctypes.c_size_t)
     lib.spec_verify_workspace_size.argtypes = [i64]
     lib.spec_verify_workspace_size.restype = sz
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
     lib.spec_verify_version.restype = ctypes.c_int
-    lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f32, u32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_probs.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.restype = ctypes.c_int
-    lib.spec_verify_ragged.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f32, u32, vp, vp, vp, vp,
+    lib.spec_verify_ragged.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp,
                                        sz, vp]
     lib.spec_verify_ragged.restype = ctypes.c_int
     _lib = lib

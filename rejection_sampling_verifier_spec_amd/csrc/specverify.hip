@@ -315,7 +315,7 @@ struct ProbsArgs {
   float* stats;          // nullptr: no statistics
   double s64;            // log2(e) / T
   float s32;             // fp32(s64)
-  float temperature;
+  double temperature;
   int B, gamma, ndraft, V;
   uint32_t flags;
 };
@@ -331,6 +331,8 @@ struct RowShared {
   double c_lo, c_hi;
   int tile;
   double p_before;
+  int cross;
+  int lastpos;
 };
 
 // Bound on sum_k |e~_k - e_k| in e-units (e_k relative to the row max), and
@@ -402,30 +404,41 @@ __device__ void exact_row(const ProbsArgs& a, const Task& t, const LT* __restric
     }
     flags |= is_draft ? kRowResidual : 0u;
     const double tau = static_cast<double>(a.u[t.srow]) * total;
-    if (tid == 0) sh.found = 0;
+    // Smallest k with C_k >= tau. The tree scan does not make incl_t equal
+    // excl_t + v_t bit for bit, so every thread whose range starts below tau
+    // walks it; only positive weights can be chosen; the smallest crossing
+    // index wins, else the last positive weight below tau (tau at the very
+    // top of the CDF, within rounding).
+    if (tid == 0) {
+      sh.cross = 0x7fffffff;
+      sh.lastpos = -1;
+    }
     __syncthreads();
-    if (tau <= 0.0) {
-      if (tid == 0) { sh.token = 0; sh.found = 1; }
-    } else if (excl < tau && incl >= tau) {
+    if (tau > 0.0 && excl < tau) {
       int tok = -1, lastpos = -1;
       double c = 0.0;
       for (int k = lo; k < hi; ++k) {
         const double w = weight(k);
         c += w;
-        if (w > 0.0) lastpos = k;
-        if (excl + c >= tau) { tok = k; break; }
+        if (w > 0.0) {
+          lastpos = k;
+          if (excl + c >= tau) {
+            tok = k;
+            break;
+          }
+        }
       }
-      sh.token = tok >= 0 ? tok : (lastpos >= 0 ? lastpos : lo);
-      sh.found = 1;
+      if (tok >= 0) atomicMin(&sh.cross, tok);
+      if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
     }
     __syncthreads();
-    token = sh.found ? sh.token : 0;
+    token = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : 0);
   }
   if (tid == 0) {
     a.ws[t.trow] = make_int2(token, static_cast<int>(flags));
     if (a.stats) {
       float* st = a.stats + t.trow * 4;
-      st[0] = static_cast<float>(m / static_cast<double>(a.temperature));
+      st[0] = static_cast<float>(m / a.temperature);
       st[1] = static_cast<float>(log(Z));
       st[2] = is_draft ? static_cast<float>(px) : NAN;
       st[3] = static_cast<float>(rmass);
@@ -679,7 +692,7 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
     a.ws[t.trow] = make_int2(sh.token, static_cast<int>(fl));
     if (want_stats) {
       float* st = a.stats + t.trow * 4;
-      st[0] = static_cast<float>(static_cast<double>(m) / static_cast<double>(a.temperature));
+      st[0] = static_cast<float>(static_cast<double>(m) / a.temperature);
       st[1] = static_cast<float>(log(Z));
       st[2] = is_draft ? static_cast<float>(sh.px) : NAN;
       st[3] = is_draft ? static_cast<float>(mode_w ? total : total / Z) : 1.f;
@@ -828,27 +841,27 @@ int finish_launch() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LA
 
 // Shared implementation of the three entry points.
 int verify_common(const void* logits, int dtype, const float* q, const int64_t* x, const int32_t* cu,
-                  const float* u, int32_t B, int32_t gamma, int32_t ndraft, int32_t V, float T, uint32_t flags,
+                  const float* u, int32_t B, int32_t gamma, int32_t ndraft, int32_t V, double T, uint32_t flags,
                   int64_t* out, int32_t* nacc, float* stats, void* ws, size_t ws_size, void* stream,
                   bool greedy_only) {
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_UNSUPPORTED;
   if (B < 0 || gamma < 0 || ndraft < 0 || V < 1) return SV_ERR_INVALID_ARGUMENT;
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
-  if (!(T >= 0.f) || !isfinite(T)) return SV_ERR_INVALID_ARGUMENT;
+  if (!(T >= 0.0) || !isfinite(T)) return SV_ERR_INVALID_ARGUMENT;
   if (flags & ~static_cast<uint32_t>(SV_FLAG_EXACT | SV_FLAG_ALL_RESIDUALS)) return SV_ERR_INVALID_ARGUMENT;
-  if (stats && !(T > 0.f)) return SV_ERR_INVALID_ARGUMENT;
+  if (stats && !(T > 0.0)) return SV_ERR_INVALID_ARGUMENT;
   const int64_t rows = static_cast<int64_t>(ndraft) + B;
   if (rows > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
   if (B == 0) return SV_OK;
   if (!logits || !out || !nacc) return SV_ERR_INVALID_ARGUMENT;
   if (ndraft > 0 && !x) return SV_ERR_INVALID_ARGUMENT;
-  if (!greedy_only && T > 0.f && !u) return SV_ERR_INVALID_ARGUMENT;
+  if (!greedy_only && T > 0.0 && !u) return SV_ERR_INVALID_ARGUMENT;
   if (!ws || ws_size < ws_bytes(rows) || (reinterpret_cast<uintptr_t>(ws) & 7u)) return SV_ERR_WORKSPACE;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   int2* wsp = static_cast<int2*>(ws);
 
-  if (greedy_only || T == 0.f) {
+  if (greedy_only || T == 0.0) {
     GreedyArgs g{logits, x, cu, wsp, B, gamma, ndraft, V};
     if (dtype == SV_DTYPE_BF16) launch_greedy<uint16_t>(g, rows, st);
     else launch_greedy<float>(g, rows, st);
@@ -861,7 +874,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.cu = cu;
     p.ws = wsp;
     p.stats = stats;
-    p.s64 = 1.4426950408889634 / static_cast<double>(T);
+    p.s64 = 1.4426950408889634 / T;
     p.s32 = static_cast<float>(p.s64);
     p.temperature = T;
     p.B = B;
@@ -904,7 +917,7 @@ int spec_verify_version(void) { return 1; }
 
 int spec_verify_probs(const void* target_logits, int logits_dtype, const float* draft_probs,
                       const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
-                      int32_t gamma, int32_t vocab_size, float temperature, uint32_t flags,
+                      int32_t gamma, int32_t vocab_size, double temperature, uint32_t flags,
                       int64_t* out_tokens, int32_t* num_accepted, float* row_stats, void* workspace,
                       size_t workspace_bytes, void* stream) {
   if (num_requests < 0 || gamma < 0) return SV_ERR_INVALID_ARGUMENT;
@@ -922,13 +935,13 @@ int spec_verify_greedy(const void* target_logits, int logits_dtype, const int64_
   const int64_t nd = static_cast<int64_t>(num_requests) * gamma;
   if (nd > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
   return verify_common(target_logits, logits_dtype, nullptr, draft_tokens, nullptr, nullptr, num_requests, gamma,
-                       static_cast<int32_t>(nd), vocab_size, 0.f, 0u, out_tokens, num_accepted, nullptr, workspace,
+                       static_cast<int32_t>(nd), vocab_size, 0.0, 0u, out_tokens, num_accepted, nullptr, workspace,
                        workspace_bytes, stream, true);
 }
 
 int spec_verify_ragged(const void* target_logits, int logits_dtype, const float* draft_probs,
                        const int64_t* draft_tokens, const int32_t* cu_num_draft_tokens, const float* uniforms,
-                       int32_t num_requests, int32_t num_draft_tokens, int32_t vocab_size, float temperature,
+                       int32_t num_requests, int32_t num_draft_tokens, int32_t vocab_size, double temperature,
                        uint32_t flags, int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
                        void* workspace, size_t workspace_bytes, void* stream) {
   if (num_requests > 0 && !cu_num_draft_tokens) return SV_ERR_INVALID_ARGUMENT;

@@ -109,6 +109,8 @@ def _flip_tolerated(w, b, gpu_toks, gpu_n, ref_toks, ref_n):
         wts = p_rows[g]
     c = np.cumsum(wts) / np.cumsum(wts)[-1]
     gt = gpu_toks[n]
+    if not 0 <= gt < len(c):
+        return False
     us = float(u[g])
     lo = c[gt - 1] if gt > 0 else 0.0
     return (lo - 1e-6) < us <= c[gt] + 1e-6
