@@ -103,7 +103,7 @@ def main():
     x = torch.from_numpy(w["draft_tokens"]).to(dev)
     u = torch.from_numpy(w["uniforms"]).to(dev)
     rows = B * (g + 1)
-    ws = torch.zeros(api.workspace_size(rows), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(api.workspace_size(rows, V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
@@ -132,6 +132,7 @@ def main():
     residual_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_RESIDUAL))
     accepted_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_ACCEPTED))
     exact_rows = int(np.count_nonzero(flags & api.SV_ROW_EXACT))
+    exact_why = {name: int(np.count_nonzero(flags & bit)) for bit, name in api.SV_ROW_WHY.items()}
     q_bytes = 0 if q is None else residual_rows * V * 4 + (positions - residual_rows) * 4
     alg_bytes = rows * V * esz + q_bytes
     full_bytes = rows * V * esz + (0 if q is None else positions * V * 4)
@@ -160,7 +161,7 @@ def main():
                      "kernel_ms_p90": float(np.percentile(ev_ms, 90)),
                      "note": "time = hipEvents around each call (row kernel + select kernel) on the launch stream"},
         "rows": {"draft": positions, "accepted_own_test": accepted_rows, "residual_drawn": residual_rows,
-                 "fp64_recomputed": exact_rows, "mean_accepted": float(nacc.float().mean().item())},
+                 "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item())},
         "speculative_full_bytes_per_call": full_bytes,
         "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
     }

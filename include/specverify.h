@@ -73,23 +73,45 @@ enum sv_status {
 #define SV_FLAG_EXACT 0x1u         /* take every row through the fp64 path (reference / testing) */
 #define SV_FLAG_ALL_RESIDUALS 0x2u /* draw the replacement token of every draft row, accepted or not */
 
-/* Workspace layout (documented for diagnostics): one 8-byte record per target
- * row, {int32 token, uint32 row_flags}, at offset 0. row_flags bits: */
+/* Workspace: device memory of spec_verify_workspace_size() bytes, 256-byte
+ * aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call leaves it ready for
+ * the next one. One workspace per call in flight (calls that share one on
+ * different streams race). It starts with one 8-byte record per target row,
+ * {int32 token, uint32 row_flags} (documented for diagnostics), followed by
+ * the list and fp64 tile sums of the rows recomputed in fp64. row_flags bits: */
 #define SV_ROW_ACCEPTED 0x1u  /* the row's own accept test passed */
 #define SV_ROW_EXACT 0x2u     /* the row was recomputed on the fp64 path */
 #define SV_ROW_RESIDUAL 0x4u  /* the row's replacement token was drawn (q read in full) */
 #define SV_ROW_FALLBACK 0x8u  /* residual mass <= 1e-8: the replacement was drawn from p */
+/* why a row went to the fp64 path (set together with SV_ROW_EXACT): */
+#define SV_ROW_WHY_ACCEPT 0x10u    /* accept test within the fp32 error bound, or p(x) < 1e-30 */
+#define SV_ROW_WHY_FALLBACK 0x20u  /* residual mass within the bound of the 1e-8 threshold */
+#define SV_ROW_WHY_SEARCH 0x40u    /* inverse-CDF search inconclusive in fp32 */
+#define SV_ROW_WHY_MARGIN 0x80u    /* sample uniform within the bound of a CDF boundary */
+#define SV_ROW_WHY_FORCED 0x100u   /* SV_FLAG_EXACT, or a degenerate row */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
- * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests).
- * Returns 0 for a negative argument. */
-size_t spec_verify_workspace_size(int64_t num_target_rows);
+ * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of
+ * `vocab_size` tokens: 8 bytes per row for the records and list, plus
+ * 16 * ceil(vocab_size / 2048) bytes per row for fp64 tile sums. The greedy
+ * entry point needs only the records (8 bytes per row, rounded up to 256).
+ * Returns 0 for a negative row count or a vocab_size outside [1, SV_MAX_VOCAB]. */
+size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size);
 
 /* Static, human-readable text for a status code. */
 const char* spec_verify_status_string(int status);
 
 /* Library ABI version (currently 1). */
 int spec_verify_version(void);
+
+/* Self-check of the one hardware property the certified fast path relies on:
+ * writes to *max_rel_err (device pointer to one double) the largest relative
+ * error of the GPU's fp32 exp2 over every fp32 input in [-126, 0], measured
+ * against fp64 exp2. spec_verify_exp2_error_bound() returns the bound the
+ * error analysis assumes; a measured value above it means results are no
+ * longer certified on that device. Asynchronous on `stream`. */
+int spec_verify_selftest_exp2(double* max_rel_err, void* stream);
+double spec_verify_exp2_error_bound(void);
 
 /*
  * spec_verify_probs - dense batch, rejection-sampling verification.
@@ -113,8 +135,8 @@ int spec_verify_version(void);
  *                 max(0, p - q) for draft rows; p(x) = NaN and R = 1 for bonus
  *                 rows. Requires T > 0. Implies SV_FLAG_ALL_RESIDUALS.
  *  workspace      device scratch of at least
- *                 spec_verify_workspace_size(B * (gamma + 1)) bytes, 8-byte
- *                 aligned; contents on entry are ignored.
+ *                 spec_verify_workspace_size(B * (gamma + 1), V) bytes, see
+ *                 the workspace note above.
  */
 int spec_verify_probs(const void* target_logits, int logits_dtype, const float* draft_probs,
                       const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,

@@ -25,9 +25,11 @@ SV_ROW_ACCEPTED = 0x1
 SV_ROW_EXACT = 0x2
 SV_ROW_RESIDUAL = 0x4
 SV_ROW_FALLBACK = 0x8
+SV_ROW_WHY = {0x10: "accept", 0x20: "fallback", 0x40: "search", 0x80: "margin", 0x100: "forced"}
 
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
-           "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged")
+           "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
+           "spec_verify_exp2_error_bound")
 
 _lib = None
 
@@ -49,12 +51,16 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, u32, i64, f64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64,
                                   ctypes.c_double, ctypes.c_size_t)
-    lib.spec_verify_workspace_size.argtypes = [i64]
+    lib.spec_verify_workspace_size.argtypes = [i64, i32]
     lib.spec_verify_workspace_size.restype = sz
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     lib.spec_verify_version.argtypes = []
     lib.spec_verify_version.restype = ctypes.c_int
+    lib.spec_verify_selftest_exp2.argtypes = [vp, vp]
+    lib.spec_verify_selftest_exp2.restype = ctypes.c_int
+    lib.spec_verify_exp2_error_bound.argtypes = []
+    lib.spec_verify_exp2_error_bound.restype = ctypes.c_double
     lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_probs.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
@@ -70,8 +76,8 @@ def status_string(status: int) -> str:
     return load().spec_verify_status_string(int(status)).decode()
 
 
-def workspace_size(num_target_rows: int) -> int:
-    return int(load().spec_verify_workspace_size(int(num_target_rows)))
+def workspace_size(num_target_rows: int, vocab_size: int) -> int:
+    return int(load().spec_verify_workspace_size(int(num_target_rows), int(vocab_size)))
 
 
 def _ptr(t):
@@ -104,10 +110,14 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(rows, device, workspace):
-    need = workspace_size(rows)
+def _workspace(rows, vocab, device, workspace):
+    """The library needs a zero-filled workspace on first use (it leaves it
+    ready for the next call); a fresh one is allocated zeroed."""
+    need = workspace_size(rows, vocab)
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=device)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace of {workspace.numel()} bytes, {need} needed")
     return workspace, need
 
 
@@ -133,7 +143,7 @@ def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, flags
     out = torch.empty((B, g1), dtype=torch.int64, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(B * g1, dev, workspace)
+    workspace, need = _workspace(B * g1, V, dev, workspace)
     rc = lib.spec_verify_probs(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(out), _ptr(nacc),
                                _ptr(stats), _ptr(workspace), workspace.numel(), _stream(dev, stream))
@@ -154,7 +164,7 @@ def verify_greedy(logits, draft_tokens, workspace=None, stream=None):
         raise ValueError("draft_tokens must be [B, gamma]")
     out = torch.empty((B, g1), dtype=torch.int64, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(B * g1, dev, workspace)
+    workspace, need = _workspace(B * g1, V, dev, workspace)
     rc = lib.spec_verify_greedy(_ptr(logits), _dtype_code(logits), _ptr(draft_tokens), B, g, V, _ptr(out),
                                 _ptr(nacc), _ptr(workspace), workspace.numel(), _stream(dev, stream))
     if rc != 0:
@@ -184,7 +194,7 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
     out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
     nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
     stats = torch.empty((T + nb, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(T + nb, dev, workspace)
+    workspace, need = _workspace(T + nb, V, dev, workspace)
     rc = lib.spec_verify_ragged(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                 _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature), int(flags),
                                 _ptr(out), _ptr(nacc), _ptr(stats), _ptr(workspace), workspace.numel(),
@@ -192,6 +202,18 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_ragged")
     return out, nacc, stats, workspace
+
+
+def selftest_exp2(device=None, stream=None):
+    """Measured max relative error of the device's fp32 exp2 on [-126, 0] and
+    the bound the certified fast path assumes: (measured, assumed)."""
+    lib = load()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    out = torch.empty(1, dtype=torch.float64, device=dev)
+    rc = lib.spec_verify_selftest_exp2(_ptr(out), _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_selftest_exp2")
+    return float(out.item()), float(lib.spec_verify_exp2_error_bound())
 
 
 def row_records(workspace, num_target_rows):

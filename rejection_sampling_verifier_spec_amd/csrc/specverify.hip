@@ -47,8 +47,9 @@ namespace {
 
 constexpr int kNT = 256;                // threads per row block
 constexpr int kWaves = kNT / 64;        // waves per row block
-constexpr int kTile = 1024;             // elements per tile (one wave, 16 per lane)
-constexpr int kLaneElems = kTile / 64;  // 16
+constexpr int kTile = 2048;             // elements per tile (one wave, 32 per lane)
+constexpr int kLaneElems = kTile / 64;  // 32
+constexpr int kSearchPer = kTile / kNT; // elements per thread in the in-tile search
 constexpr int kSelectNT = 256;
 
 // ----------------------------------------------------------------------------
@@ -59,9 +60,12 @@ constexpr double kEpsExp = 2.384185791015625e-07;  // 2^-22 >= relative error of
 // per-term relative error of e_k ~ exp2(a_k): C1 |a_k| + C0 (see bound_terms)
 constexpr double kC1 = 4.0 * kU * kLn2;
 constexpr double kC0 = 2.0 * kEpsExp + 3.0 * kU;
-constexpr double kSumErr = 26.0 * kU;   // fp32 summation chains (<= 24 levels) + slack
-constexpr double kBoundA = 21.0;        // split point of the |a| bound (V <= 2^21)
-constexpr double kSafety = 1.5;
+// fp32 summation: a lane sums its 32 terms of a tile in 4 interleaved
+// accumulators (<= 7 additions each) joined by a 2-level tree, then a 6-level
+// wave tree and one product (tile rescale): every term passes <= 16 roundings.
+// The in-tile search sums 8 terms per thread (<= 7). Bound: gamma_20.
+constexpr double kSumErr = 20.0 * kU;
+constexpr double kSafety = 1.25;
 constexpr double kFallbackMass = 1e-8;  // timinsight.com "Step 2" constant
 
 constexpr uint32_t kRowAccepted = SV_ROW_ACCEPTED;
@@ -145,40 +149,131 @@ __device__ __forceinline__ void load_q(const float* __restrict__ row, int V, int
 #pragma unroll
   for (int r = 0; r < L::kRuns; ++r) {
     const int i0 = base + (r * 64 + lane) * L::kE;
+    const bool in = i0 < V;
     if constexpr (VEC) {
+      const int ic = in ? i0 : V - L::kE;
 #pragma unroll
       for (int h = 0; h < L::kE / 4; ++h) {
-        if (i0 < V) {
-          const float4 d = *reinterpret_cast<const float4*>(row + i0 + 4 * h);
-          q[r * L::kE + 4 * h + 0] = d.x;
-          q[r * L::kE + 4 * h + 1] = d.y;
-          q[r * L::kE + 4 * h + 2] = d.z;
-          q[r * L::kE + 4 * h + 3] = d.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[r * L::kE + 4 * h + e] = 0.f;
-        }
+        const float4 d = *reinterpret_cast<const float4*>(row + ic + 4 * h);
+        q[r * L::kE + 4 * h + 0] = in ? d.x : 0.f;
+        q[r * L::kE + 4 * h + 1] = in ? d.y : 0.f;
+        q[r * L::kE + 4 * h + 2] = in ? d.z : 0.f;
+        q[r * L::kE + 4 * h + 3] = in ? d.w : 0.f;
       }
     } else {
-      q[r] = i0 < V ? row[i0] : 0.f;
+      const float d = row[in ? i0 : V - 1];
+      q[r] = in ? d : 0.f;
     }
   }
 }
+
+// A lane's 32 logits of one tile kept packed as loaded (bf16 pairs or fp32),
+// so a prefetched tile costs 16 (bf16) or 32 (fp32) VGPRs.
+template <typename LT, bool VEC>
+struct RawTile;
+
+template <>
+struct RawTile<uint16_t, true> {
+  uint4 d[4];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int V, int base, int lane) {
+    // unconditional loads (address clamped into the row), so that the compiler
+    // can count outstanding loads and wait only for the tile it consumes
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i0 = base + (r * 64 + lane) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(row + (i0 < V ? i0 : V - 8));
+      // per-component selects (a select on the whole vector becomes a branch
+      // around the load); 0xff80 is bf16 -inf
+      const bool in = i0 < V;
+      d[r].x = in ? v.x : 0xff80ff80u;
+      d[r].y = in ? v.y : 0xff80ff80u;
+      d[r].z = in ? v.z : 0xff80ff80u;
+      d[r].w = in ? v.w : 0xff80ff80u;
+    }
+  }
+  __device__ __forceinline__ float get(int k) const {
+    const uint4& q = d[k >> 3];
+    const int h = (k & 7) >> 1;
+    const uint32_t w = h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
+    return (k & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+  // same value as get(k), written differently so that the compiler re-derives
+  // it from the packed word instead of keeping 32 unpacked values live
+  __device__ __forceinline__ float get2(int k) const {
+    const uint4& q = d[k >> 3];
+    const int h = (k & 7) >> 1;
+    const uint32_t w = h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
+    return (k & 1) ? __uint_as_float((w >> 16) << 16) : __uint_as_float((w & 0xffffu) << 16);
+  }
+};
+
+template <>
+struct RawTile<float, true> {
+  float4 d[8];
+  __device__ __forceinline__ void load(const float* __restrict__ row, int V, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i0 = base + (r * 64 + lane) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(row + (i0 < V ? i0 : V - 4));
+      const bool in = i0 < V;
+      d[r].x = in ? v.x : -INFINITY;
+      d[r].y = in ? v.y : -INFINITY;
+      d[r].z = in ? v.z : -INFINITY;
+      d[r].w = in ? v.w : -INFINITY;
+    }
+  }
+  __device__ __forceinline__ float get(int k) const {
+    const float4& q = d[k >> 2];
+    const int h = k & 3;
+    return h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
+  }
+  __device__ __forceinline__ float get2(int k) const { return get(k); }
+};
+
+template <typename LT>
+struct RawTile<LT, false> {
+  float d[kLaneElems];
+  __device__ __forceinline__ void load(const LT* __restrict__ row, int V, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < kLaneElems; ++r) {
+      const int i = base + r * 64 + lane;
+      const float v = to_float(row[i < V ? i : V - 1]);
+      d[r] = i < V ? v : -INFINITY;
+    }
+  }
+  __device__ __forceinline__ float get(int k) const { return d[k]; }
+  __device__ __forceinline__ float get2(int k) const { return d[k]; }
+};
 
 __device__ __forceinline__ float fexp2(float a) { return __builtin_amdgcn_exp2f(a); }
 
 // ----------------------------------------------------------------------------
 // reductions
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Row (16-lane) reduction by DPP: xor 1, xor 2 (quad permutes), then rotate
+// by 4 and 8 within the row; every lane ends with its row's total. The four
+// row totals are then combined in a fixed order, so every lane of the wave
+// holds the same, deterministic result.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 struct BlockScratch {
@@ -318,6 +413,8 @@ struct ProbsArgs {
   double temperature;
   int B, gamma, ndraft, V;
   uint32_t flags;
+  int* xcount;    // list of rows for the fp64 path (see ExactArgs)
+  int2* xlist;
 };
 
 struct RowShared {
@@ -335,12 +432,12 @@ struct RowShared {
   int lastpos;
 };
 
-// Bound on sum_k |e~_k - e_k| in e-units (e_k relative to the row max), and
-// with it the bound on |Z~ - Z|.
-__device__ __forceinline__ double bound_terms(double z, int V) {
-  // sum_k e_k |a_k| <= A Z + V A 2^-A ; per-term error C1 |a_k| + C0
-  return kSafety * (kC1 * kBoundA * (1.01 * z + static_cast<double>(V) * 4.76837158203125e-07 /* 2^-21 */)
-                    + kC0 * 1.01 * z + 1e-30);
+// Bound on sum_k |e~_k - e_k| in e-units (e_k relative to the row max):
+// each term has relative error <= C1 |a_k| + C0, so the sum is bounded by
+// C1 sum_k e_k |a_k| + C0 Z (the sums, computed in floating point, are
+// inflated by 1%). Terms that underflow add at most 2^-126 each (1e-30 total).
+__device__ __forceinline__ double bound_terms(double z, double sum_e_abs_a) {
+  return kSafety * (kC1 * 1.01 * sum_e_abs_a + kC0 * 1.01 * z + 1e-30);
 }
 
 template <typename LT>
@@ -348,104 +445,294 @@ __device__ __forceinline__ float logit_at(const LT* row, int64_t k) {
   return to_float(row[k]);
 }
 
-// Exact (fp64) recomputation of one row; all threads of the block call it.
+// ----------------------------------------------------------------------------
+// fp64 path for the rows the fast kernel could not certify.
+//
+// The fast kernel appends such a row to a list in the workspace; three small
+// fixed-grid kernels then spread the fp64 work over the whole GPU:
+//   exact_tiles_kernel:    one (row, tile) item per block iteration; fp64 sum of
+//                          e_k = 2^((l_k - m) log2(e) / T) over the tile.
+//   exact_residual_kernel: same items, rows with q only; fp64 sum of
+//                          max(0, e_k / Z - q_k) over the tile.
+//   exact_finish_kernel:   one row per block iteration; accept test, residual
+//                          mass, fallback, tile search and in-tile search, all
+//                          in fp64; writes the row's record and statistics.
+// With an empty list each kernel reads the count and exits.
+
+constexpr uint32_t kRowNeedExact = 0x200u;  // set by the fast kernel, cleared by exact_finish_kernel
+constexpr int kExactGrid = 512;             // blocks of the item kernels
+constexpr int kExactPer = kTile / kNT;      // elements per thread of one tile (8)
+
+struct ExactArgs {
+  int* count;     // number of listed rows (reset to 0 by the select kernel)
+  int2* list;     // {row block index, bits of the row max m}
+  double* etile;  // [rows][nt] fp64 tile sums of e
+  double* wtile;  // [rows][nt] fp64 tile sums of max(0, p - q)
+  int nt;
+  int rows;
+};
+
+// Thread t of a block covers elements [base + 8t, base + 8t + 8) of a tile,
+// so the tile is covered in ascending token order by ascending threads.
 template <typename LT>
-__device__ void exact_row(const ProbsArgs& a, const Task& t, const LT* __restrict__ lrow,
-                          const float* __restrict__ qrow, int64_t x, bool need_sample,
-                          BlockScratch& sc, RowShared& sh) {
-  const int V = a.V;
-  const int tid = threadIdx.x;
-  const int per = (V + kNT - 1) / kNT;
-  const int lo = min(V, tid * per), hi = min(V, lo + per);
-  const double m = static_cast<double>(sh.m);
-  const double s = a.s64;
-  const bool is_draft = t.drow >= 0;
-  const bool x_ok = is_draft && x >= 0 && x < V;
-  const bool onehot = is_draft && qrow == nullptr;
-
-  double zl = 0.0;
-  for (int k = lo; k < hi; ++k) zl += exp2((static_cast<double>(logit_at(lrow, k)) - m) * s);
-  const double Z = block_sum(zl, sc);
-
-  double px = 0.0;
-  bool accepted = false;
-  if (is_draft) {
-    if (x_ok) px = exp2((static_cast<double>(logit_at(lrow, x)) - m) * s) / Z;
-    const double qx = onehot ? 1.0 : (x_ok ? static_cast<double>(qrow[x]) : 0.0);
-    accepted = x_ok && px > 0.0 && static_cast<double>(a.u[t.trow]) * qx <= px;
+__device__ __forceinline__ void load8(const LT* __restrict__ row, int V, int k0, double (&l)[kExactPer]) {
+#pragma unroll
+  for (int e = 0; e < kExactPer; ++e) {
+    const int k = k0 + e;
+    l[e] = k < V ? static_cast<double>(to_float(row[k])) : -INFINITY;
   }
+}
 
-  uint32_t flags = kRowExact | (accepted ? kRowAccepted : 0u);
-  int token = -1;
-  double rmass = 1.0;
-  const bool sample = !is_draft || !accepted || need_sample;
-  if (sample) {
-    // weight mode: 0 = p (bonus / fallback), 1 = max(0, p - q), 2 = p without x (one-hot)
-    int mode = is_draft ? (onehot ? 2 : 1) : 0;
-    auto weight = [&](int k) -> double {
-      const double p = exp2((static_cast<double>(logit_at(lrow, k)) - m) * s) / Z;
-      if (mode == 1) return fmax(0.0, p - static_cast<double>(qrow[k]));
-      if (mode == 2) return (x_ok && k == x) ? fmax(0.0, p - 1.0) : p;
-      return p;
-    };
-    double wl = 0.0;
-    for (int k = lo; k < hi; ++k) wl += weight(k);
-    double excl, incl, total;
-    block_scan(wl, sc, excl, incl, total);
-    if (mode != 0) {
-      rmass = total;
-      if (total <= kFallbackMass) {
-        mode = 0;
-        flags |= kRowFallback;
-        wl = 0.0;
-        for (int k = lo; k < hi; ++k) wl += weight(k);
-        block_scan(wl, sc, excl, incl, total);
+struct ExactRow {
+  Task t;
+  const void* lrow;
+  const float* qrow;
+  int64_t x;
+  bool x_ok, is_draft, onehot;
+  double m;
+};
+
+__device__ __forceinline__ ExactRow exact_row_info(const ProbsArgs& a, const ExactArgs& e, int pos) {
+  ExactRow r;
+  const int2 li = e.list[pos];
+  // a list entry is a row block index of this call; anything else (a
+  // workspace that was not zero-filled) is skipped rather than decoded
+  const bool in_range = li.x >= 0 && li.x < e.rows;
+  r.t = decode_task(in_range ? li.x : 0, a.cu, a.B, a.gamma, a.ndraft);
+  r.t.valid = r.t.valid && in_range;
+  r.m = static_cast<double>(__int_as_float(li.y));
+  r.is_draft = r.t.drow >= 0;
+  r.qrow = (r.is_draft && a.q) ? a.q + r.t.drow * static_cast<int64_t>(a.V) : nullptr;
+  r.x = r.is_draft ? a.x[r.t.drow] : -1;
+  r.x_ok = r.is_draft && r.x >= 0 && r.x < a.V;
+  r.onehot = r.is_draft && r.qrow == nullptr;
+  r.lrow = nullptr;
+  return r;
+}
+
+__device__ __forceinline__ int exact_count(const ExactArgs& e) {
+  const int n = *e.count;
+  return n < 0 ? 0 : (n > e.rows ? e.rows : n);
+}
+
+template <typename LT>
+__global__ __launch_bounds__(kNT) void exact_tiles_kernel(ProbsArgs a, ExactArgs e) {
+  __shared__ BlockScratch sc;
+  const int n = exact_count(e);
+  const int64_t items = static_cast<int64_t>(n) * e.nt;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int pos = static_cast<int>(it / e.nt), j = static_cast<int>(it % e.nt);
+    const ExactRow r = exact_row_info(a, e, pos);
+    if (!r.t.valid) continue;
+    const LT* lrow = static_cast<const LT*>(a.logits) + r.t.trow * static_cast<int64_t>(a.V);
+    double l[kExactPer];
+    load8<LT>(lrow, a.V, j * kTile + kExactPer * threadIdx.x, l);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kExactPer; ++k) acc += exp2((l[k] - r.m) * a.s64);
+    acc = block_sum(acc, sc);
+    if (threadIdx.x == 0) e.etile[static_cast<int64_t>(pos) * e.nt + j] = acc;
+  }
+}
+
+// Z of listed row `pos` from its fp64 tile sums: thread t adds tiles t,
+// t + 256, ..., then a fixed-order block sum (identical in every kernel).
+__device__ __forceinline__ double exact_z(const double* __restrict__ et, int nt, BlockScratch& sc) {
+  double z = 0.0;
+  for (int j = threadIdx.x; j < nt; j += kNT) z += et[j];
+  return block_sum(z, sc);
+}
+
+template <typename LT>
+__global__ __launch_bounds__(kNT) void exact_residual_kernel(ProbsArgs a, ExactArgs e) {
+  __shared__ BlockScratch sc;
+  const int n = exact_count(e);
+  const int64_t items = static_cast<int64_t>(n) * e.nt;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int pos = static_cast<int>(it / e.nt), j = static_cast<int>(it % e.nt);
+    const ExactRow r = exact_row_info(a, e, pos);
+    if (!r.t.valid || r.qrow == nullptr) continue;  // uniform over the block
+    const double iz = 1.0 / exact_z(e.etile + static_cast<int64_t>(pos) * e.nt, e.nt, sc);
+    const LT* lrow = static_cast<const LT*>(a.logits) + r.t.trow * static_cast<int64_t>(a.V);
+    const int k0 = j * kTile + kExactPer * threadIdx.x;
+    double l[kExactPer];
+    load8<LT>(lrow, a.V, k0, l);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kExactPer; ++k) {
+      const double q = k0 + k < a.V ? static_cast<double>(r.qrow[k0 + k]) : 0.0;
+      acc += fmax(0.0, exp2((l[k] - r.m) * a.s64) * iz - q);
+    }
+    acc = block_sum(acc, sc);
+    if (threadIdx.x == 0) e.wtile[static_cast<int64_t>(pos) * e.nt + j] = acc;
+  }
+}
+
+template <typename LT>
+__global__ __launch_bounds__(kNT) void exact_finish_kernel(ProbsArgs a, ExactArgs e) {
+  extern __shared__ double xtile[];  // [nt] e tile sums, [nt] residual tile sums
+  __shared__ BlockScratch sc;
+  __shared__ RowShared sh;
+  const int n = exact_count(e);
+  const int tid = threadIdx.x;
+  const int nt = e.nt;
+  double* ets = xtile;
+  double* wts = xtile + nt;
+  const int tper = (nt + kNT - 1) / kNT;
+  const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
+  for (int pos = blockIdx.x; pos < n; pos += gridDim.x) {
+    const ExactRow r = exact_row_info(a, e, pos);
+    if (!r.t.valid) continue;
+    const Task& t = r.t;
+    const LT* lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(a.V);
+    const double* et = e.etile + static_cast<int64_t>(pos) * nt;
+    const double* wt = e.wtile + static_cast<int64_t>(pos) * nt;
+    for (int j = tid; j < nt; j += kNT) {
+      ets[j] = et[j];
+      wts[j] = r.qrow ? wt[j] : 0.0;
+    }
+    const double Z = exact_z(et, nt, sc);  // barriers inside also publish ets / wts
+    const double iz = 1.0 / Z;
+    const double s = a.s64;
+    const uint32_t why = static_cast<uint32_t>(a.ws[t.trow].y) & 0x1f0u;
+
+    double ex = 0.0, px = 0.0;
+    bool accepted = false;
+    if (r.is_draft) {
+      if (r.x_ok) {
+        ex = exp2((static_cast<double>(logit_at(lrow, r.x)) - r.m) * s);
+        px = ex * iz;
       }
+      const double qx = r.onehot ? 1.0 : (r.x_ok ? static_cast<double>(r.qrow[r.x]) : 0.0);
+      accepted = r.x_ok && px > 0.0 && static_cast<double>(a.u[t.trow]) * qx <= px;
     }
-    flags |= is_draft ? kRowResidual : 0u;
-    const double tau = static_cast<double>(a.u[t.srow]) * total;
-    // Smallest k with C_k >= tau. The tree scan does not make incl_t equal
-    // excl_t + v_t bit for bit, so every thread whose range starts below tau
-    // walks it; only positive weights can be chosen; the smallest crossing
-    // index wins, else the last positive weight below tau (tau at the very
-    // top of the CDF, within rounding).
-    if (tid == 0) {
-      sh.cross = 0x7fffffff;
-      sh.lastpos = -1;
-    }
-    __syncthreads();
-    if (tau > 0.0 && excl < tau) {
-      int tok = -1, lastpos = -1;
-      double c = 0.0;
-      for (int k = lo; k < hi; ++k) {
-        const double w = weight(k);
-        c += w;
-        if (w > 0.0) {
-          lastpos = k;
-          if (excl + c >= tau) {
-            tok = k;
-            break;
+    const bool all_res = (a.flags & SV_FLAG_ALL_RESIDUALS) || a.stats != nullptr;
+    uint32_t flags = kRowExact | why | (accepted ? kRowAccepted : 0u);
+    int token = -1;
+    double rmass = 1.0;
+    if (!r.is_draft || !accepted || all_res) {
+      // tile values in tile order: mode 1 residual, 2 p without x, 0 p
+      int mode = r.is_draft ? (r.onehot ? 2 : 1) : 0;
+      const int jx = r.x_ok ? static_cast<int>(r.x / kTile) : -1;
+      auto tile_val = [&](int j) -> double {
+        if (mode == 1) return wts[j];
+        double v = ets[j];
+        if (mode == 2 && j == jx) v = fmax(0.0, v - ex);
+        return v * iz;
+      };
+      double tv = 0.0;
+      for (int j = tlo; j < thi; ++j) tv += tile_val(j);
+      double excl, incl, total;
+      block_scan(tv, sc, excl, incl, total);
+      if (mode != 0) {
+        rmass = total;
+        if (total <= kFallbackMass) {
+          mode = 0;
+          flags |= kRowFallback;
+          tv = 0.0;
+          for (int j = tlo; j < thi; ++j) tv += tile_val(j);
+          block_scan(tv, sc, excl, incl, total);
+        }
+        flags |= kRowResidual;
+      }
+      const double tau = static_cast<double>(a.u[t.srow]) * total;
+      // crossing tile: smallest positive tile reaching tau, else the last positive tile
+      if (tid == 0) {
+        sh.cross = 0x7fffffff;
+        sh.lastpos = -1;
+      }
+      __syncthreads();
+      if (excl < tau) {
+        double c = 0.0;
+        int tok = -1, lastpos = -1;
+        for (int j = tlo; j < thi && tok < 0; ++j) {
+          const double v = tile_val(j);
+          c += v;
+          if (v > 0.0) {
+            lastpos = j;
+            if (excl + c >= tau) tok = j;
           }
         }
+        if (tok >= 0) atomicMin(&sh.cross, tok);
+        if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
       }
-      if (tok >= 0) atomicMin(&sh.cross, tok);
-      if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
+      __syncthreads();
+      const int jt = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : 0);
+      double pbl = 0.0;
+      for (int j = tlo; j < thi; ++j)
+        if (j < jt) pbl += tile_val(j);
+      const double pb = block_sum(pbl, sc);
+      // in-tile search, fp64, 8 consecutive elements per thread
+      const int k0 = jt * kTile + kExactPer * tid;
+      double l[kExactPer], w[kExactPer];
+      load8<LT>(lrow, a.V, k0, l);
+      double tsum = 0.0;
+#pragma unroll
+      for (int k = 0; k < kExactPer; ++k) {
+        const int kk = k0 + k;
+        double v = 0.0;
+        if (kk < a.V) {
+          const double p = exp2((l[k] - r.m) * s) * iz;
+          if (mode == 1) v = fmax(0.0, p - static_cast<double>(r.qrow[kk]));
+          else if (mode == 2 && kk == r.x) v = 0.0;
+          else v = p;
+        }
+        w[k] = v;
+        tsum += v;
+      }
+      double e2, i2, t2;
+      block_scan(tsum, sc, e2, i2, t2);
+      const double tl = tau - pb;
+      if (tid == 0) {
+        sh.cross = 0x7fffffff;
+        sh.lastpos = -1;
+      }
+      __syncthreads();
+      if (e2 < tl) {
+        int tok = -1, lastpos = -1;
+        double cl = 0.0;
+#pragma unroll
+        for (int k = 0; k < kExactPer; ++k) {
+          cl += w[k];
+          if (w[k] > 0.0 && tok < 0) {
+            lastpos = k0 + k;
+            if (e2 + cl >= tl) tok = k0 + k;
+          }
+        }
+        if (tok >= 0) atomicMin(&sh.cross, tok);
+        if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
+      }
+      __syncthreads();
+      token = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : jt * kTile);
+      __syncthreads();
+    }
+    if (tid == 0) {
+      a.ws[t.trow] = make_int2(token, static_cast<int>(flags));
+      if (a.stats) {
+        float* st = a.stats + t.trow * 4;
+        st[0] = static_cast<float>(r.m / a.temperature);
+        st[1] = static_cast<float>(log(Z));
+        st[2] = r.is_draft ? static_cast<float>(px) : NAN;
+        st[3] = static_cast<float>(rmass);
+      }
     }
     __syncthreads();
-    token = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : 0);
   }
-  if (tid == 0) {
-    a.ws[t.trow] = make_int2(token, static_cast<int>(flags));
-    if (a.stats) {
-      float* st = a.stats + t.trow * 4;
-      st[0] = static_cast<float>(m / a.temperature);
-      st[1] = static_cast<float>(log(Z));
-      st[2] = is_draft ? static_cast<float>(px) : NAN;
-      st[3] = static_cast<float>(rmass);
-    }
-  }
-  __syncthreads();
 }
+
+// Hand a row to the fp64 path: mark its record and append it to the list.
+__device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, uint32_t why, float m) {
+  a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowNeedExact | why));
+  const int pos = atomicAdd(a.xcount, 1);
+  if (pos < a.B + a.ndraft) a.xlist[pos] = make_int2(static_cast<int>(blockIdx.x), __float_as_int(m));
+}
+
+// Reasons a row was recomputed on the fp64 path (row_flags bits 4..8).
+constexpr uint32_t kWhyAccept = SV_ROW_WHY_ACCEPT;
+constexpr uint32_t kWhyFallback = SV_ROW_WHY_FALLBACK;
+constexpr uint32_t kWhySearch = SV_ROW_WHY_SEARCH;
+constexpr uint32_t kWhyMargin = SV_ROW_WHY_MARGIN;
+constexpr uint32_t kWhyForced = SV_ROW_WHY_FORCED;
 
 template <typename LT, bool VEC>
 __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
@@ -453,12 +740,14 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   __shared__ BlockScratch sc;
   __shared__ RowShared sh;
   using L = Lay<LT, VEC>;
+  using Raw = RawTile<LT, VEC>;
 
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
-  float* S = dyn;        // tile sums of exp2((l - M_j) s), local units
-  float* M = dyn + nt;   // tile max
+  float* S = dyn;           // tile sums of exp2((l - M_j) s), local units
+  float* M = dyn + nt;      // running max when the tile was summed (>= every element of the tile)
   float* W = dyn + 2 * nt;  // tile sums of max(0, p - q)
+  float* EA = dyn + 3 * nt; // tile sums of e |a| (a = the exp argument), for the error bound
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   const Task t = decode_task(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft);
@@ -474,32 +763,84 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   const bool want_stats = a.stats != nullptr;
   const bool all_res = (a.flags & SV_FLAG_ALL_RESIDUALS) || want_stats;
 
-  // ---------------- pass 1: tile max and tile sum of exp2((l - M_j) s)
-  for (int j = wave; j < nt; j += kWaves) {
-    const int base = j * kTile;
-    float v[kLaneElems];
-    load_logits<LT, VEC>(lrow, V, base, lane, v);
-    float mx = v[0];
+  // ---------------- pass 1: tile sums of exp2((l - M_j) s), M_j = the wave's
+  // running maximum when tile j is reduced. One sweep per tile: the exps are
+  // taken against the running maximum while the lane maxima are tracked; only
+  // when a tile raises the maximum (a wave-wide ballot, rare after the first
+  // tiles) is the tile summed again against the new maximum. Every exponent
+  // argument is therefore <= 0. The next tile's loads are in flight meanwhile.
+  auto tile_sum = [&](const Raw& r, int base, float ref, float& es, float& ea) {
+    float e4[4] = {0.f, 0.f, 0.f, 0.f};
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 1; k < kLaneElems; ++k) mx = fmaxf(mx, v[k]);
-    mx = wave_max(mx);
-    float es = 0.f;
-    if (mx != -INFINITY) {
-      if (xmask >= base && xmask < base + kTile) {
+    for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
 #pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) {
-          const float e = fexp2((v[k] - mx) * s);
-          es += (L::index(base, lane, k) == xmask) ? 0.f : e;
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) es += fexp2((v[k] - mx) * s);
+      for (int k = g8; k < g8 + 8; ++k) {
+        const float arg = fmaxf((r.get(k) - ref) * s, -4096.f);
+        const float e = (L::index(base, lane, k) == xmask) ? 0.f : fexp2(arg);
+        e4[k & 3] += e;
+        a4[k & 3] = fmaf(e, arg, a4[k & 3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+    ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+  };
+  float ref = -INFINITY;
+  auto tile1 = [&](const Raw& r, int j) {
+    const int base = j * kTile;
+    float lm = -INFINITY, es = 0.f, ea = 0.f;
+    if (xmask >= base && xmask < base + kTile) {
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, r.get(k));
+      es = 1.f;  // forces the masked sum below
+    } else {
+      float e4[4] = {0.f, 0.f, 0.f, 0.f};
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) {
+        const float v = r.get(k);
+        lm = fmaxf(lm, v);
+        // clamped so that -inf logits give e = 0 and e * a = 0 (not NaN)
+        const float arg = fmaxf((v - ref) * s, -4096.f);
+        const float e = fexp2(arg);
+        e4[k & 3] += e;
+        a4[k & 3] = fmaf(e, arg, a4[k & 3]);  // sum of e * a (a <= 0) for the error bound
+      }
+      es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+      ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    }
+    if (__any(lm > ref || (xmask >= base && xmask < base + kTile))) {
+      ref = fmaxf(ref, wave_max(lm));
+      es = 0.f;
+      ea = 0.f;
+      if (ref != -INFINITY) tile_sum(r, base, ref, es, ea);
     }
     es = wave_sum(es);
+    ea = wave_sum(ea);
     if (lane == 0) {
       S[j] = es;
-      M[j] = mx;
+      M[j] = ref;
+      EA[j] = -ea;
+    }
+  };
+  {
+    // the prefetch of a tile past the end re-reads the last tile (in bounds,
+    // results unused) so that every iteration issues the same loads
+    Raw ra, rb;
+    int j = wave;
+    if (j < nt) {
+      ra.load(lrow, V, j * kTile, lane);
+      while (true) {
+        rb.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
+        tile1(ra, j);
+        j += kWaves;
+        if (j >= nt) break;
+        ra.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
+        tile1(rb, j);
+        j += kWaves;
+        if (j >= nt) break;
+      }
     }
   }
   __syncthreads();
@@ -508,27 +849,36 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   float mloc = -INFINITY;
   for (int j = tid; j < nt; j += kNT) mloc = fmaxf(mloc, M[j]);
   const float m = block_max(mloc, sc);
-  double zl = 0.0;
+  double zl = 0.0, eal = 0.0;
   for (int j = tid; j < nt; j += kNT) {
     const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
     zl += static_cast<double>(S[j] * f);
+    // e_k |a_k| relative to m: |a_k| = |a_k, local| + (m - M_j) s
+    if (f > 0.f)
+      eal += static_cast<double>(f) *
+             (static_cast<double>(EA[j]) + (static_cast<double>(m) - M[j]) * a.s64 * static_cast<double>(S[j]));
   }
   float ex = 0.f, lx = -INFINITY;
   if (x_ok) {
     lx = to_float(lrow[x]);
     ex = fexp2((lx - m) * s);
   }
-  if (tid == 0 && xmask >= 0) zl += static_cast<double>(ex);  // one-hot rows left x out of S
+  if (tid == 0 && xmask >= 0) {  // one-hot rows left x out of S
+    zl += static_cast<double>(ex);
+    eal += static_cast<double>(ex) * (static_cast<double>(m) - lx) * a.s64;
+  }
   const double Z = block_sum(zl, sc);
-  const double bt = bound_terms(Z, V);
-  const double dZ = bt + kSumErr * Z;   // |Z~ - Z|
+  const double sea = block_sum(eal, sc);
+  const double bt = bound_terms(Z, sea);
+  const double dZ = bt + kSumErr * Z;  // |Z~ - Z|
   const double relZ = dZ / Z;
 
   // ---------------- accept test of a draft row (fp64 p(x), certified)
   if (tid == 0) {
     sh.m = m;
     sh.z = Z;
-    int accepted = 0, uncertain = 0;
+    int accepted = 0;
+    uint32_t why = 0;
     double px = 0.0;
     if (is_draft) {
       if (x_ok) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64) / Z;
@@ -537,18 +887,18 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
       accepted = (x_ok && px > 0.0 && lhs <= px) ? 1 : 0;
       if (x_ok) {
         const double dpx = kSafety * (px * relZ * 1.01) + 1e-300;
-        if (fabs(lhs - px) <= 2.0 * dpx || px < 1e-30 || !(Z > 0.0)) uncertain = 1;
+        if (fabs(lhs - px) <= 2.0 * dpx || px < 1e-30) why |= kWhyAccept;
       }
     }
-    if (!(Z > 0.0) || m == -INFINITY || (a.flags & SV_FLAG_EXACT)) uncertain = 1;
+    if (!(Z > 0.0) || m == -INFINITY || (a.flags & SV_FLAG_EXACT)) why |= kWhyForced;
     sh.px = px;
     sh.accepted = accepted;
-    sh.uncertain = uncertain;
+    sh.uncertain = static_cast<int>(why);
   }
   __syncthreads();
   const bool accepted = sh.accepted != 0;
   if (sh.uncertain) {
-    exact_row<LT>(a, t, lrow, qrow, x, all_res, sc, sh);
+    if (tid == 0) flag_exact(a, t, static_cast<uint32_t>(sh.uncertain), m);
     return;
   }
   const bool sample = !is_draft || !accepted || all_res;
@@ -563,15 +913,21 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   if (mode_w) {
     for (int j = wave; j < nt; j += kWaves) {
       const int base = j * kTile;
-      float v[kLaneElems], q[kLaneElems];
-      load_logits<LT, VEC>(lrow, V, base, lane, v);
+      Raw r;
+      float q[kLaneElems];
+      r.load(lrow, V, base, lane);
       load_q<LT, VEC>(qrow, V, base, lane, q);
-      float ws = 0.f;
+      float w4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) {
-        const float p = fexp2((v[k] - m) * s) * izr;
-        ws += fmaxf(p - q[k], 0.f);
+      for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
+#pragma unroll
+        for (int k = g8; k < g8 + 8; ++k) {
+          const float p = fexp2((r.get(k) - m) * s) * izr;
+          w4[k & 3] += fmaxf(p - q[k], 0.f);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      float ws = (w4[0] + w4[1]) + (w4[2] + w4[3]);
       ws = wave_sum(ws);
       if (lane == 0) W[j] = ws;
     }
@@ -593,26 +949,23 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   block_scan(tv, sc, excl, incl, total);
 
   // error bound of every CDF prefix (same units as total)
-  double dC, dcheck = 0.0;
-  bool uncertain = false;
+  double dC;
+  uint32_t why = 0;
   if (mode_w) {
-    const double dp = (bt / Z + relZ + 2.0 * kU) * 1.01;   // sum_k |p~_k - p_k|
+    const double dp = (bt / Z + relZ + 2.0 * kU) * 1.01;  // sum_k |p~_k - p_k|
     dC = kSafety * (dp + kU + kSumErr * total);
-    if (total <= kFallbackMass + 2.0 * dC) uncertain = true;
+    if (total <= kFallbackMass + 2.0 * dC) why |= kWhyFallback;
   } else {
     dC = kSafety * (bt + kSumErr * Z);
-    if (onehot) {
-      dcheck = dC / Z + relZ;
-      if (total / Z <= kFallbackMass + 2.0 * kSafety * dcheck) uncertain = true;
-    }
+    if (onehot && total / Z <= kFallbackMass + 2.0 * kSafety * (dC / Z + relZ)) why |= kWhyFallback;
   }
   const double tau = static_cast<double>(a.u[t.srow]) * total;
   if (tid == 0) {
     sh.found = 0;
-    sh.uncertain = uncertain ? 1 : 0;
+    sh.uncertain = static_cast<int>(why);
   }
   __syncthreads();
-  if (!uncertain && tau > 0.0 && excl < tau && incl >= tau) {
+  if (!why && tau > 0.0 && excl < tau && incl >= tau) {
     // same sequential association as tv, so the last partial equals tv
     double cl = 0.0;
     for (int j = tlo; j < thi; ++j) {
@@ -628,23 +981,24 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   }
   __syncthreads();
   if (!sh.found || sh.uncertain) {
-    exact_row<LT>(a, t, lrow, qrow, x, all_res, sc, sh);
+    const uint32_t w2 = sh.uncertain ? static_cast<uint32_t>(sh.uncertain) : kWhySearch;
+    if (tid == 0) flag_exact(a, t, w2, m);
     return;
   }
 
-  // ---------------- in-tile search: 4 consecutive elements per thread
+  // ---------------- in-tile search: kSearchPer consecutive elements per thread
   const int jt = sh.tile;
   const double pb = sh.p_before;
-  const int base = jt * kTile + 4 * tid;
-  float unit = 1.f;   // global units per local unit
-  float mref = m;     // exponent reference of the local weights
+  const int base = jt * kTile + kSearchPer * tid;
+  float unit = 1.f;  // global units per local unit
+  float mref = m;    // exponent reference of the local weights
   if (!mode_w) {
     mref = M[jt];
     unit = fexp2((M[jt] - m) * s);
   }
-  float w4[4];
+  float wl[kSearchPer];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < kSearchPer; ++e) {
     const int k = base + e;
     float w = 0.f;
     if (k < V) {
@@ -653,9 +1007,11 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
       if (mode_w) w = fmaxf(ek * izr - qrow[k], 0.f);
       else w = (k == xmask) ? 0.f : ek;
     }
-    w4[e] = w;
+    wl[e] = w;
   }
-  const float tsum = ((w4[0] + w4[1]) + w4[2]) + w4[3];
+  float tsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < kSearchPer; ++e) tsum += wl[e];
   const double tau_loc = (tau - pb) / static_cast<double>(unit);
   double e2, i2, tot2;
   block_scan(static_cast<double>(tsum), sc, e2, i2, tot2);
@@ -664,9 +1020,9 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   if (e2 < tau_loc && i2 >= tau_loc) {
     float cl = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < kSearchPer; ++e) {
       const float prev = cl;
-      cl += w4[e];
+      cl += wl[e];
       if (e2 + static_cast<double>(cl) >= tau_loc) {
         sh.token = base + e;
         sh.c_lo = pb + (e2 + static_cast<double>(prev)) * static_cast<double>(unit);
@@ -677,14 +1033,14 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
     }
   }
   __syncthreads();
-  bool ok = sh.found != 0;
-  if (ok) {
+  uint32_t why2 = sh.found ? 0u : kWhySearch;
+  if (!why2) {
     // unit conversion adds a relative rounding of ~3u to the local prefix
     const double d2 = 2.0 * (dC + 4.0 * kU * total);
-    ok = (tau - sh.c_lo) > d2 && (sh.c_hi - tau) > d2;
+    if (!((tau - sh.c_lo) > d2 && (sh.c_hi - tau) > d2)) why2 = kWhyMargin;
   }
-  if (!ok) {
-    exact_row<LT>(a, t, lrow, qrow, x, all_res, sc, sh);
+  if (why2) {
+    if (tid == 0) flag_exact(a, t, why2, m);
     return;
   }
   if (tid == 0) {
@@ -775,11 +1131,13 @@ struct SelectArgs {
   const int2* ws;
   int64_t* out;
   int32_t* nacc;
+  int* xcount;  // fp64-path list count, reset here for the next call (may be null)
   int B, gamma, ndraft;
 };
 
 __global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
   const int b = blockIdx.x * kSelectNT + threadIdx.x;
+  if (b == 0 && a.xcount) *a.xcount = 0;
   if (b >= a.B) return;
   int d0, d1;
   if (a.cu) {
@@ -805,25 +1163,75 @@ __global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// self-check of the exp2 accuracy the fast path's error bound assumes
+
+__global__ void zero_double_kernel(double* p) { *p = 0.0; }
+
+// Relative error of the hardware exp2 for every fp32 input in [-126, 0]
+// (bit patterns 0x80000000 .. 0xC2FC0000), against fp64 exp2; the maximum is
+// combined with an integer atomicMax on the bit pattern (non-negative doubles
+// order like their bit patterns).
+__global__ __launch_bounds__(kNT) void exp2_error_kernel(double* out) {
+  constexpr uint32_t kFirst = 0x80000000u, kLast = 0xC2FC0000u;
+  double mx = 0.0;
+  const uint32_t stride = gridDim.x * kNT;
+  for (uint32_t i = blockIdx.x * kNT + threadIdx.x; i <= kLast - kFirst; i += stride) {
+    const float x = __uint_as_float(kFirst + i);
+    const double ref = exp2(static_cast<double>(x));
+    const double got = static_cast<double>(fexp2(x));
+    mx = fmax(mx, fabs(got - ref) / ref);
+  }
+  __shared__ BlockScratch sc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) sc.d[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = sc.d[0];
+    for (int w = 1; w < kWaves; ++w) m = fmax(m, sc.d[w]);
+    atomicMax(reinterpret_cast<unsigned long long*>(out), static_cast<unsigned long long>(__double_as_longlong(m)));
+  }
+}
+
+// ----------------------------------------------------------------------------
 // host side
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-size_t ws_bytes(int64_t rows) {
-  const size_t b = static_cast<size_t>(rows) * sizeof(int2);
-  return (b + 255) & ~static_cast<size_t>(255);
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Workspace layout: [records rows x int2][count, 256 B][list rows x int2]
+// [etile rows x nt doubles][wtile rows x nt doubles].
+struct WsLayout {
+  size_t rec, count, list, etile, wtile, total;
+};
+WsLayout ws_layout(int64_t rows, int V) {
+  WsLayout l;
+  const size_t nt = static_cast<size_t>((V + kTile - 1) / kTile);
+  l.rec = 0;
+  l.count = align256(static_cast<size_t>(rows) * sizeof(int2));
+  l.list = l.count + 256;
+  l.etile = l.list + align256(static_cast<size_t>(rows) * sizeof(int2));
+  l.wtile = l.etile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
+  l.total = l.wtile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
+  return l;
 }
+size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
 
 template <typename LT>
-int launch_probs(const ProbsArgs& a, int64_t rows, hipStream_t st) {
+int launch_probs(const ProbsArgs& a, const ExactArgs& e, int64_t rows, hipStream_t st) {
   const int nt = (a.V + kTile - 1) / kTile;
-  const size_t lds = static_cast<size_t>(nt) * 3 * sizeof(float);
+  const size_t lds = static_cast<size_t>(nt) * 4 * sizeof(float);
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0 &&
                    (a.q == nullptr || (aligned16(a.q) && (a.V % 4) == 0));
   if (vec)
     hipLaunchKernelGGL((probs_rows_kernel<LT, true>), dim3(static_cast<unsigned>(rows)), dim3(kNT), lds, st, a);
   else
     hipLaunchKernelGGL((probs_rows_kernel<LT, false>), dim3(static_cast<unsigned>(rows)), dim3(kNT), lds, st, a);
+  hipLaunchKernelGGL((exact_tiles_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
+  hipLaunchKernelGGL((exact_residual_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
+  hipLaunchKernelGGL((exact_finish_kernel<LT>), dim3(kNT), dim3(kNT), static_cast<size_t>(e.nt) * 2 * sizeof(double),
+                     st, a, e);
   return 0;
 }
 
@@ -856,12 +1264,17 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
   if (!logits || !out || !nacc) return SV_ERR_INVALID_ARGUMENT;
   if (ndraft > 0 && !x) return SV_ERR_INVALID_ARGUMENT;
   if (!greedy_only && T > 0.0 && !u) return SV_ERR_INVALID_ARGUMENT;
-  if (!ws || ws_size < ws_bytes(rows) || (reinterpret_cast<uintptr_t>(ws) & 7u)) return SV_ERR_WORKSPACE;
+  const bool greedy = greedy_only || T == 0.0;
+  const WsLayout wl = ws_layout(rows, V);
+  if (!ws || ws_size < (greedy ? ws_bytes(rows) : wl.total) || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return SV_ERR_WORKSPACE;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
   int2* wsp = static_cast<int2*>(ws);
 
-  if (greedy_only || T == 0.0) {
+  char* wsb = static_cast<char*>(ws);
+  int* xcount = greedy ? nullptr : reinterpret_cast<int*>(wsb + wl.count);
+  if (greedy) {
     GreedyArgs g{logits, x, cu, wsp, B, gamma, ndraft, V};
     if (dtype == SV_DTYPE_BF16) launch_greedy<uint16_t>(g, rows, st);
     else launch_greedy<float>(g, rows, st);
@@ -882,12 +1295,21 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.ndraft = ndraft;
     p.V = V;
     p.flags = flags;
-    if (dtype == SV_DTYPE_BF16) launch_probs<uint16_t>(p, rows, st);
-    else launch_probs<float>(p, rows, st);
+    p.xcount = xcount;
+    p.xlist = reinterpret_cast<int2*>(wsb + wl.list);
+    ExactArgs e;
+    e.count = xcount;
+    e.list = p.xlist;
+    e.etile = reinterpret_cast<double*>(wsb + wl.etile);
+    e.wtile = reinterpret_cast<double*>(wsb + wl.wtile);
+    e.nt = (V + kTile - 1) / kTile;
+    e.rows = static_cast<int>(rows);
+    if (dtype == SV_DTYPE_BF16) launch_probs<uint16_t>(p, e, rows, st);
+    else launch_probs<float>(p, e, rows, st);
   }
   int rc = finish_launch();
   if (rc != SV_OK) return rc;
-  SelectArgs sa{x, cu, wsp, out, nacc, B, gamma, ndraft};
+  SelectArgs sa{x, cu, wsp, out, nacc, xcount, B, gamma, ndraft};
   hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>((B + kSelectNT - 1) / kSelectNT)), dim3(kSelectNT),
                      0, st, sa);
   return finish_launch();
@@ -897,9 +1319,9 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
 
 extern "C" {
 
-size_t spec_verify_workspace_size(int64_t num_target_rows) {
-  if (num_target_rows < 0) return 0;
-  return ws_bytes(num_target_rows);
+size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size) {
+  if (num_target_rows < 0 || vocab_size < 1 || vocab_size > SV_MAX_VOCAB) return 0;
+  return ws_layout(num_target_rows, vocab_size).total;
 }
 
 const char* spec_verify_status_string(int status) {
@@ -914,6 +1336,17 @@ const char* spec_verify_status_string(int status) {
 }
 
 int spec_verify_version(void) { return 1; }
+
+double spec_verify_exp2_error_bound(void) { return kEpsExp; }
+
+int spec_verify_selftest_exp2(double* max_rel_err, void* stream) {
+  if (!max_rel_err) return SV_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, st, max_rel_err);
+  hipLaunchKernelGGL(exp2_error_kernel, dim3(2048), dim3(kNT), 0, st, max_rel_err);
+  return finish_launch();
+}
 
 int spec_verify_probs(const void* target_logits, int logits_dtype, const float* draft_probs,
                       const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,

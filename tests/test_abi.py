@@ -51,10 +51,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert api.workspace_size(0) == 0
-    assert api.workspace_size(1) == 256
-    assert api.workspace_size(2048) == 2048 * 8
-    assert lib.spec_verify_workspace_size(-1) == 0
+    # records + count + list + two fp64 tile-sum arrays (nt = ceil(V / 2048))
+    assert api.workspace_size(1, 100) == 256 * 5
+    assert api.workspace_size(2048, 128256) == 2048 * 8 + 256 + 2048 * 8 + 2 * 2048 * 63 * 8
+    assert lib.spec_verify_workspace_size(-1, 100) == 0
+    assert lib.spec_verify_workspace_size(5, 0) == 0
+    assert lib.spec_verify_workspace_size(5, (1 << 21) + 1) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation or has B == 0
@@ -86,7 +88,8 @@ def probs(lib, **kw):
     (dict(stats=FAKE, T=0.0), -1),
     (dict(ws=None), -4),
     (dict(wsb=8 * 7), -4),
-    (dict(ws=ctypes.c_void_p(0x1004)), -4),
+    (dict(wsb=1279), -4),  # 8 rows, V=100 need 1280 bytes
+    (dict(ws=ctypes.c_void_p(0x1080)), -4),
     (dict(B=0), 0),
 ])
 def test_probs_argument_validation(lib, kw, status):

@@ -281,3 +281,11 @@ def test_out_of_range_draft_token_is_rejected():
     torch.cuda.synchronize()
     assert torch.all(nacc == 0)
     assert torch.all((out[:, 0] >= 0) & (out[:, 0] < 1000))
+
+
+def test_hardware_exp2_within_the_assumed_bound():
+    """The certified fast path assumes the fp32 exp2 instruction is accurate to
+    a stated relative error; measure it exhaustively on [-126, 0]."""
+    measured, assumed = api.selftest_exp2()
+    print(f"exp2 max relative error {measured:.3e} (assumed bound {assumed:.3e})")
+    assert 0.0 < measured <= assumed
