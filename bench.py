@@ -76,7 +76,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="peaked_bf16")
-    ap.add_argument("--flags", type=int, default=0, help="SV_FLAG_* bits passed to the library")
+    ap.add_argument("--flags", type=int, default=0,
+                    help="SV_FLAG_* bits passed to the library (0: lazy residuals, 4: eager, 2: all residuals)")
     ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -69,9 +69,17 @@ enum sv_status {
 /* Largest supported vocabulary. */
 #define SV_MAX_VOCAB (1 << 21)
 
-/* flags for spec_verify_probs / spec_verify_ragged */
+/* flags for spec_verify_probs / spec_verify_ragged. The three ways of drawing
+ * replacements give identical results; they differ in the bytes they read:
+ *  default (lazy): pass 1 over the logits of every row decides every accept
+ *    test; the residual max(0, p - q) is then drawn only at each request's
+ *    first rejection (the logits and q of that one row are read again).
+ *  SV_FLAG_EAGER: every draft row whose own accept test fails draws its
+ *    replacement in the same launch (speculatively; most are unused).
+ *  SV_FLAG_ALL_RESIDUALS: every draft row draws its replacement. */
 #define SV_FLAG_EXACT 0x1u         /* take every row through the fp64 path (reference / testing) */
 #define SV_FLAG_ALL_RESIDUALS 0x2u /* draw the replacement token of every draft row, accepted or not */
+#define SV_FLAG_EAGER 0x4u         /* draw the replacement of every locally rejected draft row */
 
 /* Workspace: device memory of spec_verify_workspace_size() bytes, 256-byte
  * aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call leaves it ready for
@@ -89,6 +97,7 @@ enum sv_status {
 #define SV_ROW_WHY_SEARCH 0x40u    /* inverse-CDF search inconclusive in fp32 */
 #define SV_ROW_WHY_MARGIN 0x80u    /* sample uniform within the bound of a CDF boundary */
 #define SV_ROW_WHY_FORCED 0x100u   /* SV_FLAG_EXACT, or a degenerate row */
+#define SV_ROW_DEFERRED 0x400u     /* lazy mode: rejected row whose replacement was not needed (not drawn) */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of
@@ -134,6 +143,7 @@ double spec_verify_exp2_error_bound(void);
  *                 {max(l/T), ln sum exp(l/T - max), p(x), R}; R = sum
  *                 max(0, p - q) for draft rows; p(x) = NaN and R = 1 for bonus
  *                 rows. Requires T > 0. Implies SV_FLAG_ALL_RESIDUALS.
+ *                 Statistics come at the cost of reading every q row.
  *  workspace      device scratch of at least
  *                 spec_verify_workspace_size(B * (gamma + 1), V) bytes, see
  *                 the workspace note above.

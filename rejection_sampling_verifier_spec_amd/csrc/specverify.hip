@@ -10,27 +10,32 @@
 // emitted token, drawn from norm(max(0, p_n - q_n)) (from p_n when that mass
 // is <= 1e-8, timinsight.com "Step 2") or from p_{g+1} when all drafts pass.
 //
-// Kernel design (MI355X: 256 CUs, wave64, 160 KB LDS per CU, ~8 TB/s HBM):
-//  * one 256-thread block per target row; draft rows are dispatched first and
-//    bonus rows last, so the round-robin dispatch over the 8 XCDs spreads the
-//    heavy rows (logits + q) evenly and the light rows fill the tail;
-//  * a row is cut into 1024-element tiles; wave w streams tiles w, w+4, ...
-//    with 16-byte loads, 16 elements per lane per tile; each tile leaves one
-//    float (its sum) and, in the logits pass, its own max in LDS, so the
-//    inverse-CDF search later re-reads a single tile;
-//  * pass 1 reads the logits: tile max and sum of exp2((l - max_tile) s);
-//    pass 2 (draft rows with q whose replacement is needed) re-reads the
-//    logits (L2 / MALL resident by then) and reads q once: tile sums of
-//    max(0, p - q);
+// Kernel design (MI355X: 256 CUs in 8 XCDs, wave64, 160 KB LDS per CU,
+// ~8 TB/s HBM3E; the path is bandwidth-bound, there is no dense contraction):
+//  * one 512-thread block (8 waves) per target row; draft rows are dispatched
+//    first and bonus rows last, so the round-robin dispatch over the XCDs
+//    spreads the heavy rows (logits + q) evenly and light rows fill the tail;
+//  * a row is cut into 2048-element tiles; wave w streams tiles w, w+8, ...
+//    with 16-byte loads (32 elements per lane per tile), double-buffered so the
+//    next tile's loads are in flight while one is reduced; loads are issued
+//    unconditionally (addresses clamped into the row) so the compiler waits
+//    only for the tile it consumes. Each tile leaves its sum (and, in the
+//    logits pass, its running max) in LDS, so the inverse-CDF search re-reads
+//    one tile only;
+//  * pass 1 reads the logits: running row max per wave and the tile sums of
+//    exp2((l - M_j) s), one sweep per tile (a ballot re-sums a tile that
+//    raised the maximum); pass 2 (draft rows with q whose replacement is
+//    needed) re-reads the logits and reads q once: tile sums of max(0, p - q);
 //  * every row computes its replacement or bonus sample in parallel
-//    (speculatively); a tiny select kernel then picks, per request, the
-//    first rejection. A draft row whose own test passes skips its residual
-//    (its sample can never be emitted) unless SV_FLAG_ALL_RESIDUALS is set.
+//    (speculatively); a select kernel then picks, per request, the first
+//    rejection. A draft row whose own test passes skips its residual (its
+//    sample can never be emitted) unless SV_FLAG_ALL_RESIDUALS is set;
 //  * exactness: the fp32 fast path carries a rigorous error bound for Z, for
 //    every prefix of the sampling CDF and for p(x). When the accept decision,
 //    the 1e-8 fallback decision or the sampled token is not separated from its
-//    threshold by twice the bound, the block recomputes the whole row in fp64
-//    (exact_row). Results therefore equal exact arithmetic except within ~1e-15
+//    threshold by twice the bound, the row is appended to a list and
+//    recomputed in fp64 by three small kernels that spread the work over the
+//    whole GPU. Results therefore equal exact arithmetic except within ~1e-15
 //    relative of a decision boundary.
 //
 // All kernels read inputs only in bounds, whatever the device-side inputs
@@ -45,11 +50,10 @@
 
 namespace {
 
-constexpr int kNT = 256;                // threads per row block
+constexpr int kNT = 256;                // threads per block of the fixed-size kernels
 constexpr int kWaves = kNT / 64;        // waves per row block
 constexpr int kTile = 2048;             // elements per tile (one wave, 32 per lane)
 constexpr int kLaneElems = kTile / 64;  // 32
-constexpr int kSearchPer = kTile / kNT; // elements per thread in the in-tile search
 constexpr int kSelectNT = 256;
 
 // ----------------------------------------------------------------------------
@@ -276,13 +280,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
-struct BlockScratch {
-  double d[kNT];
-  int i[kNT];
+template <int NT>
+struct BlockScratchT {
+  double d[NT];
 };
+using BlockScratch = BlockScratchT<kNT>;
 
 // Sum over the block in a fixed order; every thread gets the same value.
-__device__ double block_sum(double v, BlockScratch& s) {
+template <int NT>
+__device__ double block_sum(double v, BlockScratchT<NT>& s) {
+  constexpr int kWaves = NT / 64;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -295,7 +302,34 @@ __device__ double block_sum(double v, BlockScratch& s) {
   return r;
 }
 
-__device__ float block_max(float v, BlockScratch& s) {
+// Two fixed-order block sums with one pair of barriers.
+template <int NT>
+__device__ void block_sum2(double v, double w, BlockScratchT<NT>& s, double& rv, double& rw) {
+  constexpr int kWaves = NT / 64;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    v += __shfl_xor(v, o);
+    w += __shfl_xor(w, o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s.d[wave] = v;
+    s.d[kWaves + wave] = w;
+  }
+  __syncthreads();
+  rv = 0.0;
+  rw = 0.0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    rv += s.d[k];
+    rw += s.d[kWaves + k];
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ float block_max(float v, BlockScratchT<NT>& s) {
+  constexpr int kWaves = NT / 64;
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) s.d[wave] = v;
@@ -310,7 +344,9 @@ __device__ float block_max(float v, BlockScratch& s) {
 // Exclusive scan over the block's threads in thread order. Thread t gets
 // excl_t and incl_t with incl_t == excl_{t+1} bit for bit; `total` is the
 // inclusive value of the last thread.
-__device__ void block_scan(double v, BlockScratch& s, double& excl, double& incl, double& total) {
+template <int NT>
+__device__ void block_scan(double v, BlockScratchT<NT>& s, double& excl, double& incl, double& total) {
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double x = v;
 #pragma unroll
@@ -334,7 +370,7 @@ __device__ void block_scan(double v, BlockScratch& s, double& excl, double& incl
   incl = off + x;
   total = tot;
   // make `total` identical to the last thread's incl
-  if (threadIdx.x == kNT - 1) s.d[0] = incl;
+  if (threadIdx.x == NT - 1) s.d[0] = incl;
   __syncthreads();
   total = s.d[0];
   __syncthreads();
@@ -415,6 +451,7 @@ struct ProbsArgs {
   uint32_t flags;
   int* xcount;    // list of rows for the fp64 path (see ExactArgs)
   int2* xlist;
+  double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
 };
 
 struct RowShared {
@@ -460,6 +497,8 @@ __device__ __forceinline__ float logit_at(const LT* row, int64_t k) {
 // With an empty list each kernel reads the count and exits.
 
 constexpr uint32_t kRowNeedExact = 0x200u;  // set by the fast kernel, cleared by exact_finish_kernel
+constexpr uint32_t kRowDeferred = SV_ROW_DEFERRED;
+constexpr uint32_t kFlagLazy = 0x80000000u;  // internal: set by the host for the lazy mode
 constexpr int kExactGrid = 512;             // blocks of the item kernels
 constexpr int kExactPer = kTile / kNT;      // elements per thread of one tile (8)
 
@@ -721,10 +760,13 @@ __global__ __launch_bounds__(kNT) void exact_finish_kernel(ProbsArgs a, ExactArg
 }
 
 // Hand a row to the fp64 path: mark its record and append it to the list.
-__device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, uint32_t why, float m) {
-  a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowNeedExact | why));
+__device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, uint32_t why, float m,
+                                           bool accepted = false) {
+  // the accept bit is meaningful unless the accept test itself is the reason
+  a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowNeedExact | why | (accepted ? kRowAccepted : 0u)));
   const int pos = atomicAdd(a.xcount, 1);
-  if (pos < a.B + a.ndraft) a.xlist[pos] = make_int2(static_cast<int>(blockIdx.x), __float_as_int(m));
+  const int blk = t.drow >= 0 ? static_cast<int>(t.drow) : a.ndraft + t.b;  // the row's index in the rows grid
+  if (pos < a.B + a.ndraft) a.xlist[pos] = make_int2(blk, __float_as_int(m));
 }
 
 // Reasons a row was recomputed on the fp64 path (row_flags bits 4..8).
@@ -734,10 +776,184 @@ constexpr uint32_t kWhySearch = SV_ROW_WHY_SEARCH;
 constexpr uint32_t kWhyMargin = SV_ROW_WHY_MARGIN;
 constexpr uint32_t kWhyForced = SV_ROW_WHY_FORCED;
 
-template <typename LT, bool VEC>
-__global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
+// Draws the token of one row and certifies it: the replacement of a draft row
+// with q (pass 2 over logits and q, then the tile and in-tile search), or the
+// p-based sample of a bonus or one-hot row from the pass-1 tile sums S, M.
+// Writes the row's record (and statistics), or hands the row to the fp64 path.
+// Called by every thread of the block.
+template <typename LT, bool VEC, int NT, bool WITH_Q>
+__device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restrict__ lrow,
+                           const float* __restrict__ qrow, int xmask, bool accepted, float m, double Z, double bt,
+                           double relZ, double px, const float* S, const float* M, float* W,
+                           BlockScratchT<NT>& sc, RowShared& sh) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kSearchPer = kTile / NT;  // elements per thread in the in-tile search
+  const int V = a.V;
+  const int nt = (V + kTile - 1) / kTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float s = a.s32;
+  const bool is_draft = t.drow >= 0;
+  const bool onehot = is_draft && qrow == nullptr;
+  const bool want_stats = a.stats != nullptr;
+  using Raw = RawTile<LT, VEC>;
+
+  // ---------------- pass 2: residual tile sums (draft rows with q)
+  const bool mode_w = WITH_Q && qrow != nullptr;
+  const float izr = static_cast<float>(1.0 / Z);
+  if constexpr (WITH_Q) if (mode_w) {
+    for (int j = wave; j < nt; j += kWaves) {
+      const int base = j * kTile;
+      Raw r;
+      float q[kLaneElems];
+      r.load(lrow, V, base, lane);
+      load_q<LT, VEC>(qrow, V, base, lane, q);
+      float w4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
+#pragma unroll
+        for (int k = g8; k < g8 + 8; ++k) {
+          const float p = fexp2((r.get(k) - m) * s) * izr;
+          w4[k & 3] += fmaxf(p - q[k], 0.f);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float ws = (w4[0] + w4[1]) + (w4[2] + w4[3]);
+      ws = wave_sum(ws);
+      if (lane == 0) W[j] = ws;
+    }
+    __syncthreads();
+  }
+
+  // ---------------- tile-level CDF: prefix over tiles in token order
+  // value of tile j in global units: W[j] (p-units) or S[j] * f_j (e-units)
+  auto tile_val = [&](int j) -> double {
+    if (mode_w) return static_cast<double>(W[j]);
+    const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
+    return static_cast<double>(S[j] * f);
+  };
+  const int tper = (nt + NT - 1) / NT;
+  const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
+  double tv = 0.0;
+  for (int j = tlo; j < thi; ++j) tv += tile_val(j);
+  double excl, incl, total;
+  block_scan(tv, sc, excl, incl, total);
+
+  // error bound of every CDF prefix (same units as total)
+  double dC;
+  uint32_t why = 0;
+  if (mode_w) {
+    const double dp = (bt / Z + relZ + 2.0 * kU) * 1.01;  // sum_k |p~_k - p_k|
+    dC = kSafety * (dp + kU + kSumErr * total);
+    if (total <= kFallbackMass + 2.0 * dC) why |= kWhyFallback;
+  } else {
+    dC = kSafety * (bt + kSumErr * Z);
+    if (onehot && total / Z <= kFallbackMass + 2.0 * kSafety * (dC / Z + relZ)) why |= kWhyFallback;
+  }
+  const double tau = static_cast<double>(a.u[t.srow]) * total;
+  if (tid == 0) {
+    sh.found = 0;
+    sh.uncertain = static_cast<int>(why);
+  }
+  __syncthreads();
+  if (!why && tau > 0.0 && excl < tau && incl >= tau) {
+    // same sequential association as tv, so the last partial equals tv
+    double cl = 0.0;
+    for (int j = tlo; j < thi; ++j) {
+      const double prev = cl;
+      cl += tile_val(j);
+      if (excl + cl >= tau) {
+        sh.tile = j;
+        sh.p_before = excl + prev;
+        sh.found = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (!sh.found || sh.uncertain) {
+    const uint32_t w2 = sh.uncertain ? static_cast<uint32_t>(sh.uncertain) : kWhySearch;
+    if (tid == 0) flag_exact(a, t, w2, m, accepted);
+    return;
+  }
+
+  // ---------------- in-tile search: kSearchPer consecutive elements per thread
+  const int jt = sh.tile;
+  const double pb = sh.p_before;
+  const int base = jt * kTile + kSearchPer * tid;
+  float unit = 1.f;  // global units per local unit
+  float mref = m;    // exponent reference of the local weights
+  if (!mode_w) {
+    mref = M[jt];
+    unit = fexp2((M[jt] - m) * s);
+  }
+  float wl[kSearchPer];
+#pragma unroll
+  for (int e = 0; e < kSearchPer; ++e) {
+    const int k = base + e;
+    float w = 0.f;
+    if (k < V) {
+      const float l = to_float(lrow[k]);
+      const float ek = fexp2((l - mref) * s);
+      if (WITH_Q && mode_w) w = fmaxf(ek * izr - qrow[k], 0.f);
+      else w = (k == xmask) ? 0.f : ek;
+    }
+    wl[e] = w;
+  }
+  float tsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < kSearchPer; ++e) tsum += wl[e];
+  const double tau_loc = (tau - pb) / static_cast<double>(unit);
+  double e2, i2, tot2;
+  block_scan(static_cast<double>(tsum), sc, e2, i2, tot2);
+  if (tid == 0) sh.found = 0;
+  __syncthreads();
+  if (e2 < tau_loc && i2 >= tau_loc) {
+    float cl = 0.f;
+#pragma unroll
+    for (int e = 0; e < kSearchPer; ++e) {
+      const float prev = cl;
+      cl += wl[e];
+      if (e2 + static_cast<double>(cl) >= tau_loc) {
+        sh.token = base + e;
+        sh.c_lo = pb + (e2 + static_cast<double>(prev)) * static_cast<double>(unit);
+        sh.c_hi = pb + (e2 + static_cast<double>(cl)) * static_cast<double>(unit);
+        sh.found = 1;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t why2 = sh.found ? 0u : kWhySearch;
+  if (!why2) {
+    // unit conversion adds a relative rounding of ~3u to the local prefix
+    const double d2 = 2.0 * (dC + 4.0 * kU * total);
+    if (!((tau - sh.c_lo) > d2 && (sh.c_hi - tau) > d2)) why2 = kWhyMargin;
+  }
+  if (why2) {
+    if (tid == 0) flag_exact(a, t, why2, m, accepted);
+    return;
+  }
+  if (tid == 0) {
+    uint32_t fl = (accepted ? kRowAccepted : 0u) | (is_draft ? kRowResidual : 0u);
+    a.ws[t.trow] = make_int2(sh.token, static_cast<int>(fl));
+    if (want_stats) {
+      float* st = a.stats + t.trow * 4;
+      st[0] = static_cast<float>(static_cast<double>(m) / a.temperature);
+      st[1] = static_cast<float>(log(Z));
+      st[2] = is_draft ? static_cast<float>(px) : NAN;
+      st[3] = is_draft ? static_cast<float>(mode_w ? total : total / Z) : 1.f;
+    }
+  }
+}
+
+// EAGER: rejected draft rows with q draw their replacement here (eager and
+// all-residual modes); otherwise (lazy mode) they are deferred, and the kernel
+// has no q pass at all.
+template <typename LT, bool VEC, int NT, bool EAGER>
+__global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
+  constexpr int kWaves = NT / 64;
   extern __shared__ float dyn[];
-  __shared__ BlockScratch sc;
+  __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
   using L = Lay<LT, VEC>;
   using Raw = RawTile<LT, VEC>;
@@ -762,6 +978,10 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
   const float s = a.s32;
   const bool want_stats = a.stats != nullptr;
   const bool all_res = (a.flags & SV_FLAG_ALL_RESIDUALS) || want_stats;
+  // the accept test's inputs, loaded now so that they arrive during pass 1
+  const float lx = x_ok ? to_float(lrow[x]) : -INFINITY;
+  const float qx_in = (x_ok && qrow) ? qrow[x] : 0.f;
+  const float u_acc = is_draft ? a.u[t.trow] : 0.f;
 
   // ---------------- pass 1: tile sums of exp2((l - M_j) s), M_j = the wave's
   // running maximum when tile j is reduced. One sweep per tile: the exps are
@@ -847,10 +1067,10 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
 
   // row max and Z (e-units relative to the row max)
   float mloc = -INFINITY;
-  for (int j = tid; j < nt; j += kNT) mloc = fmaxf(mloc, M[j]);
+  for (int j = tid; j < nt; j += NT) mloc = fmaxf(mloc, M[j]);
   const float m = block_max(mloc, sc);
   double zl = 0.0, eal = 0.0;
-  for (int j = tid; j < nt; j += kNT) {
+  for (int j = tid; j < nt; j += NT) {
     const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
     zl += static_cast<double>(S[j] * f);
     // e_k |a_k| relative to m: |a_k| = |a_k, local| + (m - M_j) s
@@ -858,17 +1078,13 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
       eal += static_cast<double>(f) *
              (static_cast<double>(EA[j]) + (static_cast<double>(m) - M[j]) * a.s64 * static_cast<double>(S[j]));
   }
-  float ex = 0.f, lx = -INFINITY;
-  if (x_ok) {
-    lx = to_float(lrow[x]);
-    ex = fexp2((lx - m) * s);
-  }
   if (tid == 0 && xmask >= 0) {  // one-hot rows left x out of S
+    const float ex = fexp2((lx - m) * s);
     zl += static_cast<double>(ex);
     eal += static_cast<double>(ex) * (static_cast<double>(m) - lx) * a.s64;
   }
-  const double Z = block_sum(zl, sc);
-  const double sea = block_sum(eal, sc);
+  double Z, sea;
+  block_sum2(zl, eal, sc, Z, sea);
   const double bt = bound_terms(Z, sea);
   const double dZ = bt + kSumErr * Z;  // |Z~ - Z|
   const double relZ = dZ / Z;
@@ -882,8 +1098,8 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
     double px = 0.0;
     if (is_draft) {
       if (x_ok) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64) / Z;
-      const double qx = onehot ? 1.0 : (x_ok ? static_cast<double>(qrow[x]) : 0.0);
-      const double lhs = static_cast<double>(a.u[t.trow]) * qx;
+      const double qx = onehot ? 1.0 : static_cast<double>(qx_in);
+      const double lhs = static_cast<double>(u_acc) * qx;
       accepted = (x_ok && px > 0.0 && lhs <= px) ? 1 : 0;
       if (x_ok) {
         const double dpx = kSafety * (px * relZ * 1.01) + 1e-300;
@@ -907,153 +1123,68 @@ __global__ __launch_bounds__(kNT) void probs_rows_kernel(ProbsArgs a) {
     return;
   }
 
-  // ---------------- pass 2: residual tile sums (draft rows with q)
-  const bool mode_w = qrow != nullptr;
-  const float izr = static_cast<float>(1.0 / Z);
-  if (mode_w) {
-    for (int j = wave; j < nt; j += kWaves) {
-      const int base = j * kTile;
-      Raw r;
-      float q[kLaneElems];
-      r.load(lrow, V, base, lane);
-      load_q<LT, VEC>(qrow, V, base, lane, q);
-      float w4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
-#pragma unroll
-        for (int k = g8; k < g8 + 8; ++k) {
-          const float p = fexp2((r.get(k) - m) * s) * izr;
-          w4[k & 3] += fmaxf(p - q[k], 0.f);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      float ws = (w4[0] + w4[1]) + (w4[2] + w4[3]);
-      ws = wave_sum(ws);
-      if (lane == 0) W[j] = ws;
+  // a rejected draft row with q: in the lazy mode its residual is drawn later,
+  // and only if it is the request's first rejection
+  if (!EAGER && qrow != nullptr && !accepted && !all_res) {
+    if (tid == 0) {
+      a.rstat[t.trow] = make_double4(static_cast<double>(m), Z, sea, 0.0);
+      a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowDeferred));
     }
-    __syncthreads();
+    return;
   }
+  sample_row<LT, VEC, NT, EAGER>(a, t, lrow, qrow, xmask, accepted, m, Z, bt, relZ, sh.px, S, M, W, sc, sh);
+}
 
-  // ---------------- tile-level CDF: prefix over tiles in token order
-  // value of tile j in global units: W[j] (p-units) or S[j] * f_j (e-units)
-  auto tile_val = [&](int j) -> double {
-    if (mode_w) return static_cast<double>(W[j]);
-    const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
-    return static_cast<double>(S[j] * f);
-  };
-  const int tper = (nt + kNT - 1) / kNT;
-  const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
-  double tv = 0.0;
-  for (int j = tlo; j < thi; ++j) tv += tile_val(j);
-  double excl, incl, total;
-  block_scan(tv, sc, excl, incl, total);
-
-  // error bound of every CDF prefix (same units as total)
-  double dC;
-  uint32_t why = 0;
-  if (mode_w) {
-    const double dp = (bt / Z + relZ + 2.0 * kU) * 1.01;  // sum_k |p~_k - p_k|
-    dC = kSafety * (dp + kU + kSumErr * total);
-    if (total <= kFallbackMass + 2.0 * dC) why |= kWhyFallback;
+// ----------------------------------------------------------------------------
+// lazy mode, phase 2: one block per request. The first draft row that is
+// certainly rejected decides the emitted token; if its residual was deferred,
+// it is drawn here. Rows whose accept test was left to the fp64 path are
+// passed over (that path decides them, and draws their token if they are
+// rejected), so the row drawn here may turn out unused; the select kernel
+// settles the request from the final records.
+template <typename LT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void residual_request_kernel(ProbsArgs a) {
+  extern __shared__ float dynw[];  // residual tile sums of the row drawn here
+  __shared__ BlockScratchT<NT> sc;
+  __shared__ RowShared sh;
+  const int b = blockIdx.x;
+  int d0, d1;
+  if (a.cu) {
+    d0 = a.cu[b];
+    d1 = a.cu[b + 1];
+    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) return;
   } else {
-    dC = kSafety * (bt + kSumErr * Z);
-    if (onehot && total / Z <= kFallbackMass + 2.0 * kSafety * (dC / Z + relZ)) why |= kWhyFallback;
+    d0 = b * a.gamma;
+    d1 = d0 + a.gamma;
   }
-  const double tau = static_cast<double>(a.u[t.srow]) * total;
-  if (tid == 0) {
-    sh.found = 0;
-    sh.uncertain = static_cast<int>(why);
+  const int g = d1 - d0;
+  const int64_t t0 = static_cast<int64_t>(d0) + b;
+  int n = g;
+  for (int i = 0; i < g; ++i) {
+    const uint32_t f = static_cast<uint32_t>(a.ws[t0 + i].y);
+    if ((f & kRowNeedExact) && (f & (kWhyAccept | kWhyForced))) continue;
+    if (f & kRowAccepted) continue;
+    n = i;
+    break;
   }
-  __syncthreads();
-  if (!why && tau > 0.0 && excl < tau && incl >= tau) {
-    // same sequential association as tv, so the last partial equals tv
-    double cl = 0.0;
-    for (int j = tlo; j < thi; ++j) {
-      const double prev = cl;
-      cl += tile_val(j);
-      if (excl + cl >= tau) {
-        sh.tile = j;
-        sh.p_before = excl + prev;
-        sh.found = 1;
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  if (!sh.found || sh.uncertain) {
-    const uint32_t w2 = sh.uncertain ? static_cast<uint32_t>(sh.uncertain) : kWhySearch;
-    if (tid == 0) flag_exact(a, t, w2, m);
-    return;
-  }
-
-  // ---------------- in-tile search: kSearchPer consecutive elements per thread
-  const int jt = sh.tile;
-  const double pb = sh.p_before;
-  const int base = jt * kTile + kSearchPer * tid;
-  float unit = 1.f;  // global units per local unit
-  float mref = m;    // exponent reference of the local weights
-  if (!mode_w) {
-    mref = M[jt];
-    unit = fexp2((M[jt] - m) * s);
-  }
-  float wl[kSearchPer];
-#pragma unroll
-  for (int e = 0; e < kSearchPer; ++e) {
-    const int k = base + e;
-    float w = 0.f;
-    if (k < V) {
-      const float l = to_float(lrow[k]);
-      const float ek = fexp2((l - mref) * s);
-      if (mode_w) w = fmaxf(ek * izr - qrow[k], 0.f);
-      else w = (k == xmask) ? 0.f : ek;
-    }
-    wl[e] = w;
-  }
-  float tsum = 0.f;
-#pragma unroll
-  for (int e = 0; e < kSearchPer; ++e) tsum += wl[e];
-  const double tau_loc = (tau - pb) / static_cast<double>(unit);
-  double e2, i2, tot2;
-  block_scan(static_cast<double>(tsum), sc, e2, i2, tot2);
-  if (tid == 0) sh.found = 0;
-  __syncthreads();
-  if (e2 < tau_loc && i2 >= tau_loc) {
-    float cl = 0.f;
-#pragma unroll
-    for (int e = 0; e < kSearchPer; ++e) {
-      const float prev = cl;
-      cl += wl[e];
-      if (e2 + static_cast<double>(cl) >= tau_loc) {
-        sh.token = base + e;
-        sh.c_lo = pb + (e2 + static_cast<double>(prev)) * static_cast<double>(unit);
-        sh.c_hi = pb + (e2 + static_cast<double>(cl)) * static_cast<double>(unit);
-        sh.found = 1;
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  uint32_t why2 = sh.found ? 0u : kWhySearch;
-  if (!why2) {
-    // unit conversion adds a relative rounding of ~3u to the local prefix
-    const double d2 = 2.0 * (dC + 4.0 * kU * total);
-    if (!((tau - sh.c_lo) > d2 && (sh.c_hi - tau) > d2)) why2 = kWhyMargin;
-  }
-  if (why2) {
-    if (tid == 0) flag_exact(a, t, why2, m);
-    return;
-  }
-  if (tid == 0) {
-    uint32_t fl = (accepted ? kRowAccepted : 0u) | (is_draft ? kRowResidual : 0u);
-    a.ws[t.trow] = make_int2(sh.token, static_cast<int>(fl));
-    if (want_stats) {
-      float* st = a.stats + t.trow * 4;
-      st[0] = static_cast<float>(static_cast<double>(m) / a.temperature);
-      st[1] = static_cast<float>(log(Z));
-      st[2] = is_draft ? static_cast<float>(sh.px) : NAN;
-      st[3] = is_draft ? static_cast<float>(mode_w ? total : total / Z) : 1.f;
-    }
-  }
+  if (n == g) return;
+  if (!(static_cast<uint32_t>(a.ws[t0 + n].y) & kRowDeferred)) return;
+  Task t;
+  t.b = b;
+  t.g = g;
+  t.i = n;
+  t.trow = t0 + n;
+  t.drow = d0 + n;
+  t.srow = static_cast<int64_t>(d1) + b;
+  t.valid = true;
+  const double4 st = a.rstat[t.trow];
+  const float m = static_cast<float>(st.x);
+  const double Z = st.y;
+  const double bt = bound_terms(Z, st.z);
+  const double relZ = (bt + kSumErr * Z) / Z;
+  const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(a.V);
+  const float* __restrict__ qrow = a.q + t.drow * static_cast<int64_t>(a.V);
+  sample_row<LT, VEC, NT, true>(a, t, lrow, qrow, -1, false, m, Z, bt, relZ, 0.0, nullptr, nullptr, dynw, sc, sh);
 }
 
 // ----------------------------------------------------------------------------
@@ -1201,9 +1332,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layout: [records rows x int2][count, 256 B][list rows x int2]
-// [etile rows x nt doubles][wtile rows x nt doubles].
+// [etile rows x nt doubles][wtile rows x nt doubles][rstat rows x 4 doubles].
 struct WsLayout {
-  size_t rec, count, list, etile, wtile, total;
+  size_t rec, count, list, etile, wtile, rstat, total;
 };
 WsLayout ws_layout(int64_t rows, int V) {
   WsLayout l;
@@ -1213,10 +1344,24 @@ WsLayout ws_layout(int64_t rows, int V) {
   l.list = l.count + 256;
   l.etile = l.list + align256(static_cast<size_t>(rows) * sizeof(int2));
   l.wtile = l.etile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
-  l.total = l.wtile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
+  l.rstat = l.wtile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
+  l.total = l.rstat + align256(static_cast<size_t>(rows) * 4 * sizeof(double));
   return l;
 }
 size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
+
+// Block sizes: the lazy first pass reads logits only and keeps more rows in
+// flight with small blocks; the eager modes and the per-request second pass
+// stream logits and q per row and prefer larger blocks (shorter per-row time).
+constexpr int kRowsNTLazy = 256;
+constexpr int kRowsNTEager = 512;
+constexpr int kRequestNT = 512;
+
+template <typename LT, bool VEC, int NT, bool EAGER>
+void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT, EAGER>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st,
+                     a);
+}
 
 template <typename LT>
 int launch_probs(const ProbsArgs& a, const ExactArgs& e, int64_t rows, hipStream_t st) {
@@ -1224,10 +1369,23 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, int64_t rows, hipStream
   const size_t lds = static_cast<size_t>(nt) * 4 * sizeof(float);
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0 &&
                    (a.q == nullptr || (aligned16(a.q) && (a.V % 4) == 0));
-  if (vec)
-    hipLaunchKernelGGL((probs_rows_kernel<LT, true>), dim3(static_cast<unsigned>(rows)), dim3(kNT), lds, st, a);
-  else
-    hipLaunchKernelGGL((probs_rows_kernel<LT, false>), dim3(static_cast<unsigned>(rows)), dim3(kNT), lds, st, a);
+  const bool lazy = (a.flags & kFlagLazy) != 0;
+  if (vec) {
+    if (lazy) launch_rows<LT, true, kRowsNTLazy, false>(a, rows, lds, st);
+    else launch_rows<LT, true, kRowsNTEager, true>(a, rows, lds, st);
+  } else {
+    if (lazy) launch_rows<LT, false, kRowsNTLazy, false>(a, rows, lds, st);
+    else launch_rows<LT, false, kRowsNTEager, true>(a, rows, lds, st);
+  }
+  if (lazy) {
+    const size_t lds2 = static_cast<size_t>(nt) * sizeof(float);
+    if (vec)
+      hipLaunchKernelGGL((residual_request_kernel<LT, true, kRequestNT>), dim3(static_cast<unsigned>(a.B)),
+                         dim3(kRequestNT), lds2, st, a);
+    else
+      hipLaunchKernelGGL((residual_request_kernel<LT, false, kRequestNT>), dim3(static_cast<unsigned>(a.B)),
+                         dim3(kRequestNT), lds2, st, a);
+  }
   hipLaunchKernelGGL((exact_tiles_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
   hipLaunchKernelGGL((exact_residual_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
   hipLaunchKernelGGL((exact_finish_kernel<LT>), dim3(kNT), dim3(kNT), static_cast<size_t>(e.nt) * 2 * sizeof(double),
@@ -1256,7 +1414,8 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
   if (B < 0 || gamma < 0 || ndraft < 0 || V < 1) return SV_ERR_INVALID_ARGUMENT;
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!(T >= 0.0) || !isfinite(T)) return SV_ERR_INVALID_ARGUMENT;
-  if (flags & ~static_cast<uint32_t>(SV_FLAG_EXACT | SV_FLAG_ALL_RESIDUALS)) return SV_ERR_INVALID_ARGUMENT;
+  if (flags & ~static_cast<uint32_t>(SV_FLAG_EXACT | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EAGER))
+    return SV_ERR_INVALID_ARGUMENT;
   if (stats && !(T > 0.0)) return SV_ERR_INVALID_ARGUMENT;
   const int64_t rows = static_cast<int64_t>(ndraft) + B;
   if (rows > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
@@ -1294,7 +1453,9 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.gamma = gamma;
     p.ndraft = ndraft;
     p.V = V;
-    p.flags = flags;
+    const bool lazy = !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS)) && stats == nullptr && q != nullptr;
+    p.flags = flags | (lazy ? kFlagLazy : 0u);
+    p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.xcount = xcount;
     p.xlist = reinterpret_cast<int2*>(wsb + wl.list);
     ExactArgs e;

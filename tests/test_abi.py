@@ -51,9 +51,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # records + count + list + two fp64 tile-sum arrays (nt = ceil(V / 2048))
-    assert api.workspace_size(1, 100) == 256 * 5
-    assert api.workspace_size(2048, 128256) == 2048 * 8 + 256 + 2048 * 8 + 2 * 2048 * 63 * 8
+    # records + count + list + two fp64 tile-sum arrays (nt = ceil(V / 2048)) + per-row {m, Z, bound}
+    assert api.workspace_size(1, 100) == 256 * 6
+    assert api.workspace_size(2048, 128256) == 2048 * 8 + 256 + 2048 * 8 + 2 * 2048 * 63 * 8 + 2048 * 32
     assert lib.spec_verify_workspace_size(-1, 100) == 0
     assert lib.spec_verify_workspace_size(5, 0) == 0
     assert lib.spec_verify_workspace_size(5, (1 << 21) + 1) == 0
@@ -88,7 +88,7 @@ def probs(lib, **kw):
     (dict(stats=FAKE, T=0.0), -1),
     (dict(ws=None), -4),
     (dict(wsb=8 * 7), -4),
-    (dict(wsb=1279), -4),  # 8 rows, V=100 need 1280 bytes
+    (dict(wsb=1535), -4),  # 8 rows, V=100 need 1536 bytes
     (dict(ws=ctypes.c_void_p(0x1080)), -4),
     (dict(B=0), 0),
 ])

@@ -145,17 +145,26 @@ def test_exact_flag_gives_same_results(name):
     assert np.array_equal(g1[0], g2[0]) and np.array_equal(g1[1], g2[1])
 
 
-def test_all_residuals_same_outputs_and_determinism():
+@pytest.mark.parametrize("name,B", [("peaked_bf16", 24), ("dense_f32", 16), ("ragged_bf16", 24)])
+def test_modes_give_identical_outputs_and_are_deterministic(name, B):
+    """Lazy (default), eager and all-residuals modes differ only in which rows
+    draw a replacement; outputs must be identical, and repeatable bit for bit."""
     gh = _gh()
-    w = make_workload("peaked_bf16", 2, B=16)
-    a = gh.run_gpu(w)
-    b = gh.run_gpu(w, flags=api.SV_FLAG_ALL_RESIDUALS)
-    c = gh.run_gpu(w)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    assert np.array_equal(a[0], c[0]) and np.array_equal(a[3], c[3])
-    # in the default mode an accepted draft row skips its residual
-    rec = b[3].reshape(w["B"], -1, 2)
-    assert np.all(rec[:, :-1, 1] & api.SV_ROW_RESIDUAL)
+    w = make_workload(name, 2, B=B)
+    lazy = gh.run_gpu(w)
+    eager = gh.run_gpu(w, flags=api.SV_FLAG_EAGER)
+    full = gh.run_gpu(w, flags=api.SV_FLAG_ALL_RESIDUALS)
+    again = gh.run_gpu(w)
+    for other in (eager, full, again):
+        assert np.array_equal(lazy[0], other[0]) and np.array_equal(lazy[1], other[1])
+    assert np.array_equal(lazy[3], again[3])
+    gh.compare(w, lazy, label=f"{name} lazy")
+    f_lazy, f_eager, f_full = lazy[3][:, 1], eager[3][:, 1], full[3][:, 1]
+    draws = lambda f: int(np.count_nonzero(f & api.SV_ROW_RESIDUAL))
+    # lazy draws at most one replacement per request; eager at most the rejected rows; full every draft row
+    assert draws(f_lazy) <= w["B"] <= draws(f_full)
+    assert draws(f_lazy) <= draws(f_eager) <= draws(f_full)
+    assert np.all((f_lazy & api.SV_ROW_DEFERRED) == 0) or np.any(f_lazy & api.SV_ROW_DEFERRED)
 
 
 def test_ragged_equals_dense():
