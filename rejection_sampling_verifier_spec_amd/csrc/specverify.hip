@@ -48,6 +48,10 @@
 
 #include "specverify.h"
 
+// The error bound of the fast path follows the rounding steps as written:
+// no multiply-add is fused unless the source says fmaf.
+#pragma clang fp contract(off)
+
 namespace {
 
 constexpr int kNT = 256;                // threads per block of the fixed-size kernels
@@ -101,9 +105,15 @@ template <typename LT, bool VEC>
 struct Lay {
   static constexpr int kE = VEC ? LogitTraits<LT>::kVecElems : 1;
   static constexpr int kRuns = kLaneElems / kE;
-  // element k (0..15) of `lane` in the tile starting at `base`
+  // element k (0..31) of `lane` in the tile starting at `base`
   __device__ static __forceinline__ int index(int base, int lane, int k) {
     return base + ((k / kE) * 64 + lane) * kE + (k % kE);
+  }
+  // inverse of index(): the k at which `lane` holds tile offset d (0..kTile-1),
+  // or -1 if another lane holds it
+  __device__ static __forceinline__ int local(int d, int lane) {
+    const int run = d / (64 * kE), w = d % (64 * kE);
+    return (w / kE == lane) ? run * kE + (w % kE) : -1;
   }
 };
 
@@ -173,6 +183,12 @@ __device__ __forceinline__ void load_q(const float* __restrict__ row, int V, int
 
 // A lane's 32 logits of one tile kept packed as loaded (bf16 pairs or fp32),
 // so a prefetched tile costs 16 (bf16) or 32 (fp32) VGPRs.
+//   load():        unconditional loads with the address clamped into the row,
+//                  so the compiler counts outstanding loads and waits only for
+//                  the tile it consumes. Elements past the end of the row hold
+//                  copies of the row's last elements: real values (harmless
+//                  to a maximum), which every sum must leave out.
+//   load_padded(): the same, with elements past the end set to -inf.
 template <typename LT, bool VEC>
 struct RawTile;
 
@@ -180,12 +196,17 @@ template <>
 struct RawTile<uint16_t, true> {
   uint4 d[4];
   __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int V, int base, int lane) {
-    // unconditional loads (address clamped into the row), so that the compiler
-    // can count outstanding loads and wait only for the tile it consumes
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i0 = base + (r * 64 + lane) * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(row + (i0 < V ? i0 : V - 8));
+      d[r] = *reinterpret_cast<const uint4*>(row + min(i0, V - 8));
+    }
+  }
+  __device__ __forceinline__ void load_padded(const uint16_t* __restrict__ row, int V, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i0 = base + (r * 64 + lane) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(row + min(i0, V - 8));
       // per-component selects (a select on the whole vector becomes a branch
       // around the load); 0xff80 is bf16 -inf
       const bool in = i0 < V;
@@ -218,7 +239,14 @@ struct RawTile<float, true> {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int i0 = base + (r * 64 + lane) * 4;
-      const float4 v = *reinterpret_cast<const float4*>(row + (i0 < V ? i0 : V - 4));
+      d[r] = *reinterpret_cast<const float4*>(row + min(i0, V - 4));
+    }
+  }
+  __device__ __forceinline__ void load_padded(const float* __restrict__ row, int V, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i0 = base + (r * 64 + lane) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(row + min(i0, V - 4));
       const bool in = i0 < V;
       d[r].x = in ? v.x : -INFINITY;
       d[r].y = in ? v.y : -INFINITY;
@@ -239,9 +267,13 @@ struct RawTile<LT, false> {
   float d[kLaneElems];
   __device__ __forceinline__ void load(const LT* __restrict__ row, int V, int base, int lane) {
 #pragma unroll
+    for (int r = 0; r < kLaneElems; ++r) d[r] = to_float(row[min(base + r * 64 + lane, V - 1)]);
+  }
+  __device__ __forceinline__ void load_padded(const LT* __restrict__ row, int V, int base, int lane) {
+#pragma unroll
     for (int r = 0; r < kLaneElems; ++r) {
       const int i = base + r * 64 + lane;
-      const float v = to_float(row[i < V ? i : V - 1]);
+      const float v = to_float(row[min(i, V - 1)]);
       d[r] = i < V ? v : -INFINITY;
     }
   }
@@ -455,6 +487,7 @@ struct ProbsArgs {
 };
 
 struct RowShared {
+  float wmax[16];  // per-wave maxima (blocks of up to 1024 threads)
   float m;
   double z;        // Z (e-units)
   double px;
@@ -800,19 +833,20 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
   // ---------------- pass 2: residual tile sums (draft rows with q)
   const bool mode_w = WITH_Q && qrow != nullptr;
   const float izr = static_cast<float>(1.0 / Z);
+  const float cm = -(m * s);  // c_m, as in pass 1
   if constexpr (WITH_Q) if (mode_w) {
     for (int j = wave; j < nt; j += kWaves) {
       const int base = j * kTile;
       Raw r;
       float q[kLaneElems];
-      r.load(lrow, V, base, lane);
+      r.load_padded(lrow, V, base, lane);
       load_q<LT, VEC>(qrow, V, base, lane, q);
       float w4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
 #pragma unroll
         for (int k = g8; k < g8 + 8; ++k) {
-          const float p = fexp2((r.get(k) - m) * s) * izr;
+          const float p = fexp2(fmaf(r.get(k), s, cm)) * izr;
           w4[k & 3] += fmaxf(p - q[k], 0.f);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -828,7 +862,9 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
   // value of tile j in global units: W[j] (p-units) or S[j] * f_j (e-units)
   auto tile_val = [&](int j) -> double {
     if (mode_w) return static_cast<double>(W[j]);
-    const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
+    if (M[j] == -INFINITY) return 0.0;
+    const float cj = -(M[j] * s);
+    const float f = fexp2(cm - cj);  // bit for bit the factor Z was summed with
     return static_cast<double>(S[j] * f);
   };
   const int tper = (nt + NT - 1) / NT;
@@ -881,10 +917,10 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
   const double pb = sh.p_before;
   const int base = jt * kTile + kSearchPer * tid;
   float unit = 1.f;  // global units per local unit
-  float mref = m;    // exponent reference of the local weights
+  float cref = cm;   // exponent offset of the local weights (c_j of the tile)
   if (!mode_w) {
-    mref = M[jt];
-    unit = fexp2((M[jt] - m) * s);
+    cref = -(M[jt] * s);
+    unit = fexp2(cm - cref);
   }
   float wl[kSearchPer];
 #pragma unroll
@@ -893,7 +929,7 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
     float w = 0.f;
     if (k < V) {
       const float l = to_float(lrow[k]);
-      const float ek = fexp2((l - mref) * s);
+      const float ek = fexp2(fmaf(l, s, cref));
       if (WITH_Q && mode_w) w = fmaxf(ek * izr - qrow[k], 0.f);
       else w = (k == xmask) ? 0.f : ek;
     }
@@ -939,7 +975,9 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
     if (want_stats) {
       float* st = a.stats + t.trow * 4;
       st[0] = static_cast<float>(static_cast<double>(m) / a.temperature);
-      st[1] = static_cast<float>(log(Z));
+      // Z carries the factor 2^D, D = c_m + m s (see pass 1)
+      const double shift = static_cast<double>(cm) + static_cast<double>(m) * static_cast<double>(s);
+      st[1] = static_cast<float>(log(Z) - shift * kLn2);
       st[2] = is_draft ? static_cast<float>(px) : NAN;
       st[3] = is_draft ? static_cast<float>(mode_w ? total : total / Z) : 1.f;
     }
@@ -983,21 +1021,31 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   const float qx_in = (x_ok && qrow) ? qrow[x] : 0.f;
   const float u_acc = is_draft ? a.u[t.trow] : 0.f;
 
-  // ---------------- pass 1: tile sums of exp2((l - M_j) s), M_j = the wave's
-  // running maximum when tile j is reduced. One sweep per tile: the exps are
-  // taken against the running maximum while the lane maxima are tracked; only
-  // when a tile raises the maximum (a wave-wide ballot, rare after the first
-  // tiles) is the tile summed again against the new maximum. Every exponent
-  // argument is therefore <= 0. The next tile's loads are in flight meanwhile.
-  auto tile_sum = [&](const Raw& r, int base, float ref, float& es, float& ea) {
+  // ---------------- pass 1: per tile j, with reference M_j (the wave's running
+  // maximum, >= every element of the tile) and c_j = fl(-M_j s):
+  //   S_j = sum_k exp2(a_k),  a_k = fma(l_k, s, c_j)  (<= 0 up to u |c_j|),
+  //   EA_j = -sum_k e_k a_k  (for the error bound).
+  // The running maximum starts at the block-wide maximum of every wave's first
+  // tile, so a tile is rarely summed twice; when a tile does raise it (a
+  // wave-wide ballot), the tile is summed again against the new maximum. The
+  // next tile's loads are in flight meanwhile. The row's last tile (when it
+  // is partial), a tile holding the one-hot draft token, and a tile with a
+  // -inf or a NaN (e a = NaN) take the careful sum, which leaves out the
+  // elements past the end and the token, and clamps the argument.
+  auto tile_sum_careful = [&](const Raw& r, int base, float ref, float& es, float& ea) {
+    const float c = -(ref * s);
+    const int lpos = (xmask >= base && xmask < base + kTile) ? L::local(xmask - base, lane) : -1;
+    const int lim = V - L::index(base, lane, 0);  // element k is in the row iff its offset < lim
     float e4[4] = {0.f, 0.f, 0.f, 0.f};
     float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g8 = 0; g8 < kLaneElems; g8 += 8) {
 #pragma unroll
       for (int k = g8; k < g8 + 8; ++k) {
-        const float arg = fmaxf((r.get(k) - ref) * s, -4096.f);
-        const float e = (L::index(base, lane, k) == xmask) ? 0.f : fexp2(arg);
+        constexpr int kE = L::kE;
+        const int off = (k / kE) * 64 * kE + (k % kE);
+        const float arg = fmaxf(fmaf(r.get(k), s, c), -4096.f);
+        const float e = (k == lpos || off >= lim) ? 0.f : fexp2(arg);
         e4[k & 3] += e;
         a4[k & 3] = fmaf(e, arg, a4[k & 3]);
       }
@@ -1009,32 +1057,27 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   float ref = -INFINITY;
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
-    float lm = -INFINITY, es = 0.f, ea = 0.f;
-    if (xmask >= base && xmask < base + kTile) {
+    const float c = -(ref * s);
+    float lm = -INFINITY;
+    float e4[4] = {0.f, 0.f, 0.f, 0.f};
+    float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, r.get(k));
-      es = 1.f;  // forces the masked sum below
-    } else {
-      float e4[4] = {0.f, 0.f, 0.f, 0.f};
-      float a4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) {
-        const float v = r.get(k);
-        lm = fmaxf(lm, v);
-        // clamped so that -inf logits give e = 0 and e * a = 0 (not NaN)
-        const float arg = fmaxf((v - ref) * s, -4096.f);
-        const float e = fexp2(arg);
-        e4[k & 3] += e;
-        a4[k & 3] = fmaf(e, arg, a4[k & 3]);  // sum of e * a (a <= 0) for the error bound
-      }
-      es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
-      ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    for (int k = 0; k < kLaneElems; ++k) {
+      const float v = r.get(k);
+      lm = fmaxf(lm, v);
+      const float arg = fmaf(v, s, c);
+      const float e = fexp2(arg);
+      e4[k & 3] += e;
+      a4[k & 3] = fmaf(e, arg, a4[k & 3]);
     }
-    if (__any(lm > ref || (xmask >= base && xmask < base + kTile))) {
+    float es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+    float ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    const bool redo = lm > ref || !(ea == ea) || base + kTile > V || (xmask >= base && xmask < base + kTile);
+    if (__any(redo)) {
       ref = fmaxf(ref, wave_max(lm));
       es = 0.f;
       ea = 0.f;
-      if (ref != -INFINITY) tile_sum(r, base, ref, es, ea);
+      if (ref != -INFINITY) tile_sum_careful(r, base, ref, es, ea);
     }
     es = wave_sum(es);
     ea = wave_sum(ea);
@@ -1051,6 +1094,18 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
     int j = wave;
     if (j < nt) {
       ra.load(lrow, V, j * kTile, lane);
+      float lm0 = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) lm0 = fmaxf(lm0, ra.get(k));
+      lm0 = wave_max(lm0);
+      if (lane == 0) sh.wmax[wave] = lm0;
+    } else if (lane == 0) {
+      sh.wmax[wave] = -INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) ref = fmaxf(ref, sh.wmax[w]);
+    if (j < nt) {
       while (true) {
         rb.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
         tile1(ra, j);
@@ -1065,29 +1120,39 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   }
   __syncthreads();
 
-  // row max and Z (e-units relative to the row max)
+  // Row max m, c_m = fl(-m s) and Z = sum_j S_j exp2(c_m - c_j) in e-units.
+  // The c_j cancel exactly, so Z approximates 2^D sum_k 2^((l_k - m) s) with
+  // D = c_m + m s (|D| <= u |m s|); D is carried into p(x) exactly.
   float mloc = -INFINITY;
   for (int j = tid; j < nt; j += NT) mloc = fmaxf(mloc, M[j]);
   const float m = block_max(mloc, sc);
+  const float cm = -(m * s);
   double zl = 0.0, eal = 0.0;
   for (int j = tid; j < nt; j += NT) {
-    const float f = M[j] == -INFINITY ? 0.f : fexp2((M[j] - m) * s);
+    if (M[j] == -INFINITY) continue;
+    const float cj = -(M[j] * s);
+    const float d = cm - cj;  // <= 0
+    const float f = fexp2(d);
     zl += static_cast<double>(S[j] * f);
-    // e_k |a_k| relative to m: |a_k| = |a_k, local| + (m - M_j) s
+    // sum_k e_k |a_k| in global units: |a_k| <= -a_k,local + |d| + the
+    // rounding of c_j (elements at M_j may give a_k,local up to u |c_j| > 0)
     if (f > 0.f)
-      eal += static_cast<double>(f) *
-             (static_cast<double>(EA[j]) + (static_cast<double>(m) - M[j]) * a.s64 * static_cast<double>(S[j]));
+      eal += static_cast<double>(f) * (static_cast<double>(EA[j]) +
+                                       (-static_cast<double>(d) + 2.0 * kU * fabs(static_cast<double>(cj))) *
+                                           static_cast<double>(S[j]));
   }
   if (tid == 0 && xmask >= 0) {  // one-hot rows left x out of S
-    const float ex = fexp2((lx - m) * s);
+    const float ax = fmaxf(fmaf(lx, s, cm), -4096.f);
+    const float ex = fexp2(ax);
     zl += static_cast<double>(ex);
-    eal += static_cast<double>(ex) * (static_cast<double>(m) - lx) * a.s64;
+    eal += static_cast<double>(ex) * (-static_cast<double>(ax) + 2.0 * kU * fabs(static_cast<double>(cm)));
   }
   double Z, sea;
   block_sum2(zl, eal, sc, Z, sea);
   const double bt = bound_terms(Z, sea);
-  const double dZ = bt + kSumErr * Z;  // |Z~ - Z|
+  const double dZ = bt + kSumErr * Z;  // |Z~ - 2^D Z|
   const double relZ = dZ / Z;
+  const double shift = static_cast<double>(cm) + static_cast<double>(m) * static_cast<double>(s);  // D, exact
 
   // ---------------- accept test of a draft row (fp64 p(x), certified)
   if (tid == 0) {
@@ -1097,7 +1162,7 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
     uint32_t why = 0;
     double px = 0.0;
     if (is_draft) {
-      if (x_ok) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64) / Z;
+      if (x_ok) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64 + shift) / Z;
       const double qx = onehot ? 1.0 : static_cast<double>(qx_in);
       const double lhs = static_cast<double>(u_acc) * qx;
       accepted = (x_ok && px > 0.0 && lhs <= px) ? 1 : 0;
@@ -1127,7 +1192,7 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   // and only if it is the request's first rejection
   if (!EAGER && qrow != nullptr && !accepted && !all_res) {
     if (tid == 0) {
-      a.rstat[t.trow] = make_double4(static_cast<double>(m), Z, sea, 0.0);
+      a.rstat[t.trow] = make_double4(static_cast<double>(m), Z, sea, shift);
       a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowDeferred));
     }
     return;
