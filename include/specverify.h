@@ -86,7 +86,10 @@ enum sv_status {
  * the next one. One workspace per call in flight (calls that share one on
  * different streams race). It starts with one 8-byte record per target row,
  * {int32 token, uint32 row_flags} (documented for diagnostics), followed by
- * the list and fp64 tile sums of the rows recomputed in fp64. row_flags bits: */
+ * the list, counters and fp64 tile sums of the rows recomputed in fp64 (the
+ * counters return to zero at the end of every call that completes; a call
+ * that was never run to completion leaves the workspace to be zero-filled
+ * again). row_flags bits: */
 #define SV_ROW_ACCEPTED 0x1u  /* the row's own accept test passed */
 #define SV_ROW_EXACT 0x2u     /* the row was recomputed on the fp64 path */
 #define SV_ROW_RESIDUAL 0x4u  /* the row's replacement token was drawn (q read in full) */
@@ -97,12 +100,15 @@ enum sv_status {
 #define SV_ROW_WHY_SEARCH 0x40u    /* inverse-CDF search inconclusive in fp32 */
 #define SV_ROW_WHY_MARGIN 0x80u    /* sample uniform within the bound of a CDF boundary */
 #define SV_ROW_WHY_FORCED 0x100u   /* SV_FLAG_EXACT, or a degenerate row */
-#define SV_ROW_DEFERRED 0x400u     /* lazy mode: rejected row whose replacement was not needed (not drawn) */
+#define SV_ROW_DEFERRED 0x400u     /* lazy mode: rejected (or bonus) row whose token was not needed (not drawn) */
+#define SV_ROW_UNDECIDED 0x800u    /* lazy mode: accept test left to the per-request fp64 pass, which did not
+                                      need this row (an earlier row was rejected) */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of
- * `vocab_size` tokens: 8 bytes per row for the records and list, plus
- * 16 * ceil(vocab_size / 2048) bytes per row for fp64 tile sums. The greedy
+ * `vocab_size` tokens: 92 bytes per row for the records, list, counters and
+ * lazy-mode statistics, plus 28 * ceil(vocab_size / 2048) bytes
+ * per row for fp64 tile sums, each part rounded up to 256 bytes. The greedy
  * entry point needs only the records (8 bytes per row, rounded up to 256).
  * Returns 0 for a negative row count or a vocab_size outside [1, SV_MAX_VOCAB]. */
 size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size);

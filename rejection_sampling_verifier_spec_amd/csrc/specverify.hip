@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "specverify.h"
@@ -468,6 +469,15 @@ __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__
 // ----------------------------------------------------------------------------
 // probabilistic verification
 
+// One listed row, self-contained so that the fp64 kernel decodes nothing.
+struct ExactEntry {
+  double z, dz;  // the fast path's Z and the bound on its error (fp64 units), or {0, inf}
+  int trow, drow, srow, b;  // target row, draft row (-1: bonus row), row of the sample uniform, request
+  int x;                    // draft token if in [0, V), else -1
+  float m;                  // row max
+  int pad0, pad1;
+};
+
 struct ProbsArgs {
   const void* logits;
   const float* q;        // nullptr: one-hot drafts
@@ -482,7 +492,7 @@ struct ProbsArgs {
   int B, gamma, ndraft, V;
   uint32_t flags;
   int* xcount;    // list of rows for the fp64 path (see ExactArgs)
-  int2* xlist;
+  ExactEntry* xlist;
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
 };
 
@@ -500,6 +510,10 @@ struct RowShared {
   double p_before;
   int cross;
   int lastpos;
+  double lx, qx, ua, us;  // fp64 finish: l_x, q(x), accept and sample uniforms
+  uint32_t why;
+  int nund;               // fp64 finish: tiles with undecided elements
+  int und[16];
 };
 
 // Bound on sum_k |e~_k - e_k| in e-units (e_k relative to the row max):
@@ -516,69 +530,161 @@ __device__ __forceinline__ float logit_at(const LT* row, int64_t k) {
 }
 
 // ----------------------------------------------------------------------------
-// fp64 path for the rows the fast kernel could not certify.
-//
-// The fast kernel appends such a row to a list in the workspace; three small
-// fixed-grid kernels then spread the fp64 work over the whole GPU:
-//   exact_tiles_kernel:    one (row, tile) item per block iteration; fp64 sum of
-//                          e_k = 2^((l_k - m) log2(e) / T) over the tile.
-//   exact_residual_kernel: same items, rows with q only; fp64 sum of
-//                          max(0, e_k / Z - q_k) over the tile.
-//   exact_finish_kernel:   one row per block iteration; accept test, residual
-//                          mass, fallback, tile search and in-tile search, all
-//                          in fp64; writes the row's record and statistics.
-// With an empty list each kernel reads the count and exits.
+// per-request select: first rejection, then the accepted drafts and one token
 
-constexpr uint32_t kRowNeedExact = 0x200u;  // set by the fast kernel, cleared by exact_finish_kernel
+constexpr uint32_t kRowNeedExactBit = 0x200u;  // a row waiting for the fp64 path
+
+struct SelectArgs {
+  const int64_t* x;
+  const int32_t* cu;
+  const int2* ws;
+  int64_t* out;
+  int32_t* nacc;
+  int B, gamma, ndraft;
+};
+
+// With final_only, a request is left alone while a row up to its first
+// rejection still waits for the fp64 path (it is selected again afterwards).
+__device__ void select_request(const SelectArgs& a, int b, bool final_only) {
+  int d0, d1;
+  if (a.cu) {
+    d0 = a.cu[b];
+    d1 = a.cu[b + 1];
+    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) {
+      // invalid offsets: emit nothing for this request
+      a.nacc[b] = 0;
+      return;
+    }
+  } else {
+    d0 = b * a.gamma;
+    d1 = d0 + a.gamma;
+  }
+  const int g = d1 - d0;
+  const int64_t t0 = static_cast<int64_t>(d0) + b;
+  // every record is read (independent loads); n = first row whose own test failed
+  int n = g;
+  bool pending = false;
+#pragma unroll 4
+  for (int i = 0; i <= g; ++i) {
+    const uint32_t f = static_cast<uint32_t>(a.ws[t0 + i].y);
+    if (i <= n) {
+      pending = pending || (f & kRowNeedExactBit) != 0;
+      if (i < n && !(f & kRowAccepted)) n = i;
+    }
+  }
+  if (final_only && pending) return;
+  for (int i = 0; i < n; ++i) a.out[t0 + i] = a.x[d0 + i];
+  a.out[t0 + n] = static_cast<int64_t>(a.ws[t0 + n].x);
+  for (int i = n + 1; i <= g; ++i) a.out[t0 + i] = -1;
+  a.nacc[b] = n;
+}
+
+__global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
+  const int b = blockIdx.x * kSelectNT + threadIdx.x;
+  if (b < a.B) select_request(a, b, false);
+}
+
+// ----------------------------------------------------------------------------
+// fp64 path for the rows the fast kernels could not certify.
+//
+// The fast kernels append such a row to a list in the workspace, with the fast
+// path's Z and its certified error bound when they have them. One fixed-grid
+// kernel then spreads the fp64 work over the whole GPU, one (row, tile) item
+// per block iteration:
+//   - the item: the fp64 sum E_j of e_k = 2^((l_k - m) log2(e) / T) over the
+//     tile and, for rows with q, the part of the residual sum that the Z
+//     interval already decides: P_j and Q_j, the sums of e_k and of q_k over
+//     the elements with e_k / Z > q_k for every Z in the interval, and whether
+//     any element is left undecided (e_k / Z - q_k changes sign within it);
+//   - the block that completes a row's last tile (a device-scope counter per
+//     row, fence before and after) finishes the row: Z = sum_j E_j, the accept
+//     test, the residual tile sums W_j = P_j / Z - Q_j (a tile with undecided
+//     elements is summed again with the final Z), fallback, tile search and
+//     in-tile search, all in fp64; it writes the row's record and statistics;
+//   - the block that finishes the last listed row (a second counter) runs the
+//     per-request select and resets the counters for the next call.
+// With an empty list, block 0 runs the select and the other blocks exit. No
+// block ever waits for another.
+
+constexpr uint32_t kRowNeedExact = kRowNeedExactBit;  // set by the fast kernels, cleared by the fp64 finish
 constexpr uint32_t kRowDeferred = SV_ROW_DEFERRED;
+constexpr uint32_t kRowUndecided = SV_ROW_UNDECIDED;
 constexpr uint32_t kFlagLazy = 0x80000000u;  // internal: set by the host for the lazy mode
-constexpr int kExactGrid = 512;             // blocks of the item kernels
 constexpr int kExactPer = kTile / kNT;      // elements per thread of one tile (8)
+constexpr double kZSlack = 1e-12;           // widening of the Z interval for fp64 rounding
+constexpr int kItemTiles = 4;               // tiles per item of the fp64 kernel
+constexpr int kMaxUndecided = 16;           // undecided tiles the finish lists in LDS
+constexpr int kExactItemGrid = 256;         // blocks of the fp64 kernel
+
 
 struct ExactArgs {
-  int* count;     // number of listed rows (reset to 0 by the select kernel)
-  int2* list;     // {row block index, bits of the row max m}
-  double* etile;  // [rows][nt] fp64 tile sums of e
-  double* wtile;  // [rows][nt] fp64 tile sums of max(0, p - q)
+  int* count;         // listed rows (reset by the block that finishes the last one)
+  int* finished;      // listed rows finished (reset likewise)
+  int* done;          // [rows] tiles finished per listed row (reset by the row's finisher)
+  ExactEntry* list;   // [rows]
+  double* etile;   // [rows][nt] sum of e_k
+  double* ptile;   // [rows][nt] sum of e_k over the elements certainly in the residual's support
+  double* qtile;   // [rows][nt] sum of q_k over the same elements
+  int* amb;        // [rows][nt] 1 if the Z interval leaves an element of the tile undecided
   int nt;
   int rows;
 };
 
 // Thread t of a block covers elements [base + 8t, base + 8t + 8) of a tile,
 // so the tile is covered in ascending token order by ascending threads.
+// The loads are unconditional (index clamped into the row) so that all of
+// them are in flight at once; elements past the end read as -inf (logits) or
+// 0 (q).
 template <typename LT>
 __device__ __forceinline__ void load8(const LT* __restrict__ row, int V, int k0, double (&l)[kExactPer]) {
+  LT raw[kExactPer];
 #pragma unroll
-  for (int e = 0; e < kExactPer; ++e) {
-    const int k = k0 + e;
-    l[e] = k < V ? static_cast<double>(to_float(row[k])) : -INFINITY;
-  }
+  for (int e = 0; e < kExactPer; ++e) raw[e] = row[min(k0 + e, V - 1)];
+#pragma unroll
+  for (int e = 0; e < kExactPer; ++e) l[e] = k0 + e < V ? static_cast<double>(to_float(raw[e])) : -INFINITY;
+}
+// q of the same elements. With q == nullptr it reads fallback[0] (any valid
+// address) instead, so that the loads need no branch around them, and
+// returns zeros.
+__device__ __forceinline__ void load8q(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
+                                       double (&v)[kExactPer]) {
+  const bool has = q != nullptr;
+  const float* src = has ? q : fallback;
+  float raw[kExactPer];
+#pragma unroll
+  for (int e = 0; e < kExactPer; ++e) raw[e] = src[has ? min(k0 + e, V - 1) : 0];
+#pragma unroll
+  for (int e = 0; e < kExactPer; ++e) v[e] = (has && k0 + e < V) ? static_cast<double>(raw[e]) : 0.0;
 }
 
 struct ExactRow {
   Task t;
-  const void* lrow;
   const float* qrow;
   int64_t x;
   bool x_ok, is_draft, onehot;
-  double m;
+  double m, z, dz;
 };
 
 __device__ __forceinline__ ExactRow exact_row_info(const ProbsArgs& a, const ExactArgs& e, int pos) {
   ExactRow r;
-  const int2 li = e.list[pos];
-  // a list entry is a row block index of this call; anything else (a
-  // workspace that was not zero-filled) is skipped rather than decoded
-  const bool in_range = li.x >= 0 && li.x < e.rows;
-  r.t = decode_task(in_range ? li.x : 0, a.cu, a.B, a.gamma, a.ndraft);
-  r.t.valid = r.t.valid && in_range;
-  r.m = static_cast<double>(__int_as_float(li.y));
+  const ExactEntry en = e.list[pos];
+  // an entry out of range (a workspace that was not zero-filled) is skipped
+  r.t.valid = en.trow >= 0 && en.trow < e.rows && en.drow >= -1 && en.drow < a.ndraft && en.srow >= 0 &&
+              en.srow < e.rows && en.b >= 0 && en.b < a.B && en.x >= -1 && en.x < a.V;
+  r.t.trow = r.t.valid ? en.trow : 0;
+  r.t.drow = r.t.valid ? en.drow : -1;
+  r.t.srow = r.t.valid ? en.srow : 0;
+  r.t.b = r.t.valid ? en.b : 0;
+  r.t.i = 0;
+  r.t.g = 0;
+  r.m = static_cast<double>(en.m);
+  r.z = en.z;
+  r.dz = en.dz;
   r.is_draft = r.t.drow >= 0;
   r.qrow = (r.is_draft && a.q) ? a.q + r.t.drow * static_cast<int64_t>(a.V) : nullptr;
-  r.x = r.is_draft ? a.x[r.t.drow] : -1;
-  r.x_ok = r.is_draft && r.x >= 0 && r.x < a.V;
+  r.x = r.is_draft ? en.x : -1;
+  r.x_ok = r.is_draft && r.x >= 0;
   r.onehot = r.is_draft && r.qrow == nullptr;
-  r.lrow = nullptr;
   return r;
 }
 
@@ -587,219 +693,370 @@ __device__ __forceinline__ int exact_count(const ExactArgs& e) {
   return n < 0 ? 0 : (n > e.rows ? e.rows : n);
 }
 
-template <typename LT>
-__global__ __launch_bounds__(kNT) void exact_tiles_kernel(ProbsArgs a, ExactArgs e) {
-  __shared__ BlockScratch sc;
-  const int n = exact_count(e);
-  const int64_t items = static_cast<int64_t>(n) * e.nt;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int pos = static_cast<int>(it / e.nt), j = static_cast<int>(it % e.nt);
-    const ExactRow r = exact_row_info(a, e, pos);
-    if (!r.t.valid) continue;
-    const LT* lrow = static_cast<const LT*>(a.logits) + r.t.trow * static_cast<int64_t>(a.V);
-    double l[kExactPer];
-    load8<LT>(lrow, a.V, j * kTile + kExactPer * threadIdx.x, l);
-    double acc = 0.0;
+// N fixed-order block sums with one pair of barriers (s.d holds N * waves).
+template <int N>
+__device__ void block_sum_n(double (&v)[N], BlockScratch& s) {
 #pragma unroll
-    for (int k = 0; k < kExactPer; ++k) acc += exp2((l[k] - r.m) * a.s64);
-    acc = block_sum(acc, sc);
-    if (threadIdx.x == 0) e.etile[static_cast<int64_t>(pos) * e.nt + j] = acc;
+  for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], o);
   }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) s.d[i * kWaves + wave] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double r = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) r += s.d[i * kWaves + w];
+    v[i] = r;
+  }
+  __syncthreads();
 }
 
-// Z of listed row `pos` from its fp64 tile sums: thread t adds tiles t,
-// t + 256, ..., then a fixed-order block sum (identical in every kernel).
-__device__ __forceinline__ double exact_z(const double* __restrict__ et, int nt, BlockScratch& sc) {
-  double z = 0.0;
-  for (int j = threadIdx.x; j < nt; j += kNT) z += et[j];
-  return block_sum(z, sc);
-}
-
+// One item: kItemTiles consecutive tiles of a listed row. Per tile, the fp64
+// sum of e_k and, for rows with q, the sums over the elements the Z interval
+// decides: e_k / Z > q_k for every Z in [zlo, zhi] iff e_k > q_k zhi, and
+// e_k / Z <= q_k for every Z iff e_k <= q_k zlo.
 template <typename LT>
-__global__ __launch_bounds__(kNT) void exact_residual_kernel(ProbsArgs a, ExactArgs e) {
-  __shared__ BlockScratch sc;
-  const int n = exact_count(e);
-  const int64_t items = static_cast<int64_t>(n) * e.nt;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int pos = static_cast<int>(it / e.nt), j = static_cast<int>(it % e.nt);
-    const ExactRow r = exact_row_info(a, e, pos);
-    if (!r.t.valid || r.qrow == nullptr) continue;  // uniform over the block
-    const double iz = 1.0 / exact_z(e.etile + static_cast<int64_t>(pos) * e.nt, e.nt, sc);
-    const LT* lrow = static_cast<const LT*>(a.logits) + r.t.trow * static_cast<int64_t>(a.V);
-    const int k0 = j * kTile + kExactPer * threadIdx.x;
-    double l[kExactPer];
-    load8<LT>(lrow, a.V, k0, l);
-    double acc = 0.0;
+__device__ void exact_item(const ProbsArgs& a, const ExactArgs& e, const ExactRow& r, int pos, int j0,
+                           BlockScratch& sc) {
+  const LT* lrow = static_cast<const LT*>(a.logits) + r.t.trow * static_cast<int64_t>(a.V);
+  const double zhi = (r.z + r.dz) * (1.0 + kZSlack), zlo = (r.z - r.dz) * (1.0 - kZSlack);
+  // tiles past the end of the row (the last item) read clamped, unused data
+  double l[kItemTiles][kExactPer], qv[kItemTiles][kExactPer];
+  const bool has_q = r.qrow != nullptr;
+#pragma unroll
+  for (int u = 0; u < kItemTiles; ++u) {
+    const int k0 = (j0 + u) * kTile + kExactPer * threadIdx.x;
+    load8<LT>(lrow, a.V, k0, l[u]);
+    load8q(r.qrow, a.u, a.V, k0, qv[u]);
+  }
+  double v[3 * kItemTiles];
+  int undecided = 0;
+#pragma unroll
+  for (int u = 0; u < kItemTiles; ++u) {
+    double es = 0.0, ps = 0.0, qs = 0.0;
 #pragma unroll
     for (int k = 0; k < kExactPer; ++k) {
-      const double q = k0 + k < a.V ? static_cast<double>(r.qrow[k0 + k]) : 0.0;
-      acc += fmax(0.0, exp2((l[k] - r.m) * a.s64) * iz - q);
+      const double ek = exp2((l[u][k] - r.m) * a.s64);
+      es += ek;
+      if (has_q) {
+        const double q = qv[u][k];  // 0 past the end, where e_k = 0 too: decided, not in the support
+        if (ek > q * zhi) {
+          ps += ek;
+          qs += q;
+        } else if (!(ek <= q * zlo)) {
+          undecided |= 1 << u;
+        }
+      }
     }
-    acc = block_sum(acc, sc);
-    if (threadIdx.x == 0) e.wtile[static_cast<int64_t>(pos) * e.nt + j] = acc;
+    v[3 * u] = es;
+    v[3 * u + 1] = ps;
+    v[3 * u + 2] = qs;
+  }
+  block_sum_n<3 * kItemTiles>(v, sc);
+  // the per-tile undecided bits, OR-ed over the block
+  __shared__ int und;
+  if (threadIdx.x == 0) und = 0;
+  __syncthreads();
+  if (undecided) atomicOr(&und, undecided);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int u = 0; u < kItemTiles; ++u) {
+      if (j0 + u >= e.nt) break;
+      const int64_t idx = static_cast<int64_t>(pos) * e.nt + j0 + u;
+      e.etile[idx] = v[3 * u];
+      e.ptile[idx] = v[3 * u + 1];
+      e.qtile[idx] = v[3 * u + 2];
+      e.amb[idx] = (und >> u) & 1;
+    }
   }
 }
 
 template <typename LT>
-__global__ __launch_bounds__(kNT) void exact_finish_kernel(ProbsArgs a, ExactArgs e) {
-  extern __shared__ double xtile[];  // [nt] e tile sums, [nt] residual tile sums
-  __shared__ BlockScratch sc;
-  __shared__ RowShared sh;
-  const int n = exact_count(e);
+__device__ void exact_finish_row(const ProbsArgs& a, const ExactArgs& e, const ExactRow& r, int pos,
+                                 double* xtile, BlockScratch& sc, RowShared& sh) {
   const int tid = threadIdx.x;
   const int nt = e.nt;
   double* ets = xtile;
   double* wts = xtile + nt;
+  double* pts = xtile + 2 * nt;
+  double* qts = xtile + 3 * nt;
   const int tper = (nt + kNT - 1) / kNT;
   const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
-  for (int pos = blockIdx.x; pos < n; pos += gridDim.x) {
-    const ExactRow r = exact_row_info(a, e, pos);
-    if (!r.t.valid) continue;
-    const Task& t = r.t;
-    const LT* lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(a.V);
-    const double* et = e.etile + static_cast<int64_t>(pos) * nt;
-    const double* wt = e.wtile + static_cast<int64_t>(pos) * nt;
+  const Task& t = r.t;
+  const LT* lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(a.V);
+  const int64_t row0 = static_cast<int64_t>(pos) * nt;
+  // every load that does not depend on Z, issued together
+  double zl = 0.0;
+  for (int j = tid; j < nt; j += kNT) {
+    const double ev = e.etile[row0 + j];
+    ets[j] = ev;
+    zl += ev;
+    if (r.qrow) {
+      pts[j] = e.amb[row0 + j] ? -1.0 : e.ptile[row0 + j];  // -1: the tile has undecided elements
+      qts[j] = e.qtile[row0 + j];
+    }
+  }
+  if (tid == 0) {
+    sh.why = static_cast<uint32_t>(a.ws[t.trow].y) & 0x1f0u;
+    sh.lx = r.x_ok ? static_cast<double>(logit_at(lrow, r.x)) : 0.0;
+    sh.qx = r.onehot ? 1.0 : (r.x_ok ? static_cast<double>(r.qrow[r.x]) : 0.0);
+    sh.ua = r.is_draft ? static_cast<double>(a.u[t.trow]) : 0.0;
+    sh.us = static_cast<double>(a.u[t.srow]);
+  }
+  // Z: thread t adds tiles t, t + 256, ..., then a fixed-order block sum
+  // (whose barriers also publish the loads above)
+  const double Z = block_sum(zl, sc);
+  const double iz = 1.0 / Z;
+  const double s = a.s64;
+  if (r.qrow) {
+    // residual tile sums: decided tiles from P_j and Q_j, then the tiles with
+    // undecided elements (listed in LDS, any order) summed again with the final Z
+    if (tid == 0) sh.nund = 0;
+    __syncthreads();
     for (int j = tid; j < nt; j += kNT) {
-      ets[j] = et[j];
-      wts[j] = r.qrow ? wt[j] : 0.0;
-    }
-    const double Z = exact_z(et, nt, sc);  // barriers inside also publish ets / wts
-    const double iz = 1.0 / Z;
-    const double s = a.s64;
-    const uint32_t why = static_cast<uint32_t>(a.ws[t.trow].y) & 0x1f0u;
-
-    double ex = 0.0, px = 0.0;
-    bool accepted = false;
-    if (r.is_draft) {
-      if (r.x_ok) {
-        ex = exp2((static_cast<double>(logit_at(lrow, r.x)) - r.m) * s);
-        px = ex * iz;
-      }
-      const double qx = r.onehot ? 1.0 : (r.x_ok ? static_cast<double>(r.qrow[r.x]) : 0.0);
-      accepted = r.x_ok && px > 0.0 && static_cast<double>(a.u[t.trow]) * qx <= px;
-    }
-    const bool all_res = (a.flags & SV_FLAG_ALL_RESIDUALS) || a.stats != nullptr;
-    uint32_t flags = kRowExact | why | (accepted ? kRowAccepted : 0u);
-    int token = -1;
-    double rmass = 1.0;
-    if (!r.is_draft || !accepted || all_res) {
-      // tile values in tile order: mode 1 residual, 2 p without x, 0 p
-      int mode = r.is_draft ? (r.onehot ? 2 : 1) : 0;
-      const int jx = r.x_ok ? static_cast<int>(r.x / kTile) : -1;
-      auto tile_val = [&](int j) -> double {
-        if (mode == 1) return wts[j];
-        double v = ets[j];
-        if (mode == 2 && j == jx) v = fmax(0.0, v - ex);
-        return v * iz;
-      };
-      double tv = 0.0;
-      for (int j = tlo; j < thi; ++j) tv += tile_val(j);
-      double excl, incl, total;
-      block_scan(tv, sc, excl, incl, total);
-      if (mode != 0) {
-        rmass = total;
-        if (total <= kFallbackMass) {
-          mode = 0;
-          flags |= kRowFallback;
-          tv = 0.0;
-          for (int j = tlo; j < thi; ++j) tv += tile_val(j);
-          block_scan(tv, sc, excl, incl, total);
-        }
-        flags |= kRowResidual;
-      }
-      const double tau = static_cast<double>(a.u[t.srow]) * total;
-      // crossing tile: smallest positive tile reaching tau, else the last positive tile
-      if (tid == 0) {
-        sh.cross = 0x7fffffff;
-        sh.lastpos = -1;
-      }
-      __syncthreads();
-      if (excl < tau) {
-        double c = 0.0;
-        int tok = -1, lastpos = -1;
-        for (int j = tlo; j < thi && tok < 0; ++j) {
-          const double v = tile_val(j);
-          c += v;
-          if (v > 0.0) {
-            lastpos = j;
-            if (excl + c >= tau) tok = j;
-          }
-        }
-        if (tok >= 0) atomicMin(&sh.cross, tok);
-        if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
-      }
-      __syncthreads();
-      const int jt = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : 0);
-      double pbl = 0.0;
-      for (int j = tlo; j < thi; ++j)
-        if (j < jt) pbl += tile_val(j);
-      const double pb = block_sum(pbl, sc);
-      // in-tile search, fp64, 8 consecutive elements per thread
-      const int k0 = jt * kTile + kExactPer * tid;
-      double l[kExactPer], w[kExactPer];
-      load8<LT>(lrow, a.V, k0, l);
-      double tsum = 0.0;
-#pragma unroll
-      for (int k = 0; k < kExactPer; ++k) {
-        const int kk = k0 + k;
-        double v = 0.0;
-        if (kk < a.V) {
-          const double p = exp2((l[k] - r.m) * s) * iz;
-          if (mode == 1) v = fmax(0.0, p - static_cast<double>(r.qrow[kk]));
-          else if (mode == 2 && kk == r.x) v = 0.0;
-          else v = p;
-        }
-        w[k] = v;
-        tsum += v;
-      }
-      double e2, i2, t2;
-      block_scan(tsum, sc, e2, i2, t2);
-      const double tl = tau - pb;
-      if (tid == 0) {
-        sh.cross = 0x7fffffff;
-        sh.lastpos = -1;
-      }
-      __syncthreads();
-      if (e2 < tl) {
-        int tok = -1, lastpos = -1;
-        double cl = 0.0;
-#pragma unroll
-        for (int k = 0; k < kExactPer; ++k) {
-          cl += w[k];
-          if (w[k] > 0.0 && tok < 0) {
-            lastpos = k0 + k;
-            if (e2 + cl >= tl) tok = k0 + k;
-          }
-        }
-        if (tok >= 0) atomicMin(&sh.cross, tok);
-        if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
-      }
-      __syncthreads();
-      token = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : jt * kTile);
-      __syncthreads();
-    }
-    if (tid == 0) {
-      a.ws[t.trow] = make_int2(token, static_cast<int>(flags));
-      if (a.stats) {
-        float* st = a.stats + t.trow * 4;
-        st[0] = static_cast<float>(r.m / a.temperature);
-        st[1] = static_cast<float>(log(Z));
-        st[2] = r.is_draft ? static_cast<float>(px) : NAN;
-        st[3] = static_cast<float>(rmass);
+      if (pts[j] < 0.0) {
+        const int k = atomicAdd(&sh.nund, 1);
+        if (k < kMaxUndecided) sh.und[k] = j;
+        wts[j] = -1.0;
+      } else {
+        wts[j] = fmax(0.0, pts[j] * iz - qts[j]);
       }
     }
     __syncthreads();
+    const int nund = sh.nund;
+    for (int kk = 0; kk < nund; ++kk) {
+      int j = -1;
+      if (nund <= kMaxUndecided) {
+        j = sh.und[kk];
+      } else {  // many undecided tiles: the first one not yet summed (its W_j is still -1)
+        for (int jj = 0; jj < nt && j < 0; ++jj)
+          if (wts[jj] < 0.0) j = jj;
+      }
+      const int k0 = j * kTile + kExactPer * tid;
+      double l[kExactPer], qv[kExactPer];
+      load8<LT>(lrow, a.V, k0, l);
+      load8q(r.qrow, a.u, a.V, k0, qv);
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < kExactPer; ++k) acc += fmax(0.0, exp2((l[k] - r.m) * s) * iz - qv[k]);
+      acc = block_sum(acc, sc);
+      if (tid == 0) wts[j] = acc;
+      __syncthreads();
+    }
+  } else {
+    for (int j = tid; j < nt; j += kNT) wts[j] = 0.0;
+    __syncthreads();
   }
+  const uint32_t why = sh.why;
+
+  double ex = 0.0, px = 0.0;
+  bool accepted = false;
+  if (r.is_draft) {
+    if (r.x_ok) {
+      ex = exp2((sh.lx - r.m) * s);
+      px = ex * iz;
+    }
+    accepted = r.x_ok && px > 0.0 && sh.ua * sh.qx <= px;
+  }
+  const bool all_res = (a.flags & SV_FLAG_ALL_RESIDUALS) || a.stats != nullptr;
+  uint32_t flags = kRowExact | why | (accepted ? kRowAccepted : 0u);
+  int token = -1;
+  double rmass = 1.0;
+  if (!r.is_draft || !accepted || all_res) {
+    // tile values in tile order: mode 1 residual, 2 p without x, 0 p
+    int mode = r.is_draft ? (r.onehot ? 2 : 1) : 0;
+    const int jx = r.x_ok ? static_cast<int>(r.x / kTile) : -1;
+    auto tile_val = [&](int j) -> double {
+      if (mode == 1) return wts[j];
+      double v = ets[j];
+      if (mode == 2 && j == jx) v = fmax(0.0, v - ex);
+      return v * iz;
+    };
+    double tv = 0.0;
+    for (int j = tlo; j < thi; ++j) tv += tile_val(j);
+    double excl, incl, total;
+    block_scan(tv, sc, excl, incl, total);
+    if (mode != 0) {
+      rmass = total;
+      if (total <= kFallbackMass) {
+        mode = 0;
+        flags |= kRowFallback;
+        tv = 0.0;
+        for (int j = tlo; j < thi; ++j) tv += tile_val(j);
+        block_scan(tv, sc, excl, incl, total);
+      }
+      flags |= kRowResidual;
+    }
+    const double tau = sh.us * total;
+    // crossing tile: smallest positive tile reaching tau, else the last positive tile
+    if (tid == 0) {
+      sh.cross = 0x7fffffff;
+      sh.lastpos = -1;
+    }
+    __syncthreads();
+    if (excl < tau) {
+      double c = 0.0;
+      int tok = -1, lastpos = -1;
+      for (int j = tlo; j < thi && tok < 0; ++j) {
+        const double v = tile_val(j);
+        c += v;
+        if (v > 0.0) {
+          lastpos = j;
+          if (excl + c >= tau) tok = j;
+        }
+      }
+      if (tok >= 0) atomicMin(&sh.cross, tok);
+      if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
+    }
+    __syncthreads();
+    const int jt = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : 0);
+    double pbl = 0.0;
+    for (int j = tlo; j < thi; ++j)
+      if (j < jt) pbl += tile_val(j);
+    const double pb = block_sum(pbl, sc);
+    // in-tile search, fp64, 8 consecutive elements per thread
+    const int k0 = jt * kTile + kExactPer * tid;
+    double l[kExactPer], w[kExactPer], qv[kExactPer];
+    load8<LT>(lrow, a.V, k0, l);
+    load8q(mode == 1 ? r.qrow : nullptr, a.u, a.V, k0, qv);
+    double tsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < kExactPer; ++k) {
+      const int kk = k0 + k;
+      double v = 0.0;
+      if (kk < a.V) {
+        const double p = exp2((l[k] - r.m) * s) * iz;
+        if (mode == 1) v = fmax(0.0, p - qv[k]);
+        else if (mode == 2 && kk == r.x) v = 0.0;
+        else v = p;
+      }
+      w[k] = v;
+      tsum += v;
+    }
+    double e2, i2, t2;
+    block_scan(tsum, sc, e2, i2, t2);
+    const double tl = tau - pb;
+    if (tid == 0) {
+      sh.cross = 0x7fffffff;
+      sh.lastpos = -1;
+    }
+    __syncthreads();
+    if (e2 < tl) {
+      int tok = -1, lastpos = -1;
+      double cl = 0.0;
+#pragma unroll
+      for (int k = 0; k < kExactPer; ++k) {
+        cl += w[k];
+        if (w[k] > 0.0 && tok < 0) {
+          lastpos = k0 + k;
+          if (e2 + cl >= tl) tok = k0 + k;
+        }
+      }
+      if (tok >= 0) atomicMin(&sh.cross, tok);
+      if (lastpos >= 0) atomicMax(&sh.lastpos, lastpos);
+    }
+    __syncthreads();
+    token = sh.cross != 0x7fffffff ? sh.cross : (sh.lastpos >= 0 ? sh.lastpos : jt * kTile);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.ws[t.trow] = make_int2(token, static_cast<int>(flags));
+    if (a.stats) {
+      float* st = a.stats + t.trow * 4;
+      st[0] = static_cast<float>(r.m / a.temperature);
+      st[1] = static_cast<float>(log(Z));
+      st[2] = r.is_draft ? static_cast<float>(px) : NAN;
+      st[3] = static_cast<float>(rmass);
+    }
+  }
+  __syncthreads();
+}
+
+template <typename LT>
+__global__ __launch_bounds__(kNT) void exact_kernel(ProbsArgs a, ExactArgs e, SelectArgs sel) {
+  extern __shared__ double xtile[];  // [nt] each: e tile sums, residual tile sums, P_j, Q_j
+  __shared__ BlockScratch sc;
+  __shared__ RowShared sh;
+  __shared__ int last;
+  const int n = exact_count(e);
+  const int nt = e.nt;
+  const int per_row = (nt + kItemTiles - 1) / kItemTiles;  // items per row
+  const int64_t items = static_cast<int64_t>(n) * per_row;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int pos = static_cast<int>(it / per_row), j0 = static_cast<int>(it % per_row) * kItemTiles;
+    const ExactRow r = exact_row_info(a, e, pos);
+    __syncthreads();  // every thread is done with `last` of the previous item
+    if (r.t.valid) exact_item<LT>(a, e, r, pos, j0, sc);
+    if (threadIdx.x == 0) {
+      __threadfence();  // release this item's tile sums
+      last = atomicAdd(&e.done[pos], 1) == per_row - 1;
+    }
+    __syncthreads();
+    if (!last) continue;
+    __threadfence();  // acquire every tile sum of the row
+    if (r.t.valid) exact_finish_row<LT>(a, e, r, pos, xtile, sc, sh);
+    if (threadIdx.x == 0) {
+      e.done[pos] = 0;
+      __threadfence();  // release the row's record
+      last = atomicAdd(e.finished, 1) == n - 1;
+    }
+    __syncthreads();
+    if (!last) continue;
+    // the last listed row is done: select every request that holds a listed row
+    __threadfence();  // acquire every record
+    for (int p = threadIdx.x; p < n; p += kNT) {
+      const ExactRow rr = exact_row_info(a, e, p);
+      if (rr.t.valid) select_request(sel, rr.t.b, false);
+    }
+    if (threadIdx.x == 0) {
+      *e.finished = 0;
+      *e.count = 0;
+    }
+  }
+  // every other request is final already (no row up to its first rejection
+  // waits for the fp64 path): select it here, spread over the blocks
+  for (int b = blockIdx.x * kNT + threadIdx.x; b < sel.B; b += gridDim.x * kNT) select_request(sel, b, true);
+  if (n == 0 && blockIdx.x == 0 && threadIdx.x == 0) *e.count = 0;
 }
 
 // Hand a row to the fp64 path: mark its record and append it to the list.
-__device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, uint32_t why, float m,
-                                           bool accepted = false) {
+// Z and dZ are the fast path's Z (carrying the factor 2^D of pass 1) and the
+// bound on its error; they are handed on in fp64 units (without 2^D), or as
+// {0, inf} when the fast path has no usable Z.
+__device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, uint32_t why, float m, bool accepted,
+                                           double Z, double dZ) {
   // the accept bit is meaningful unless the accept test itself is the reason
   a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowNeedExact | why | (accepted ? kRowAccepted : 0u)));
   const int pos = atomicAdd(a.xcount, 1);
-  const int blk = t.drow >= 0 ? static_cast<int>(t.drow) : a.ndraft + t.b;  // the row's index in the rows grid
-  if (pos < a.B + a.ndraft) a.xlist[pos] = make_int2(blk, __float_as_int(m));
+  if (pos < a.B + a.ndraft) {
+    ExactEntry en;
+    en.z = 0.0;
+    en.dz = INFINITY;
+    if (Z > 0.0 && Z < INFINITY && dZ >= 0.0 && dZ < Z && m != -INFINITY) {
+      const float s = a.s32;
+      const float cm = -(m * s);
+      const double unshift =
+          exp2(-(static_cast<double>(cm) + static_cast<double>(m) * static_cast<double>(s)));  // 2^-D
+      en.z = Z * unshift;
+      en.dz = dZ * unshift;
+    }
+    en.trow = static_cast<int>(t.trow);
+    en.drow = static_cast<int>(t.drow);
+    en.srow = static_cast<int>(t.srow);
+    en.b = t.b;
+    const int64_t x = t.drow >= 0 ? a.x[t.drow] : -1;
+    en.x = (x >= 0 && x < a.V) ? static_cast<int>(x) : -1;
+    en.m = m;
+    en.pad0 = en.pad1 = 0;
+    a.xlist[pos] = en;
+  }
 }
 
 // Reasons a row was recomputed on the fp64 path (row_flags bits 4..8).
@@ -908,7 +1165,7 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
   __syncthreads();
   if (!sh.found || sh.uncertain) {
     const uint32_t w2 = sh.uncertain ? static_cast<uint32_t>(sh.uncertain) : kWhySearch;
-    if (tid == 0) flag_exact(a, t, w2, m, accepted);
+    if (tid == 0) flag_exact(a, t, w2, m, accepted, Z, relZ * Z);
     return;
   }
 
@@ -922,15 +1179,25 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
     cref = -(M[jt] * s);
     unit = fexp2(cm - cref);
   }
+  // unconditional loads (index clamped into the row), all in flight at once
+  // (without q, the q loads read u[0], a valid address, and are unused)
+  LT lraw[kSearchPer];
+  float qraw[kSearchPer];
+  const bool use_q = WITH_Q && mode_w;
+  const float* qsrc = use_q ? qrow : a.u;
+#pragma unroll
+  for (int e = 0; e < kSearchPer; ++e) {
+    lraw[e] = lrow[min(base + e, V - 1)];
+    qraw[e] = qsrc[use_q ? min(base + e, V - 1) : 0];
+  }
   float wl[kSearchPer];
 #pragma unroll
   for (int e = 0; e < kSearchPer; ++e) {
     const int k = base + e;
     float w = 0.f;
     if (k < V) {
-      const float l = to_float(lrow[k]);
-      const float ek = fexp2(fmaf(l, s, cref));
-      if (WITH_Q && mode_w) w = fmaxf(ek * izr - qrow[k], 0.f);
+      const float ek = fexp2(fmaf(to_float(lraw[e]), s, cref));
+      if (WITH_Q && mode_w) w = fmaxf(ek * izr - qraw[e], 0.f);
       else w = (k == xmask) ? 0.f : ek;
     }
     wl[e] = w;
@@ -966,7 +1233,7 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
     if (!((tau - sh.c_lo) > d2 && (sh.c_hi - tau) > d2)) why2 = kWhyMargin;
   }
   if (why2) {
-    if (tid == 0) flag_exact(a, t, why2, m, accepted);
+    if (tid == 0) flag_exact(a, t, why2, m, accepted, Z, relZ * Z);
     return;
   }
   if (tid == 0) {
@@ -1178,8 +1445,27 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   }
   __syncthreads();
   const bool accepted = sh.accepted != 0;
+  if constexpr (!EAGER) {
+    // lazy mode: an accept test the bound cannot settle, every rejection and
+    // every bonus row are left to the per-request pass, with the row max and
+    // the certified Z interval in fp64 units (or {0, inf} when there is none)
+    if (tid == 0) {
+      const uint32_t f = sh.uncertain ? kRowUndecided : ((is_draft && accepted) ? kRowAccepted : kRowDeferred);
+      if (f != kRowAccepted) {
+        double z = 0.0, dz = INFINITY;
+        if (Z > 0.0 && Z < INFINITY && dZ < Z && m != -INFINITY) {
+          const double unshift = exp2(-shift);  // 2^-D
+          z = Z * unshift;
+          dz = dZ * unshift;
+        }
+        a.rstat[t.trow] = make_double4(static_cast<double>(m), z, dz, 0.0);
+      }
+      a.ws[t.trow] = make_int2(-1, static_cast<int>(f));
+    }
+    return;
+  }
   if (sh.uncertain) {
-    if (tid == 0) flag_exact(a, t, static_cast<uint32_t>(sh.uncertain), m);
+    if (tid == 0) flag_exact(a, t, static_cast<uint32_t>(sh.uncertain), m, false, Z, dZ);
     return;
   }
   const bool sample = !is_draft || !accepted || all_res;
@@ -1188,68 +1474,635 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
     return;
   }
 
-  // a rejected draft row with q: in the lazy mode its residual is drawn later,
-  // and only if it is the request's first rejection
-  if (!EAGER && qrow != nullptr && !accepted && !all_res) {
-    if (tid == 0) {
-      a.rstat[t.trow] = make_double4(static_cast<double>(m), Z, sea, shift);
-      a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowDeferred));
-    }
-    return;
-  }
   sample_row<LT, VEC, NT, EAGER>(a, t, lrow, qrow, xmask, accepted, m, Z, bt, relZ, sh.px, S, M, W, sc, sh);
 }
 
 // ----------------------------------------------------------------------------
-// lazy mode, phase 2: one block per request. The first draft row that is
-// certainly rejected decides the emitted token; if its residual was deferred,
-// it is drawn here. Rows whose accept test was left to the fp64 path are
-// passed over (that path decides them, and draws their token if they are
-// rejected), so the row drawn here may turn out unused; the select kernel
-// settles the request from the final records.
-template <typename LT, bool VEC, int NT>
-__global__ __launch_bounds__(NT) void residual_request_kernel(ProbsArgs a) {
-  extern __shared__ float dynw[];  // residual tile sums of the row drawn here
-  __shared__ BlockScratchT<NT> sc;
-  __shared__ RowShared sh;
+// lazy mode, phase 2: one block per request decides the request in fp64.
+//
+// The rows are taken in order; an accepted row passes. The first row that is
+// not (certainly rejected, or with an accept test the bound could not settle)
+// gets one fp64 pass over its logits and q: per tile, the sum E_j of
+// e_k = 2^((l_k - m) log2(e) / T) and the part of the residual sum that the
+// certified Z interval [zlo, zhi] of the fast pass already decides: P_j and
+// Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
+// every Z in the interval, and whether any element is left undecided. Then
+// Z = sum_j E_j; an undecided accept test is settled exactly (an accepted row
+// passes, and the next row is taken); W_j = P_j / Z - Q_j, the tiles with
+// undecided elements summed again with Z; residual mass <= 1e-8 falls back to
+// p; the tile search and the in-tile search draw the token in fp64. If every
+// draft is accepted, the bonus row is sampled from p the same way. The block
+// then writes the request's outputs.
+
+// Block size: 512 threads (2 waves per SIMD, up to 256 VGPRs each); the
+// eight-wide exp phases supply the instruction-level parallelism.
+template <bool VEC>
+constexpr int req_nt() { return 512; }
+constexpr int kExp2Tab = 64;  // 2^(j/64), j = 0..63
+
+// 2^a in fp64 for a <= 0 (or -inf), to about 1 ulp. J = round(64 a) comes out
+// of one fma with 1.5 * 2^52 (the integer is left in the low word), so
+// a = J / 64 + r with |r| <= 1/128 exactly; J = 64 n + j with 0 <= j < 64;
+// 2^r from its Taylor series to degree 5 (truncation < 4e-17 relative),
+// 2^(j/64) from `tab` (an LDS copy), 2^n by ldexp. Arguments below -1100 (and
+// -inf) give 0.
+__device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
+  constexpr double kRnd = 6755399441055744.0;  // 1.5 * 2^52
+  constexpr double c1 = 0.6931471805599453, c2 = 0.2402265069591007, c3 = 0.05550410866482158,
+                   c4 = 0.009618129107628477, c5 = 0.0013333558146428443;
+  a = fmax(a, -1100.0);
+  const double t = fma(a, 64.0, kRnd);
+  const double r = fma(t - kRnd, -0.015625, a);  // a - J / 64, exact
+  const int J = __double2loint(t);
+  double p = fma(c5, r, c4);
+  p = fma(p, r, c3);
+  p = fma(p, r, c2);
+  p = fma(p, r, c1);
+  p = fma(p, r, 1.0);
+  return ldexp(p * tab[J & 63], J >> 6);
+}
+
+// The constants of exp2_neg, held in VGPRs (read from LDS once per thread):
+// an fp64 instruction can take only one scalar operand, so two uniform
+// constants in one fma would otherwise be copied into VGPRs at every use.
+struct Exp2Consts {
+  double rnd, c64, cinv64, lo, c1, c2, c3, c4, c5;
+};
+constexpr int kExp2Consts = 9;
+__device__ __forceinline__ void exp2_consts_init(double* lds) {
+  const double v[kExp2Consts] = {6755399441055744.0, 64.0, -0.015625, -1100.0, 0.6931471805599453,
+                                 0.2402265069591007, 0.05550410866482158, 0.009618129107628477,
+                                 0.0013333558146428443};
+#pragma unroll
+  for (int i = 0; i < kExp2Consts; ++i) lds[i] = v[i];
+}
+__device__ __forceinline__ Exp2Consts exp2_consts_load(const double* lds) {
+  return Exp2Consts{lds[0], lds[1], lds[2], lds[3], lds[4], lds[5], lds[6], lds[7], lds[8]};
+}
+
+// exp2_neg of 8 arguments at once, in phases (all table reads, then all
+// polynomials, then the scaling), so that the LDS latency is paid once.
+__device__ __forceinline__ void exp2_neg8(const double (&a)[8], const double* __restrict__ tab, const Exp2Consts& C,
+                                          double (&e)[8]) {
+  const double kRnd = C.rnd;
+  const double c1 = C.c1, c2 = C.c2, c3 = C.c3, c4 = C.c4, c5 = C.c5;
+  double r[8], tv[8];
+  int J[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const double ak = fmax(a[k], C.lo);
+    const double t = fma(ak, C.c64, kRnd);
+    r[k] = fma(t - kRnd, C.cinv64, ak);
+    J[k] = __double2loint(t);
+    tv[k] = tab[J[k] & 63];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    double p = fma(c5, r[k], c4);
+    p = fma(p, r[k], c3);
+    p = fma(p, r[k], c2);
+    p = fma(p, r[k], c1);
+    p = fma(p, r[k], 1.0);
+    e[k] = ldexp(p * tv[k], J[k] >> 6);
+  }
+}
+
+// Sum over a wave by an xor butterfly: every lane ends with the same value
+// (a + b == b + a), in a fixed association.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Chunk c (0..3) of a lane's part of the tile at `base`: the lane's elements
+// k = 8c .. 8c + 7 in the tile layout (see Lay), as fp32 logits (-inf past the
+// end of the row) and q (0 past the end; q == nullptr: zeros). Loads are
+// unconditional, with addresses clamped into the row.
+template <typename LT, bool VEC, bool PAD>
+__device__ __forceinline__ void load_chunk(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V,
+                                           int base, int lane, int c, float (&lv)[8], float (&qv)[8]) {
+  using L = Lay<LT, VEC>;
+  if constexpr (VEC && sizeof(LT) == 2) {
+    const int i0 = L::index(base, lane, 8 * c);
+    const uint4 w = *reinterpret_cast<const uint4*>(lrow + min(i0, V - 8));
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const bool in = !PAD || i0 < V;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      lv[2 * h] = in ? __uint_as_float(ww[h] << 16) : -INFINITY;
+      lv[2 * h + 1] = in ? __uint_as_float(ww[h] & 0xffff0000u) : -INFINITY;
+    }
+    if (qrow) {
+      const float4 q0 = *reinterpret_cast<const float4*>(qrow + min(i0, V - 8));
+      const float4 q1 = *reinterpret_cast<const float4*>(qrow + min(i0, V - 8) + 4);
+      qv[0] = in ? q0.x : 0.f; qv[1] = in ? q0.y : 0.f; qv[2] = in ? q0.z : 0.f; qv[3] = in ? q0.w : 0.f;
+      qv[4] = in ? q1.x : 0.f; qv[5] = in ? q1.y : 0.f; qv[6] = in ? q1.z : 0.f; qv[7] = in ? q1.w : 0.f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+    }
+  } else if constexpr (VEC) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i0 = L::index(base, lane, 8 * c + 4 * h);
+      const bool in = !PAD || i0 < V;
+      const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(lrow) + min(i0, V - 4));
+      lv[4 * h + 0] = in ? v.x : -INFINITY; lv[4 * h + 1] = in ? v.y : -INFINITY;
+      lv[4 * h + 2] = in ? v.z : -INFINITY; lv[4 * h + 3] = in ? v.w : -INFINITY;
+      if (qrow) {
+        const float4 q = *reinterpret_cast<const float4*>(qrow + min(i0, V - 4));
+        qv[4 * h + 0] = in ? q.x : 0.f; qv[4 * h + 1] = in ? q.y : 0.f;
+        qv[4 * h + 2] = in ? q.z : 0.f; qv[4 * h + 3] = in ? q.w : 0.f;
+      } else {
+        qv[4 * h + 0] = qv[4 * h + 1] = qv[4 * h + 2] = qv[4 * h + 3] = 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = L::index(base, lane, 8 * c + e);
+      const bool in = !PAD || i < V;
+      lv[e] = in ? to_float(lrow[min(i, V - 1)]) : -INFINITY;
+      qv[e] = (qrow && in) ? qrow[min(i, V - 1)] : 0.f;
+    }
+  }
+}
+
+// A lane's chunk (elements k = 8c .. 8c + 7 of a tile, see Lay) kept raw as
+// loaded, so that several chunks can be in flight: bf16 logits take 4 VGPRs,
+// fp32 logits 8, q 8. Addresses are clamped into the row; elements past the
+// end are masked when the chunk is used (get_l / get_q with PAD).
+template <typename LT, bool VEC>
+struct RawChunk;
+template <>
+struct RawChunk<uint16_t, true> {
+  uint4 l;
+  float4 q0, q1;
+  int i0;
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ lrow, const float* __restrict__ qrow, int V,
+                                       int base, int lane, int c, bool has_q) {
+    i0 = Lay<uint16_t, true>::index(base, lane, 8 * c);
+    const int ic = min(i0, V - 8);
+    l = *reinterpret_cast<const uint4*>(lrow + ic);
+    if (has_q) {
+      q0 = *reinterpret_cast<const float4*>(qrow + ic);
+      q1 = *reinterpret_cast<const float4*>(qrow + ic + 4);
+    }
+  }
+  template <bool PAD>
+  __device__ __forceinline__ float get_l(int e, int V) const {
+    const uint32_t w = (e >> 1) == 0 ? l.x : (e >> 1) == 1 ? l.y : (e >> 1) == 2 ? l.z : l.w;
+    const float v = (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    return (!PAD || i0 + e < V) ? v : -INFINITY;
+  }
+  template <bool PAD>
+  __device__ __forceinline__ float get_q(int e, int V) const {
+    const float4& h = e < 4 ? q0 : q1;
+    const int k = e & 3;
+    const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    return (!PAD || i0 + e < V) ? v : 0.f;
+  }
+};
+template <>
+struct RawChunk<float, true> {
+  float4 l0, l1, q0, q1;
+  int i0;
+  __device__ __forceinline__ void load(const float* __restrict__ lrow, const float* __restrict__ qrow, int V,
+                                       int base, int lane, int c, bool has_q) {
+    // two runs of 4 consecutive elements (Lay<float, true>: kE = 4)
+    i0 = Lay<float, true>::index(base, lane, 8 * c);
+    const int i1 = Lay<float, true>::index(base, lane, 8 * c + 4);
+    l0 = *reinterpret_cast<const float4*>(lrow + min(i0, V - 4));
+    l1 = *reinterpret_cast<const float4*>(lrow + min(i1, V - 4));
+    if (has_q) {
+      q0 = *reinterpret_cast<const float4*>(qrow + min(i0, V - 4));
+      q1 = *reinterpret_cast<const float4*>(qrow + min(i1, V - 4));
+    }
+  }
+  __device__ __forceinline__ int idx(int e) const { return e < 4 ? i0 + e : i0 + 64 * 4 + (e - 4); }
+  template <bool PAD>
+  __device__ __forceinline__ float get_l(int e, int V) const {
+    const float4& h = e < 4 ? l0 : l1;
+    const int k = e & 3;
+    const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    return (!PAD || idx(e) < V) ? v : -INFINITY;
+  }
+  template <bool PAD>
+  __device__ __forceinline__ float get_q(int e, int V) const {
+    const float4& h = e < 4 ? q0 : q1;
+    const int k = e & 3;
+    const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    return (!PAD || idx(e) < V) ? v : 0.f;
+  }
+};
+template <typename LT>
+struct RawChunk<LT, false> {
+  float l[8], q[8];
+  int base, lane, c;
+  __device__ __forceinline__ void load(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int b_,
+                                       int lane_, int c_, bool has_q) {
+    base = b_;
+    lane = lane_;
+    c = c_;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = min(Lay<LT, false>::index(base, lane, 8 * c + e), V - 1);
+      l[e] = to_float(lrow[i]);
+      q[e] = has_q ? qrow[i] : 0.f;
+    }
+  }
+  template <bool PAD>
+  __device__ __forceinline__ float get_l(int e, int V) const {
+    return (!PAD || Lay<LT, false>::index(base, lane, 8 * c + e) < V) ? l[e] : -INFINITY;
+  }
+  template <bool PAD>
+  __device__ __forceinline__ float get_q(int e, int V) const {
+    return (!PAD || Lay<LT, false>::index(base, lane, 8 * c + e) < V) ? q[e] : 0.f;
+  }
+};
+
+// Inclusive scan over the 64 lanes (lane order), fixed association.
+__device__ __forceinline__ double wave_scan_incl_d(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// 32 consecutive elements from k0 (a multiple of 32), as fp32 logits (-inf
+// past the end of the row) or q (0 past the end; q == nullptr: zeros, with
+// fallback[0] read instead so that the loads need no branch). Loads are
+// unconditional, with addresses clamped into the row.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void load32(const LT* __restrict__ row, int V, int k0, float (&v)[32]) {
+  if constexpr (VEC && sizeof(LT) == 2) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint4 w = *reinterpret_cast<const uint4*>(row + min(k0 + 8 * h, V - 8));
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * h + 2 * i] = __uint_as_float(ww[i] << 16);
+        v[8 * h + 2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+      }
+    }
+  } else if constexpr (VEC) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row) + min(k0 + 4 * h, V - 4));
+      v[4 * h] = w.x;
+      v[4 * h + 1] = w.y;
+      v[4 * h + 2] = w.z;
+      v[4 * h + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = to_float(row[min(k0 + k, V - 1)]);
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if (k0 + k >= V) v[k] = -INFINITY;
+}
+template <bool VEC>
+__device__ __forceinline__ void load32q(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
+                                        float (&v)[32]) {
+  const bool has = q != nullptr;
+  if constexpr (VEC) {
+    const float* src = has ? q : fallback;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      float4 w;
+      if (has) w = *reinterpret_cast<const float4*>(src + min(k0 + 4 * h, V - 4));
+      else w = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[4 * h] = w.x;
+      v[4 * h + 1] = w.y;
+      v[4 * h + 2] = w.z;
+      v[4 * h + 3] = w.w;
+    }
+  } else {
+    const float* src = has ? q : fallback;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = has ? src[min(k0 + k, V - 1)] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if (k0 + k >= V) v[k] = 0.f;
+}
+
+// whether tile j of a row of V elements reaches past its end
+__device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j == nt - 1 && j * kTile + kTile > V; }
+
+struct ReqShared {
+  int first;    // first row not yet accepted
+  int nund;     // tiles with undecided elements
+  int cross, lastpos;
+  int tile;
+  double p_before;
+  int token;
+  int pad;
+};
+
+template <typename LT, bool VEC, int kReqNT = req_nt<VEC>()>
+__global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs sel) {
+  constexpr int kReqWaves = kReqNT / 64;
+  constexpr int kReqPer = kTile / kReqNT;  // elements per thread in the in-tile search
+  extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
+  __shared__ BlockScratchT<kReqNT> sc;
+  __shared__ ReqShared rs;
+  using L = Lay<LT, VEC>;
+  using Raw = RawTile<LT, VEC>;
+  const int V = a.V;
+  const int nt = (V + kTile - 1) / kTile;
+  double* E = rbuf;
+  double* P = rbuf + nt;
+  double* Q = rbuf + 2 * nt;
+  double* W = rbuf + 3 * nt;
+  int* ulist = reinterpret_cast<int*>(rbuf + 4 * nt);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   int d0, d1;
   if (a.cu) {
     d0 = a.cu[b];
     d1 = a.cu[b + 1];
-    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) return;
+    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) {
+      if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
+      return;
+    }
   } else {
     d0 = b * a.gamma;
     d1 = d0 + a.gamma;
   }
   const int g = d1 - d0;
   const int64_t t0 = static_cast<int64_t>(d0) + b;
-  int n = g;
-  for (int i = 0; i < g; ++i) {
-    const uint32_t f = static_cast<uint32_t>(a.ws[t0 + i].y);
-    if ((f & kRowNeedExact) && (f & (kWhyAccept | kWhyForced))) continue;
-    if (f & kRowAccepted) continue;
-    n = i;
-    break;
+  const double s = a.s64;
+  const double u_smp = static_cast<double>(a.u[t0 + g]);  // the request's sample uniform
+  const int tper = (nt + kReqNT - 1) / kReqNT;
+  const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
+  __shared__ double tab[kExp2Tab];
+  __shared__ double tconst[kExp2Consts];
+  if (tid < kExp2Tab) tab[tid] = exp2(static_cast<double>(tid) / 64.0);
+  if (tid == 0) exp2_consts_init(tconst);
+  __syncthreads();
+  const Exp2Consts C = exp2_consts_load(tconst);
+
+  int start = 0;
+  for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
+    // first row >= start whose own accept test did not pass
+    if (tid == 0) rs.first = g;
+    __syncthreads();
+    for (int i = start + tid; i < g; i += kReqNT)
+      if (!(static_cast<uint32_t>(a.ws[t0 + i].y) & kRowAccepted)) atomicMin(&rs.first, i);
+    __syncthreads();
+    const int n = rs.first;
+    const int64_t trow = t0 + n;
+    const bool draft = n < g;
+    const uint32_t f0 = static_cast<uint32_t>(a.ws[trow].y);
+    const bool undecided = draft && (f0 & kRowUndecided);
+    const double4 st = a.rstat[trow];
+    const double m = st.x;
+    const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
+    const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
+    const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
+    const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+
+    // ---- fp64 pass: one tile per wave at a time, in four chunks of 8
+    // elements per lane; a ring of four raw chunks keeps the loads of the next
+    // three chunks in flight while one is computed
+    {
+      using Chunk = RawChunk<LT, VEC>;
+      Chunk ring[4];
+      int j = wave;
+      auto load = [&](int slot, int jj, int c) {
+        // chunks of tiles past the wave's last one re-read the last tile (in
+        // bounds, unused)
+        ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
+      };
+      double es = 0.0, ps = 0.0, qs = 0.0;
+      bool und = false;
+      auto compute = [&](int slot, auto pad) {
+        constexpr bool PD = decltype(pad)::value;
+        double ar[8], e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(k, V)), s, nms);
+        exp2_neg8(ar, tab, C, e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) es += e[k];
+        if (draft) {  // uniform; the element's side by a 0/1 factor
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const double q = static_cast<double>(ring[slot].template get_q<PD>(k, V));
+            const bool pos = e[k] > q * zhi;
+            const double w = pos ? 1.0 : 0.0;
+            ps = fma(e[k], w, ps);
+            qs = fma(q, w, qs);
+            und = und || (!pos && e[k] > q * zlo);
+          }
+        }
+      };
+      auto flush = [&](int jj) {
+        const double te = wave_sum_d(es);
+        double tp = 0.0, tq = 0.0;
+        if (draft) {
+          tp = wave_sum_d(ps);
+          tq = wave_sum_d(qs);
+        }
+        const bool tu = __any(und);
+        if (lane == 0) {
+          E[jj] = te;
+          P[jj] = tp;
+          Q[jj] = tq;
+          W[jj] = tu ? -1.0 : 0.0;  // -1 marks a tile with undecided elements
+        }
+        es = ps = qs = 0.0;
+        und = false;
+      };
+      if (j < nt) {
+        load(0, j, 0);
+        load(1, j, 1);
+        load(2, j, 2);
+        for (; j < nt; j += kReqWaves) {
+          const int jn = j + kReqWaves;
+          if (base_partial(j, nt, V)) {
+            load(3, j, 3); compute(0, std::true_type{});
+            load(0, jn, 0); compute(1, std::true_type{});
+            load(1, jn, 1); compute(2, std::true_type{});
+            load(2, jn, 2); compute(3, std::true_type{});
+          } else {
+            load(3, j, 3); compute(0, std::false_type{});
+            load(0, jn, 0); compute(1, std::false_type{});
+            load(1, jn, 1); compute(2, std::false_type{});
+            load(2, jn, 2); compute(3, std::false_type{});
+          }
+          flush(j);
+        }
+      }
+    }
+    __syncthreads();
+    double zl = 0.0;
+    for (int j = tid; j < nt; j += kReqNT) zl += E[j];
+    const double Z = block_sum<kReqNT>(zl, sc);
+    const double iz = 1.0 / Z;
+
+    uint32_t rflags = undecided ? (kRowExact | kWhyAccept) : 0u;
+    if (undecided) {
+      const int64_t x = a.x[d0 + n];
+      const bool x_ok = x >= 0 && x < V;
+      const double px = x_ok ? exp2_neg(fma(static_cast<double>(to_float(lrow[x])), s, nms), tab) * iz : 0.0;
+      const double qx = x_ok ? static_cast<double>(qrow[x]) : 0.0;
+      if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
+        if (tid == 0) a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags));
+        start = n + 1;
+        __syncthreads();
+        continue;
+      }
+    }
+
+    // ---- tile values: residual (draft row) or p (bonus row, or fallback)
+    int mode = draft ? 1 : 0;
+    if (draft) {
+      if (tid == 0) rs.nund = 0;
+      __syncthreads();
+      for (int j = tid; j < nt; j += kReqNT) {
+        if (W[j] < 0.0) ulist[atomicAdd(&rs.nund, 1)] = j;
+        else W[j] = fmax(0.0, P[j] * iz - Q[j]);
+      }
+      __syncthreads();
+      // tiles with undecided elements, one per wave, summed again with Z
+      for (int k = wave; k < rs.nund; k += kReqWaves) {
+        const int j = ulist[k];
+        const int base = j * kTile;
+        double ws = 0.0;
+        for (int c = 0; c < 4; ++c) {
+          float lv[8], qv[8];
+          load_chunk<LT, VEC, true>(lrow, qrow, V, base, lane, c, lv, qv);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            ws += fmax(0.0, exp2_neg(fma(static_cast<double>(lv[kk]), s, nms), tab) * iz - static_cast<double>(qv[kk]));
+            if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        ws = wave_sum_d(ws);
+        if (lane == 0) W[j] = ws;
+      }
+      __syncthreads();
+    }
+    auto tile_val = [&](int j) -> double { return mode == 1 ? W[j] : E[j] * iz; };
+    // ---- the rest is sequential work on one row: wave 0 alone, with wave-level
+    // scans (lanes in token order) and no block barriers
+    if (wave != 0) return;
+    // tile-level CDF: lane l owns tiles [l tp, (l + 1) tp)
+    const int tp = (nt + 63) / 64;
+    const int jlo = min(nt, lane * tp), jhi = min(nt, jlo + tp);
+    double tv = 0.0;
+    for (int j = jlo; j < jhi; ++j) tv += tile_val(j);
+    double incl = wave_scan_incl_d(tv);
+    double total = __shfl(incl, 63);
+    if (mode == 1) {
+      rflags |= kRowResidual;
+      if (total <= kFallbackMass) {  // residual mass too small: sample from p
+        mode = 0;
+        rflags |= kRowFallback;
+        tv = 0.0;
+        for (int j = jlo; j < jhi; ++j) tv += tile_val(j);
+        incl = wave_scan_incl_d(tv);
+        total = __shfl(incl, 63);
+      }
+    }
+    const double tau = u_smp * total;
+    // crossing tile: the smallest positive tile whose prefix reaches tau, else
+    // the last positive tile; pb = the prefix before it, in the scan's order
+    int jt = -1, jlast = -1;
+    double pb = 0.0;
+    {
+      double c = incl - tv;  // exclusive prefix of the lane
+      for (int j = jlo; j < jhi; ++j) {
+        const double v = tile_val(j);
+        if (v > 0.0) {
+          jlast = j;
+          if (jt < 0 && c + v >= tau) {
+            jt = j;
+            pb = c;
+          }
+        }
+        c += v;
+      }
+    }
+    const uint64_t hit = __ballot(jt >= 0);
+    if (hit) {
+      const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      jt = __shfl(jt, src);
+      pb = __shfl(pb, src);
+    } else {
+      int jl = jlast;
+      for (int o = 32; o > 0; o >>= 1) jl = max(jl, __shfl_xor(jl, o));
+      jt = jl >= 0 ? jl : 0;
+      // prefix before the last positive tile
+      double pl = 0.0;
+      for (int j = jlo; j < jhi; ++j)
+        if (j < jt) pl += tile_val(j);
+      pb = wave_sum_d(pl);
+    }
+    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31)
+    const int k0 = jt * kTile + 32 * lane;
+    float lv[32], qv[32];
+    load32<LT, VEC>(lrow, V, k0, lv);
+    load32q<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0, qv);
+    double wv[32];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      double ar[8], e[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(lv[8 * h + k]), s, nms);
+      exp2_neg8(ar, tab, C, e);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const double p = e[k] * iz;
+        wv[8 * h + k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[8 * h + k])) : p;
+      }
+    }
+    double ls = 0.0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) ls += wv[k];
+    const double lincl = wave_scan_incl_d(ls);
+    const double tl = tau - pb;
+    int tok = -1, lastpos = -1;
+    {
+      double c = lincl - ls;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        c += wv[k];
+        if (wv[k] > 0.0) {
+          lastpos = k0 + k;
+          if (tok < 0 && c >= tl) tok = k0 + k;
+        }
+      }
+    }
+    int token;
+    const uint64_t thit = __ballot(tok >= 0);
+    if (thit) {
+      token = __shfl(tok, __ffsll(static_cast<unsigned long long>(thit)) - 1);
+    } else {
+      int lp = lastpos;
+      for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+      token = lp >= 0 ? lp : jt * kTile;
+    }
+    // ---- outputs of the request
+    for (int i = lane; i <= g; i += 64) {
+      int64_t o = -1;
+      if (i < n) o = a.x[d0 + i];
+      else if (i == n) o = token;
+      sel.out[t0 + i] = o;
+    }
+    if (lane == 0) {
+      sel.nacc[b] = n;
+      a.ws[trow] = make_int2(token, static_cast<int>(rflags));
+    }
+    return;
   }
-  if (n == g) return;
-  if (!(static_cast<uint32_t>(a.ws[t0 + n].y) & kRowDeferred)) return;
-  Task t;
-  t.b = b;
-  t.g = g;
-  t.i = n;
-  t.trow = t0 + n;
-  t.drow = d0 + n;
-  t.srow = static_cast<int64_t>(d1) + b;
-  t.valid = true;
-  const double4 st = a.rstat[t.trow];
-  const float m = static_cast<float>(st.x);
-  const double Z = st.y;
-  const double bt = bound_terms(Z, st.z);
-  const double relZ = (bt + kSumErr * Z) / Z;
-  const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(a.V);
-  const float* __restrict__ qrow = a.q + t.drow * static_cast<int64_t>(a.V);
-  sample_row<LT, VEC, NT, true>(a, t, lrow, qrow, -1, false, m, Z, bt, relZ, 0.0, nullptr, nullptr, dynw, sc, sh);
 }
 
 // ----------------------------------------------------------------------------
@@ -1319,46 +2172,6 @@ __global__ __launch_bounds__(kNT) void greedy_rows_kernel(GreedyArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// per-request select: first rejection, then accepted drafts + one token
-
-struct SelectArgs {
-  const int64_t* x;
-  const int32_t* cu;
-  const int2* ws;
-  int64_t* out;
-  int32_t* nacc;
-  int* xcount;  // fp64-path list count, reset here for the next call (may be null)
-  int B, gamma, ndraft;
-};
-
-__global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
-  const int b = blockIdx.x * kSelectNT + threadIdx.x;
-  if (b == 0 && a.xcount) *a.xcount = 0;
-  if (b >= a.B) return;
-  int d0, d1;
-  if (a.cu) {
-    d0 = a.cu[b];
-    d1 = a.cu[b + 1];
-    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) {
-      // invalid offsets: emit nothing for this request
-      a.nacc[b] = 0;
-      return;
-    }
-  } else {
-    d0 = b * a.gamma;
-    d1 = d0 + a.gamma;
-  }
-  const int g = d1 - d0;
-  const int64_t t0 = static_cast<int64_t>(d0) + b;
-  int n = 0;
-  while (n < g && (static_cast<uint32_t>(a.ws[t0 + n].y) & kRowAccepted)) ++n;
-  for (int i = 0; i < n; ++i) a.out[t0 + i] = a.x[d0 + i];
-  a.out[t0 + n] = static_cast<int64_t>(a.ws[t0 + n].x);
-  for (int i = n + 1; i <= g; ++i) a.out[t0 + i] = -1;
-  a.nacc[b] = n;
-}
-
-// ----------------------------------------------------------------------------
 // self-check of the exp2 accuracy the fast path's error bound assumes
 
 __global__ void zero_double_kernel(double* p) { *p = 0.0; }
@@ -1398,19 +2211,26 @@ inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 
 // Workspace layout: [records rows x int2][count, 256 B][list rows x int2]
 // [etile rows x nt doubles][wtile rows x nt doubles][rstat rows x 4 doubles].
+// Workspace: row records, then the fp64 path's counters, list and per-tile
+// arrays, then the lazy mode's per-row statistics. Every part starts on a
+// 256-byte boundary.
 struct WsLayout {
-  size_t rec, count, list, etile, wtile, rstat, total;
+  size_t rec, count, list, done, etile, ptile, qtile, amb, rstat, total;
 };
 WsLayout ws_layout(int64_t rows, int V) {
   WsLayout l;
   const size_t nt = static_cast<size_t>((V + kTile - 1) / kTile);
+  const size_t r = static_cast<size_t>(rows);
   l.rec = 0;
-  l.count = align256(static_cast<size_t>(rows) * sizeof(int2));
+  l.count = align256(r * sizeof(int2));  // list count at +0, finished rows at +64
   l.list = l.count + 256;
-  l.etile = l.list + align256(static_cast<size_t>(rows) * sizeof(int2));
-  l.wtile = l.etile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
-  l.rstat = l.wtile + align256(static_cast<size_t>(rows) * nt * sizeof(double));
-  l.total = l.rstat + align256(static_cast<size_t>(rows) * 4 * sizeof(double));
+  l.done = l.list + align256(r * sizeof(ExactEntry));
+  l.etile = l.done + align256(r * sizeof(int));
+  l.ptile = l.etile + align256(r * nt * sizeof(double));
+  l.qtile = l.ptile + align256(r * nt * sizeof(double));
+  l.amb = l.qtile + align256(r * nt * sizeof(double));
+  l.rstat = l.amb + align256(r * nt * sizeof(int));
+  l.total = l.rstat + align256(r * 4 * sizeof(double));
   return l;
 }
 size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
@@ -1420,7 +2240,6 @@ size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * size
 // stream logits and q per row and prefer larger blocks (shorter per-row time).
 constexpr int kRowsNTLazy = 256;
 constexpr int kRowsNTEager = 512;
-constexpr int kRequestNT = 512;
 
 template <typename LT, bool VEC, int NT, bool EAGER>
 void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
@@ -1429,7 +2248,7 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
 }
 
 template <typename LT>
-int launch_probs(const ProbsArgs& a, const ExactArgs& e, int64_t rows, hipStream_t st) {
+int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, int64_t rows, hipStream_t st) {
   const int nt = (a.V + kTile - 1) / kTile;
   const size_t lds = static_cast<size_t>(nt) * 4 * sizeof(float);
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0 &&
@@ -1443,18 +2262,18 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, int64_t rows, hipStream
     else launch_rows<LT, false, kRowsNTEager, true>(a, rows, lds, st);
   }
   if (lazy) {
-    const size_t lds2 = static_cast<size_t>(nt) * sizeof(float);
+    // the per-request fp64 pass decides every request and writes the outputs
+    const size_t lds2 = static_cast<size_t>(nt) * (4 * sizeof(double) + sizeof(int));
     if (vec)
-      hipLaunchKernelGGL((residual_request_kernel<LT, true, kRequestNT>), dim3(static_cast<unsigned>(a.B)),
-                         dim3(kRequestNT), lds2, st, a);
+      hipLaunchKernelGGL((request_kernel<LT, true>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<true>()), lds2,
+                         st, a, sel);
     else
-      hipLaunchKernelGGL((residual_request_kernel<LT, false, kRequestNT>), dim3(static_cast<unsigned>(a.B)),
-                         dim3(kRequestNT), lds2, st, a);
+      hipLaunchKernelGGL((request_kernel<LT, false>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<false>()), lds2,
+                         st, a, sel);
+    return 0;
   }
-  hipLaunchKernelGGL((exact_tiles_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
-  hipLaunchKernelGGL((exact_residual_kernel<LT>), dim3(kExactGrid), dim3(kNT), 0, st, a, e);
-  hipLaunchKernelGGL((exact_finish_kernel<LT>), dim3(kNT), dim3(kNT), static_cast<size_t>(e.nt) * 2 * sizeof(double),
-                     st, a, e);
+  hipLaunchKernelGGL((exact_kernel<LT>), dim3(kExactItemGrid), dim3(kNT), static_cast<size_t>(e.nt) * 4 * sizeof(double),
+                     st, a, e, sel);
   return 0;
 }
 
@@ -1498,6 +2317,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
 
   char* wsb = static_cast<char*>(ws);
   int* xcount = greedy ? nullptr : reinterpret_cast<int*>(wsb + wl.count);
+  const SelectArgs sa{x, cu, wsp, out, nacc, B, gamma, ndraft};
   if (greedy) {
     GreedyArgs g{logits, x, cu, wsp, B, gamma, ndraft, V};
     if (dtype == SV_DTYPE_BF16) launch_greedy<uint16_t>(g, rows, st);
@@ -1518,24 +2338,31 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.gamma = gamma;
     p.ndraft = ndraft;
     p.V = V;
-    const bool lazy = !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS)) && stats == nullptr && q != nullptr;
+    // lazy (default): with q, no statistics, and not every row forced through the fp64 path
+    const bool lazy =
+        !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EXACT)) && stats == nullptr && q != nullptr;
     p.flags = flags | (lazy ? kFlagLazy : 0u);
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.xcount = xcount;
-    p.xlist = reinterpret_cast<int2*>(wsb + wl.list);
+    p.xlist = reinterpret_cast<ExactEntry*>(wsb + wl.list);
     ExactArgs e;
     e.count = xcount;
+    e.finished = reinterpret_cast<int*>(wsb + wl.count + 64);
+    e.done = reinterpret_cast<int*>(wsb + wl.done);
     e.list = p.xlist;
     e.etile = reinterpret_cast<double*>(wsb + wl.etile);
-    e.wtile = reinterpret_cast<double*>(wsb + wl.wtile);
+    e.ptile = reinterpret_cast<double*>(wsb + wl.ptile);
+    e.qtile = reinterpret_cast<double*>(wsb + wl.qtile);
+    e.amb = reinterpret_cast<int*>(wsb + wl.amb);
     e.nt = (V + kTile - 1) / kTile;
     e.rows = static_cast<int>(rows);
-    if (dtype == SV_DTYPE_BF16) launch_probs<uint16_t>(p, e, rows, st);
-    else launch_probs<float>(p, e, rows, st);
+    // the fp64 kernel ends with the per-request select
+    if (dtype == SV_DTYPE_BF16) launch_probs<uint16_t>(p, e, sa, rows, st);
+    else launch_probs<float>(p, e, sa, rows, st);
+    return finish_launch();
   }
   int rc = finish_launch();
   if (rc != SV_OK) return rc;
-  SelectArgs sa{x, cu, wsp, out, nacc, xcount, B, gamma, ndraft};
   hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>((B + kSelectNT - 1) / kSelectNT)), dim3(kSelectNT),
                      0, st, sa);
   return finish_launch();
