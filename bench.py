@@ -8,11 +8,19 @@ rejection select). Inputs are synthetic and seeded, already resident in HBM
 when the timed region starts.
 
 Prints one JSON line. `value` is verified draft positions per second
-(B * gamma per call). The roofline object prices the row kernel against HBM:
-algorithmic bytes = every target logit row once + the q rows the call had to
-read in full (rows whose replacement token was drawn) + one q(x) gather per
-accepted draft row. The oracle (float64 numpy) is timed on the host cores on
-the same inputs as the CPU baseline.
+(B * gamma per call). The roofline object prices the dominant kernel (the
+per-row pass) against HBM: its algorithmic bytes per launch are every target
+logit row once, plus per draft row the token, its q(x), the accept uniform and
+l(x), plus the row records and the statistics it hands to the per-request
+pass; its duration is the mean of HIP events the library records on the launch
+stream around that kernel over the timed region. The per-request pass is
+reported beside it (algorithmic bytes: the logit row and, for a replacement
+draw, the q row of each request's deciding row). `traffic` is the HBM traffic
+per launch of the dominant kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE
+counters scaled by a copy-kernel calibration, read from the committed summary
+under profiles/ only when that summary was taken on the current kernel source
+(else null). The oracle (float64 numpy) is timed on the host cores on the
+same inputs as the CPU baseline.
 """
 
 from __future__ import annotations
@@ -27,6 +35,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probs_rows_kernel_peaked_bf16_b256_g7_v128256_traffic.txt")
+
+
+def source_sha256() -> str:
+    import hashlib
+
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the per-row pass from the committed rocprofv3
+    summary, or None when it is missing or was taken on another source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_sha256():
+        return None
+    try:
+        return float(vals["rows_kernel_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=256 γ=7 V=128k"
 
 
@@ -73,7 +108,7 @@ def cpu_baseline(w, max_requests: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="peaked_bf16")
     ap.add_argument("--flags", type=int, default=0,
@@ -115,6 +150,7 @@ def main():
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    api.profile_start((api.SV_PROFILE_ROWS, api.SV_PROFILE_REQUEST), capacity=args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -123,6 +159,7 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    prof = api.profile_stop()
     ev_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = wall / args.steps * 1e3
     positions = B * g
@@ -134,11 +171,22 @@ def main():
     accepted_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_ACCEPTED))
     exact_rows = int(np.count_nonzero(flags & api.SV_ROW_EXACT))
     exact_why = {name: int(np.count_nonzero(flags & bit)) for bit, name in api.SV_ROW_WHY.items()}
-    q_bytes = 0 if q is None else residual_rows * V * 4 + (positions - residual_rows) * 4
-    alg_bytes = rows * V * esz + q_bytes
+    bonus_drawn = int(np.count_nonzero(rec[:, g, 0] >= 0))
+    # per-row pass: logits once; per draft row x (8 B), q(x) (4), u (4), l(x); records (8 per row)
+    # and the {m, Z, bound} statistics (32 B) of every row it leaves to the per-request pass
+    handed = int(np.count_nonzero((flags & api.SV_ROW_ACCEPTED) == 0)) if q is not None else 0
+    rows_bytes = rows * V * esz + positions * (8 + 4 + 4 + esz) + rows * 8 + handed * 32
+    # per-request pass: the deciding row's logits and, for a replacement draw, its q row
+    req_bytes = residual_rows * V * (esz + 4) + bonus_drawn * V * esz
+    alg_bytes = rows_bytes + req_bytes
     full_bytes = rows * V * esz + (0 if q is None else positions * V * 4)
     call_s = float(np.mean(ev_ms)) * 1e-3
-    achieved = alg_bytes / call_s / 1e9
+    rows_ms, rows_n = prof[api.SV_PROFILE_ROWS]
+    req_ms, req_n = prof[api.SV_PROFILE_REQUEST]
+    rows_s = rows_ms / max(rows_n, 1) * 1e-3
+    req_s = req_ms / max(req_n, 1) * 1e-3
+    achieved = rows_bytes / rows_s / 1e9 if rows_n else None
+    traffic = measured_traffic()
 
     result = {
         "metric": METRIC,
@@ -156,12 +204,18 @@ def main():
         "config": {"workload": f"{args.workload}: B={B} gamma={g} V={V} T={T} {w['dtype']} logits",
                    "global_batch": B, "gamma": g, "vocab": V, "flags": args.flags},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_call": alg_bytes,
-                     "kernel_ms_mean": float(np.mean(ev_ms)), "kernel_ms_p10": float(np.percentile(ev_ms, 10)),
-                     "kernel_ms_p90": float(np.percentile(ev_ms, 90)),
-                     "note": "time = hipEvents around each call (row kernel + select kernel) on the launch stream"},
+                     "frac": None if achieved is None else achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "probs_rows_kernel (per-row pass)", "bytes_per_launch": rows_bytes,
+                     "launch_ms_mean": rows_s * 1e3, "launches_timed": rows_n,
+                     "note": "HIP events recorded by the library on the launch stream around the kernel"},
+        "request_pass": {"kernel": "request_kernel (per-request fp64 pass)", "bytes_per_launch": req_bytes,
+                         "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
+                         "achieved_GBps": req_bytes / req_s / 1e9 if req_n else None},
+        "whole_call": {"bytes": alg_bytes, "ms_mean": float(np.mean(ev_ms)), "ms_median": float(np.median(ev_ms)),
+                       "ms_p10": float(np.percentile(ev_ms, 10)), "ms_p90": float(np.percentile(ev_ms, 90)),
+                       "achieved_GBps": alg_bytes / call_s / 1e9},
         "rows": {"draft": positions, "accepted_own_test": accepted_rows, "residual_drawn": residual_rows,
+                 "bonus_drawn": bonus_drawn,
                  "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item())},
         "speculative_full_bytes_per_call": full_bytes,
         "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,

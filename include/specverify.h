@@ -128,6 +128,25 @@ int spec_verify_version(void);
 int spec_verify_selftest_exp2(double* max_rel_err, void* stream);
 double spec_verify_exp2_error_bound(void);
 
+/* Benchmark diagnostics: time kernels of the probabilistic entry points with
+ * HIP events that the library records on the launch stream right before and
+ * right after each launch of a selected kernel.
+ *   kernel_mask  bit SV_PROFILE_ROWS: the per-row pass (softmax statistics
+ *                and accept test, every mode); bit SV_PROFILE_REQUEST: the
+ *                per-request fp64 pass of the default (lazy) mode
+ *   capacity     launches recorded per kernel, 1 .. 2^20; later ones are not
+ * spec_verify_profile_start drops any earlier recording, creates the events
+ * and starts recording (SV_ERR_INVALID_ARGUMENT for a bad mask or capacity,
+ * SV_ERR_LAUNCH if events cannot be created). spec_verify_profile_stop waits
+ * for the recorded events, writes per kernel id (arrays of 2) the summed
+ * duration in milliseconds and the number of launches recorded, releases the
+ * events and stops recording (either pointer may be NULL). Library-wide host
+ * state: not for concurrent callers. */
+#define SV_PROFILE_ROWS 0
+#define SV_PROFILE_REQUEST 1
+int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity);
+int spec_verify_profile_stop(double* total_ms, int32_t* launches);
+
 /*
  * spec_verify_probs - dense batch, rejection-sampling verification.
  *

@@ -29,10 +29,12 @@ SV_ROW_FALLBACK = 0x8
 SV_ROW_DEFERRED = 0x400
 SV_ROW_UNDECIDED = 0x800
 SV_ROW_WHY = {0x10: "accept", 0x20: "fallback", 0x40: "search", 0x80: "margin", 0x100: "forced"}
+SV_PROFILE_ROWS = 0
+SV_PROFILE_REQUEST = 1
 
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
            "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
-           "spec_verify_exp2_error_bound")
+           "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop")
 
 _lib = None
 
@@ -64,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_selftest_exp2.restype = ctypes.c_int
     lib.spec_verify_exp2_error_bound.argtypes = []
     lib.spec_verify_exp2_error_bound.restype = ctypes.c_double
+    lib.spec_verify_profile_start.argtypes = [u32, i32]
+    lib.spec_verify_profile_start.restype = ctypes.c_int
+    lib.spec_verify_profile_stop.argtypes = [vp, vp]
+    lib.spec_verify_profile_stop.restype = ctypes.c_int
     lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_probs.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
@@ -217,6 +223,26 @@ def selftest_exp2(device=None, stream=None):
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_selftest_exp2")
     return float(out.item()), float(lib.spec_verify_exp2_error_bound())
+
+
+def profile_start(kernels=(SV_PROFILE_ROWS, SV_PROFILE_REQUEST), capacity=1024):
+    """Start recording HIP events around the given kernels (see the header)."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << int(k)
+    rc = load().spec_verify_profile_start(mask, int(capacity))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_profile_start")
+
+
+def profile_stop():
+    """Stop recording; returns {kernel id: (summed ms, launches)}."""
+    total = (ctypes.c_double * 2)()
+    count = (ctypes.c_int32 * 2)()
+    rc = load().spec_verify_profile_stop(ctypes.cast(total, ctypes.c_void_p), ctypes.cast(count, ctypes.c_void_p))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_profile_stop")
+    return {SV_PROFILE_ROWS: (float(total[0]), int(count[0])), SV_PROFILE_REQUEST: (float(total[1]), int(count[1]))}
 
 
 def row_records(workspace, num_target_rows):

@@ -1494,10 +1494,12 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
 // draft is accepted, the bonus row is sampled from p the same way. The block
 // then writes the request's outputs.
 
-// Block size: 512 threads (2 waves per SIMD, up to 256 VGPRs each); the
-// eight-wide exp phases supply the instruction-level parallelism.
+// Block size: 512 threads (2 waves per SIMD, up to 256 VGPRs each), with
+// eight exps in flight per lane; smaller register budgets (more waves) spill
+// and measured slower.
 template <bool VEC>
 constexpr int req_nt() { return 512; }
+constexpr int kExpW = 8;  // exps in flight per lane in the pass
 constexpr int kExp2Tab = 64;  // 2^(j/64), j = 0..63
 
 // 2^a in fp64 for a <= 0 (or -inf), to about 1 ulp. J = round(64 a) comes out
@@ -1537,19 +1539,22 @@ __device__ __forceinline__ void exp2_consts_init(double* lds) {
   for (int i = 0; i < kExp2Consts; ++i) lds[i] = v[i];
 }
 __device__ __forceinline__ Exp2Consts exp2_consts_load(const double* lds) {
-  return Exp2Consts{lds[0], lds[1], lds[2], lds[3], lds[4], lds[5], lds[6], lds[7], lds[8]};
+  (void)lds;  // compile-time constants: scalar operands or rematerialised, no VGPRs held
+  return Exp2Consts{6755399441055744.0, 64.0, -0.015625, -1100.0, 0.6931471805599453, 0.2402265069591007,
+                    0.05550410866482158, 0.009618129107628477, 0.0013333558146428443};
 }
 
-// exp2_neg of 8 arguments at once, in phases (all table reads, then all
+// exp2_neg of N arguments at once, in phases (all table reads, then all
 // polynomials, then the scaling), so that the LDS latency is paid once.
-__device__ __forceinline__ void exp2_neg8(const double (&a)[8], const double* __restrict__ tab, const Exp2Consts& C,
-                                          double (&e)[8]) {
+template <int N>
+__device__ __forceinline__ void exp2_negN(const double (&a)[N], const double* __restrict__ tab, const Exp2Consts& C,
+                                          double (&e)[N]) {
   const double kRnd = C.rnd;
   const double c1 = C.c1, c2 = C.c2, c3 = C.c3, c4 = C.c4, c5 = C.c5;
-  double r[8], tv[8];
-  int J[8];
+  double r[N], tv[N];
+  int J[N];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < N; ++k) {
     const double ak = fmax(a[k], C.lo);
     const double t = fma(ak, C.c64, kRnd);
     r[k] = fma(t - kRnd, C.cinv64, ak);
@@ -1557,7 +1562,7 @@ __device__ __forceinline__ void exp2_neg8(const double (&a)[8], const double* __
     tv[k] = tab[J[k] & 63];
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < N; ++k) {
     double p = fma(c5, r[k], c4);
     p = fma(p, r[k], c3);
     p = fma(p, r[k], c2);
@@ -1733,26 +1738,23 @@ __device__ __forceinline__ double wave_scan_incl_d(double v) {
   return v;
 }
 
-// 32 consecutive elements from k0 (a multiple of 32), as fp32 logits (-inf
-// past the end of the row) or q (0 past the end; q == nullptr: zeros, with
+// 8 consecutive elements from k0 (a multiple of 8), as fp32 logits (-inf past
+// the end of the row) or q (0 past the end; q == nullptr: zeros, with
 // fallback[0] read instead so that the loads need no branch). Loads are
 // unconditional, with addresses clamped into the row.
 template <typename LT, bool VEC>
-__device__ __forceinline__ void load32(const LT* __restrict__ row, int V, int k0, float (&v)[32]) {
+__device__ __forceinline__ void load8f(const LT* __restrict__ row, int V, int k0, float (&v)[8]) {
   if constexpr (VEC && sizeof(LT) == 2) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + min(k0, V - 8));
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint4 w = *reinterpret_cast<const uint4*>(row + min(k0 + 8 * h, V - 8));
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[8 * h + 2 * i] = __uint_as_float(ww[i] << 16);
-        v[8 * h + 2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
-      }
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(ww[i] << 16);
+      v[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
     }
   } else if constexpr (VEC) {
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
+    for (int h = 0; h < 2; ++h) {
       const float4 w = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row) + min(k0 + 4 * h, V - 4));
       v[4 * h] = w.x;
       v[4 * h + 1] = w.y;
@@ -1761,36 +1763,33 @@ __device__ __forceinline__ void load32(const LT* __restrict__ row, int V, int k0
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] = to_float(row[min(k0 + k, V - 1)]);
+    for (int k = 0; k < 8; ++k) v[k] = to_float(row[min(k0 + k, V - 1)]);
   }
 #pragma unroll
-  for (int k = 0; k < 32; ++k)
+  for (int k = 0; k < 8; ++k)
     if (k0 + k >= V) v[k] = -INFINITY;
 }
 template <bool VEC>
-__device__ __forceinline__ void load32q(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
-                                        float (&v)[32]) {
+__device__ __forceinline__ void load8qf(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
+                                        float (&v)[8]) {
   const bool has = q != nullptr;
+  const float* src = has ? q : fallback;
   if constexpr (VEC) {
-    const float* src = has ? q : fallback;
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      float4 w;
-      if (has) w = *reinterpret_cast<const float4*>(src + min(k0 + 4 * h, V - 4));
-      else w = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int h = 0; h < 2; ++h) {
+      const float4 w = *reinterpret_cast<const float4*>(src + (has ? min(k0 + 4 * h, V - 4) : 0));
       v[4 * h] = w.x;
       v[4 * h + 1] = w.y;
       v[4 * h + 2] = w.z;
       v[4 * h + 3] = w.w;
     }
   } else {
-    const float* src = has ? q : fallback;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) v[k] = has ? src[min(k0 + k, V - 1)] : 0.f;
+    for (int k = 0; k < 8; ++k) v[k] = src[has ? min(k0 + k, V - 1) : 0];
   }
 #pragma unroll
-  for (int k = 0; k < 32; ++k)
-    if (k0 + k >= V) v[k] = 0.f;
+  for (int k = 0; k < 8; ++k)
+    if (!has || k0 + k >= V) v[k] = 0.f;
 }
 
 // whether tile j of a row of V elements reaches past its end
@@ -1885,21 +1884,25 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
       bool und = false;
       auto compute = [&](int slot, auto pad) {
         constexpr bool PD = decltype(pad)::value;
-        double ar[8], e[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(k, V)), s, nms);
-        exp2_neg8(ar, tab, C, e);
+        for (int h = 0; h < 8; h += kExpW) {
+          double ar[kExpW], e[kExpW];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) es += e[k];
-        if (draft) {  // uniform; the element's side by a 0/1 factor
+          for (int k = 0; k < kExpW; ++k)
+            ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(h + k, V)), s, nms);
+          exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const double q = static_cast<double>(ring[slot].template get_q<PD>(k, V));
-            const bool pos = e[k] > q * zhi;
-            const double w = pos ? 1.0 : 0.0;
-            ps = fma(e[k], w, ps);
-            qs = fma(q, w, qs);
-            und = und || (!pos && e[k] > q * zlo);
+          for (int k = 0; k < kExpW; ++k) es += e[k];
+          if (draft) {  // uniform; the element's side by a 0/1 factor
+#pragma unroll
+            for (int k = 0; k < kExpW; ++k) {
+              const double q = static_cast<double>(ring[slot].template get_q<PD>(h + k, V));
+              const bool pos = e[k] > q * zhi;
+              const double w = pos ? 1.0 : 0.0;
+              ps = fma(e[k], w, ps);
+              qs = fma(q, w, qs);
+              und = und || (!pos && e[k] > q * zlo);
+            }
           }
         }
       };
@@ -2046,38 +2049,48 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
         if (j < jt) pl += tile_val(j);
       pb = wave_sum_d(pl);
     }
-    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31)
+    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31);
+    // the weights are computed twice (lane sums, then the crossing lane's
+    // prefix) rather than held in registers
     const int k0 = jt * kTile + 32 * lane;
-    float lv[32], qv[32];
-    load32<LT, VEC>(lrow, V, k0, lv);
-    load32q<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0, qv);
-    double wv[32];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    auto weights8 = [&](int h, double (&w8)[8]) {
+      float lv[8], qv[8];
+      load8f<LT, VEC>(lrow, V, k0 + 8 * h, lv);
+      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qv);
       double ar[8], e[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(lv[8 * h + k]), s, nms);
-      exp2_neg8(ar, tab, C, e);
+      for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(lv[k]), s, nms);
+      exp2_negN<8>(ar, tab, C, e);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const double p = e[k] * iz;
-        wv[8 * h + k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[8 * h + k])) : p;
+        w8[k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[k])) : p;
       }
-    }
+    };
     double ls = 0.0;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) ls += wv[k];
+    for (int h = 0; h < 4; ++h) {
+      double w8[8];
+      weights8(h, w8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ls += w8[k];
+    }
     const double lincl = wave_scan_incl_d(ls);
     const double tl = tau - pb;
     int tok = -1, lastpos = -1;
     {
       double c = lincl - ls;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        c += wv[k];
-        if (wv[k] > 0.0) {
-          lastpos = k0 + k;
-          if (tok < 0 && c >= tl) tok = k0 + k;
+      for (int h = 0; h < 4; ++h) {
+        double w8[8];
+        weights8(h, w8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          c += w8[k];
+          if (w8[k] > 0.0) {
+            lastpos = k0 + 8 * h + k;
+            if (tok < 0 && c >= tl) tok = k0 + 8 * h + k;
+          }
         }
       }
     }
@@ -2247,6 +2260,22 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
                      a);
 }
 
+// Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
+// recorded on the launch stream around the selected kernels. Host state.
+struct Profiler {
+  uint32_t mask = 0;
+  int capacity = 0;
+  hipEvent_t* ev[2] = {nullptr, nullptr};  // per kernel id: [capacity][2] start, stop
+  int used[2] = {0, 0};
+};
+Profiler g_prof;
+
+void prof_record(int id, int which, hipStream_t st) {
+  if (!(g_prof.mask & (1u << id)) || g_prof.used[id] >= g_prof.capacity) return;
+  hipEventRecord(g_prof.ev[id][2 * g_prof.used[id] + which], st);
+  if (which == 1) ++g_prof.used[id];
+}
+
 template <typename LT>
 int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, int64_t rows, hipStream_t st) {
   const int nt = (a.V + kTile - 1) / kTile;
@@ -2254,6 +2283,7 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, 
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0 &&
                    (a.q == nullptr || (aligned16(a.q) && (a.V % 4) == 0));
   const bool lazy = (a.flags & kFlagLazy) != 0;
+  prof_record(SV_PROFILE_ROWS, 0, st);
   if (vec) {
     if (lazy) launch_rows<LT, true, kRowsNTLazy, false>(a, rows, lds, st);
     else launch_rows<LT, true, kRowsNTEager, true>(a, rows, lds, st);
@@ -2261,15 +2291,18 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, 
     if (lazy) launch_rows<LT, false, kRowsNTLazy, false>(a, rows, lds, st);
     else launch_rows<LT, false, kRowsNTEager, true>(a, rows, lds, st);
   }
+  prof_record(SV_PROFILE_ROWS, 1, st);
   if (lazy) {
     // the per-request fp64 pass decides every request and writes the outputs
     const size_t lds2 = static_cast<size_t>(nt) * (4 * sizeof(double) + sizeof(int));
+    prof_record(SV_PROFILE_REQUEST, 0, st);
     if (vec)
       hipLaunchKernelGGL((request_kernel<LT, true>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<true>()), lds2,
                          st, a, sel);
     else
       hipLaunchKernelGGL((request_kernel<LT, false>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<false>()), lds2,
                          st, a, sel);
+    prof_record(SV_PROFILE_REQUEST, 1, st);
     return 0;
   }
   hipLaunchKernelGGL((exact_kernel<LT>), dim3(kExactItemGrid), dim3(kNT), static_cast<size_t>(e.nt) * 4 * sizeof(double),
@@ -2391,6 +2424,57 @@ const char* spec_verify_status_string(int status) {
 int spec_verify_version(void) { return 1; }
 
 double spec_verify_exp2_error_bound(void) { return kEpsExp; }
+
+int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20) || (kernel_mask & ~3u) || !kernel_mask) return SV_ERR_INVALID_ARGUMENT;
+  double t[2];
+  int n[2];
+  spec_verify_profile_stop(t, n);  // drops any earlier recording
+  for (int id = 0; id < 2; ++id) {
+    if (!(kernel_mask & (1u << id))) continue;
+    g_prof.ev[id] = new hipEvent_t[2 * static_cast<size_t>(capacity)];
+    for (int i = 0; i < 2 * capacity; ++i) {
+      if (hipEventCreate(&g_prof.ev[id][i]) != hipSuccess) {
+        for (int k = 0; k < i; ++k) hipEventDestroy(g_prof.ev[id][k]);
+        delete[] g_prof.ev[id];
+        g_prof.ev[id] = nullptr;
+        spec_verify_profile_stop(t, n);
+        return SV_ERR_LAUNCH;
+      }
+    }
+  }
+  g_prof.mask = kernel_mask;
+  g_prof.capacity = capacity;
+  g_prof.used[0] = g_prof.used[1] = 0;
+  return SV_OK;
+}
+
+int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
+  int rc = SV_OK;
+  for (int id = 0; id < 2; ++id) {
+    double sum = 0.0;
+    int used = 0;
+    if (g_prof.ev[id]) {
+      used = g_prof.used[id];
+      for (int i = 0; i < used; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(g_prof.ev[id][2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_prof.ev[id][2 * i], g_prof.ev[id][2 * i + 1]) != hipSuccess)
+          rc = SV_ERR_LAUNCH;
+        sum += ms;
+      }
+      for (int i = 0; i < 2 * g_prof.capacity; ++i) hipEventDestroy(g_prof.ev[id][i]);
+      delete[] g_prof.ev[id];
+      g_prof.ev[id] = nullptr;
+    }
+    if (total_ms) total_ms[id] = sum;
+    if (launches) launches[id] = used;
+  }
+  g_prof.mask = 0;
+  g_prof.capacity = 0;
+  g_prof.used[0] = g_prof.used[1] = 0;
+  return rc;
+}
 
 int spec_verify_selftest_exp2(double* max_rel_err, void* stream) {
   if (!max_rel_err) return SV_ERR_INVALID_ARGUMENT;
