@@ -1494,12 +1494,7 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
 // draft is accepted, the bonus row is sampled from p the same way. The block
 // then writes the request's outputs.
 
-// Block size: 512 threads (2 waves per SIMD, up to 256 VGPRs each), with
-// eight exps in flight per lane; smaller register budgets (more waves) spill
-// and measured slower.
-template <bool VEC>
-constexpr int req_nt() { return 512; }
-constexpr int kExpW = 8;  // exps in flight per lane in the pass
+constexpr int kExpW = 4;  // exps in flight per lane in the fp64 pass
 constexpr int kExp2Tab = 64;  // 2^(j/64), j = 0..63
 
 // 2^a in fp64 for a <= 0 (or -inf), to about 1 ulp. J = round(64 a) comes out
@@ -1805,15 +1800,164 @@ struct ReqShared {
   int pad;
 };
 
-template <typename LT, bool VEC, int kReqNT = req_nt<VEC>()>
-__global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs sel) {
-  constexpr int kReqWaves = kReqNT / 64;
-  constexpr int kReqPer = kTile / kReqNT;  // elements per thread in the in-tile search
+// The fp64 pass of one row over tiles j = j0, j0 + step, ... < j1, one tile
+// per wave at a time, in four chunks of 8 elements per lane; a ring of four
+// raw chunks keeps the loads of the next three chunks in flight while one is
+// computed. Per tile it writes E_j (sum of e_k) and, for a draft row, Q_j and
+// P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
+// interval leaves an element undecided (LDS or global, indexed by tile).
+template <typename LT, bool VEC>
+__device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
+                              double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
+                              const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q) {
+  const int lane = threadIdx.x & 63;
+  const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
+  using Chunk = RawChunk<LT, VEC>;
+  Chunk ring[4];
+  auto load = [&](int slot, int jj, int c) {
+    // chunks past the wave's last tile re-read the row's last tile (in bounds, unused)
+    ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
+  };
+  double es = 0.0, ps = 0.0, qs = 0.0;
+  bool und = false;
+  auto compute = [&](int slot, auto pad) {
+    constexpr bool PD = decltype(pad)::value;
+#pragma unroll
+    for (int h = 0; h < 8; h += kExpW) {
+      double ar[kExpW], e[kExpW];
+#pragma unroll
+      for (int k = 0; k < kExpW; ++k) ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(h + k, V)), s, nms);
+      exp2_negN<kExpW>(ar, tab, C, e);
+#pragma unroll
+      for (int k = 0; k < kExpW; ++k) es += e[k];
+      if (draft) {  // uniform; the element's side by a 0/1 factor
+#pragma unroll
+        for (int k = 0; k < kExpW; ++k) {
+          const double q = static_cast<double>(ring[slot].template get_q<PD>(h + k, V));
+          const bool pos = e[k] > q * zhi;
+          const double w = pos ? 1.0 : 0.0;
+          ps = fma(e[k], w, ps);
+          qs = fma(q, w, qs);
+          und = und || (!pos && e[k] > q * zlo);
+        }
+      }
+    }
+  };
+  auto flush = [&](int jj) {
+    const double te = wave_sum_d(es);
+    double tp = 0.0, tq = 0.0;
+    if (draft) {
+      tp = wave_sum_d(ps);
+      tq = wave_sum_d(qs);
+    }
+    const bool tu = __any(und);
+    if (lane == 0) {
+      E[jj] = te;
+      P[jj] = tu ? -1.0 : tp;
+      Q[jj] = tq;
+    }
+    es = ps = qs = 0.0;
+    und = false;
+  };
+  int j = j0;
+  if (j >= j1) return;
+  load(0, j, 0);
+  load(1, j, 1);
+  load(2, j, 2);
+  for (; j < j1; j += step) {
+    const int jn = j + step < j1 ? j + step : j;
+    if (base_partial(j, nt, V)) {
+      load(3, j, 3); compute(0, std::true_type{});
+      load(0, jn, 0); compute(1, std::true_type{});
+      load(1, jn, 1); compute(2, std::true_type{});
+      load(2, jn, 2); compute(3, std::true_type{});
+    } else {
+      load(3, j, 3); compute(0, std::false_type{});
+      load(0, jn, 0); compute(1, std::false_type{});
+      load(1, jn, 1); compute(2, std::false_type{});
+      load(2, jn, 2); compute(3, std::false_type{});
+    }
+    flush(j);
+  }
+}
+
+// The request's first row >= start whose own accept test did not pass (g if
+// none), found by the whole block; uniform (scalar) on return.
+template <int NT>
+__device__ __forceinline__ int first_open_row(const int2* __restrict__ ws, int64_t t0, int start, int g, int* slot) {
+  if (threadIdx.x == 0) *slot = g;
+  __syncthreads();
+  for (int i = start + static_cast<int>(threadIdx.x); i < g; i += NT)
+    if (!(static_cast<uint32_t>(ws[t0 + i].y) & kRowAccepted)) atomicMin(slot, i);
+  __syncthreads();
+  const int n = __builtin_amdgcn_readfirstlane(*slot);
+  __syncthreads();
+  return n;
+}
+
+__device__ __forceinline__ bool request_range(const ProbsArgs& a, int b, int& d0, int& d1) {
+  if (a.cu) {
+    d0 = a.cu[b];
+    d1 = a.cu[b + 1];
+    return d0 >= 0 && d1 >= d0 && d1 <= a.ndraft;
+  }
+  d0 = b * a.gamma;
+  d1 = d0 + a.gamma;
+  return true;
+}
+
+constexpr int kPassNT = 256;       // threads per block of the pass kernel
+constexpr int kPassWaves = kPassNT / 64;
+constexpr int kPassSlices = 3;     // blocks per request in the pass kernel (768: one round at 3 blocks per CU)
+constexpr int kFinishNT = 256;     // threads per block of the finish kernel
+constexpr int kFinishWaves = kFinishNT / 64;
+
+struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the fp64 path's tile arrays)
+  double* E;
+  double* P;
+  double* Q;
+};
+
+// Lazy mode, per-request pass: kPassSlices blocks per request, each over a
+// slice of the deciding row's tiles.
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, PassArrays pa) {
+  __shared__ double tab[kExp2Tab];
+  __shared__ int slot;
+  const int b = blockIdx.x / kPassSlices, sl = blockIdx.x % kPassSlices;
+  const int V = a.V, nt = (V + kTile - 1) / kTile;
+  const int wave = threadIdx.x >> 6;
+  int d0, d1;
+  if (!request_range(a, b, d0, d1)) return;
+  const int g = d1 - d0;
+  const int64_t t0 = static_cast<int64_t>(d0) + b;
+  if (threadIdx.x < kExp2Tab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / 64.0);
+  const int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &slot);  // (its barriers also publish tab)
+  const Exp2Consts C = exp2_consts_load(nullptr);
+  const int64_t trow = t0 + n;
+  const bool draft = n < g;
+  const double4 st = a.rstat[trow];
+  const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
+  const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
+  const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+  const int per = (nt + kPassSlices - 1) / kPassSlices;
+  const int j0 = sl * per, j1 = min(nt, j0 + per);
+  const int64_t o = static_cast<int64_t>(b) * nt;
+  fp64_row_pass<LT, VEC>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, draft, j0 + wave, j1, kPassWaves, tab, C,
+                         pa.E + o, pa.P + o, pa.Q + o);
+}
+
+// Lazy mode, per-request finish: one block per request. Z from the pass's
+// tile sums; an undecided accept test settled exactly (if the row is accepted
+// after all, the next open row gets its fp64 pass here, in LDS); residual tile
+// sums W_j = P_j / Z - Q_j, tiles with undecided elements summed again with
+// Z; then wave 0 draws the token and writes the request's outputs.
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa) {
   extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
-  __shared__ BlockScratchT<kReqNT> sc;
+  __shared__ BlockScratchT<kFinishNT> sc;
   __shared__ ReqShared rs;
-  using L = Lay<LT, VEC>;
-  using Raw = RawTile<LT, VEC>;
+  __shared__ double tab[kExp2Tab];
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
   double* E = rbuf;
@@ -1824,130 +1968,46 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   int d0, d1;
-  if (a.cu) {
-    d0 = a.cu[b];
-    d1 = a.cu[b + 1];
-    if (d0 < 0 || d1 < d0 || d1 > a.ndraft) {
-      if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
-      return;
-    }
-  } else {
-    d0 = b * a.gamma;
-    d1 = d0 + a.gamma;
+  if (!request_range(a, b, d0, d1)) {
+    if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
+    return;
   }
   const int g = d1 - d0;
   const int64_t t0 = static_cast<int64_t>(d0) + b;
   const double s = a.s64;
   const double u_smp = static_cast<double>(a.u[t0 + g]);  // the request's sample uniform
-  const int tper = (nt + kReqNT - 1) / kReqNT;
-  const int tlo = min(nt, tid * tper), thi = min(nt, tlo + tper);
-  __shared__ double tab[kExp2Tab];
-  __shared__ double tconst[kExp2Consts];
   if (tid < kExp2Tab) tab[tid] = exp2(static_cast<double>(tid) / 64.0);
-  if (tid == 0) exp2_consts_init(tconst);
-  __syncthreads();
-  const Exp2Consts C = exp2_consts_load(tconst);
+  const Exp2Consts C = exp2_consts_load(nullptr);
 
   int start = 0;
+  bool from_pass = true;  // the first open row's tile sums come from the pass kernel
   for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
-    // first row >= start whose own accept test did not pass
-    if (tid == 0) rs.first = g;
-    __syncthreads();
-    for (int i = start + tid; i < g; i += kReqNT)
-      if (!(static_cast<uint32_t>(a.ws[t0 + i].y) & kRowAccepted)) atomicMin(&rs.first, i);
-    __syncthreads();
-    const int n = rs.first;
+    const int n = first_open_row<kFinishNT>(a.ws, t0, start, g, &rs.first);
     const int64_t trow = t0 + n;
     const bool draft = n < g;
     const uint32_t f0 = static_cast<uint32_t>(a.ws[trow].y);
     const bool undecided = draft && (f0 & kRowUndecided);
     const double4 st = a.rstat[trow];
     const double m = st.x;
-    const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
-    const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
+    const double nms = -(m * s);
     const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
     const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
-
-    // ---- fp64 pass: one tile per wave at a time, in four chunks of 8
-    // elements per lane; a ring of four raw chunks keeps the loads of the next
-    // three chunks in flight while one is computed
-    {
-      using Chunk = RawChunk<LT, VEC>;
-      Chunk ring[4];
-      int j = wave;
-      auto load = [&](int slot, int jj, int c) {
-        // chunks of tiles past the wave's last one re-read the last tile (in
-        // bounds, unused)
-        ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
-      };
-      double es = 0.0, ps = 0.0, qs = 0.0;
-      bool und = false;
-      auto compute = [&](int slot, auto pad) {
-        constexpr bool PD = decltype(pad)::value;
-#pragma unroll
-        for (int h = 0; h < 8; h += kExpW) {
-          double ar[kExpW], e[kExpW];
-#pragma unroll
-          for (int k = 0; k < kExpW; ++k)
-            ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(h + k, V)), s, nms);
-          exp2_negN<kExpW>(ar, tab, C, e);
-#pragma unroll
-          for (int k = 0; k < kExpW; ++k) es += e[k];
-          if (draft) {  // uniform; the element's side by a 0/1 factor
-#pragma unroll
-            for (int k = 0; k < kExpW; ++k) {
-              const double q = static_cast<double>(ring[slot].template get_q<PD>(h + k, V));
-              const bool pos = e[k] > q * zhi;
-              const double w = pos ? 1.0 : 0.0;
-              ps = fma(e[k], w, ps);
-              qs = fma(q, w, qs);
-              und = und || (!pos && e[k] > q * zlo);
-            }
-          }
-        }
-      };
-      auto flush = [&](int jj) {
-        const double te = wave_sum_d(es);
-        double tp = 0.0, tq = 0.0;
-        if (draft) {
-          tp = wave_sum_d(ps);
-          tq = wave_sum_d(qs);
-        }
-        const bool tu = __any(und);
-        if (lane == 0) {
-          E[jj] = te;
-          P[jj] = tp;
-          Q[jj] = tq;
-          W[jj] = tu ? -1.0 : 0.0;  // -1 marks a tile with undecided elements
-        }
-        es = ps = qs = 0.0;
-        und = false;
-      };
-      if (j < nt) {
-        load(0, j, 0);
-        load(1, j, 1);
-        load(2, j, 2);
-        for (; j < nt; j += kReqWaves) {
-          const int jn = j + kReqWaves;
-          if (base_partial(j, nt, V)) {
-            load(3, j, 3); compute(0, std::true_type{});
-            load(0, jn, 0); compute(1, std::true_type{});
-            load(1, jn, 1); compute(2, std::true_type{});
-            load(2, jn, 2); compute(3, std::true_type{});
-          } else {
-            load(3, j, 3); compute(0, std::false_type{});
-            load(0, jn, 0); compute(1, std::false_type{});
-            load(1, jn, 1); compute(2, std::false_type{});
-            load(2, jn, 2); compute(3, std::false_type{});
-          }
-          flush(j);
-        }
+    if (from_pass) {
+      const int64_t o = static_cast<int64_t>(b) * nt;
+      for (int j = tid; j < nt; j += kFinishNT) {
+        E[j] = pa.E[o + j];
+        P[j] = pa.P[o + j];
+        Q[j] = pa.Q[o + j];
       }
+    } else {  // a later row (an undecided accept test turned out accepted): its pass here
+      const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
+      fp64_row_pass<LT, VEC>(lrow, qrow, V, nt, m, s, zhi, zlo, draft, wave, nt, kFinishWaves, tab, C, E, P, Q);
     }
     __syncthreads();
+    for (int j = tid; j < nt; j += kFinishNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
     double zl = 0.0;
-    for (int j = tid; j < nt; j += kReqNT) zl += E[j];
-    const double Z = block_sum<kReqNT>(zl, sc);
+    for (int j = tid; j < nt; j += kFinishNT) zl += E[j];
+    const double Z = block_sum<kFinishNT>(zl, sc);
     const double iz = 1.0 / Z;
 
     uint32_t rflags = undecided ? (kRowExact | kWhyAccept) : 0u;
@@ -1959,6 +2019,7 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
         if (tid == 0) a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags));
         start = n + 1;
+        from_pass = false;
         __syncthreads();
         continue;
       }
@@ -1969,13 +2030,13 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
     if (draft) {
       if (tid == 0) rs.nund = 0;
       __syncthreads();
-      for (int j = tid; j < nt; j += kReqNT) {
+      for (int j = tid; j < nt; j += kFinishNT) {
         if (W[j] < 0.0) ulist[atomicAdd(&rs.nund, 1)] = j;
         else W[j] = fmax(0.0, P[j] * iz - Q[j]);
       }
       __syncthreads();
       // tiles with undecided elements, one per wave, summed again with Z
-      for (int k = wave; k < rs.nund; k += kReqWaves) {
+      for (int k = wave; k < rs.nund; k += kFinishWaves) {
         const int j = ulist[k];
         const int base = j * kTile;
         double ws = 0.0;
@@ -1983,9 +2044,13 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
           float lv[8], qv[8];
           load_chunk<LT, VEC, true>(lrow, qrow, V, base, lane, c, lv, qv);
 #pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            ws += fmax(0.0, exp2_neg(fma(static_cast<double>(lv[kk]), s, nms), tab) * iz - static_cast<double>(qv[kk]));
-            if (kk & 1) __builtin_amdgcn_sched_barrier(0);
+          for (int g4 = 0; g4 < 8; g4 += kExpW) {
+            double ar[kExpW], e[kExpW];
+#pragma unroll
+            for (int kk = 0; kk < kExpW; ++kk) ar[kk] = fma(static_cast<double>(lv[g4 + kk]), s, nms);
+            exp2_negN<kExpW>(ar, tab, C, e);
+#pragma unroll
+            for (int kk = 0; kk < kExpW; ++kk) ws += fmax(0.0, e[kk] * iz - static_cast<double>(qv[g4 + kk]));
           }
         }
         ws = wave_sum_d(ws);
@@ -2057,14 +2122,17 @@ __global__ __launch_bounds__(kReqNT) void request_kernel(ProbsArgs a, SelectArgs
       float lv[8], qv[8];
       load8f<LT, VEC>(lrow, V, k0 + 8 * h, lv);
       load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qv);
-      double ar[8], e[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ar[k] = fma(static_cast<double>(lv[k]), s, nms);
-      exp2_negN<8>(ar, tab, C, e);
+      for (int g4 = 0; g4 < 8; g4 += kExpW) {
+        double ar[kExpW], e[kExpW];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const double p = e[k] * iz;
-        w8[k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[k])) : p;
+        for (int k = 0; k < kExpW; ++k) ar[k] = fma(static_cast<double>(lv[g4 + k]), s, nms);
+        exp2_negN<kExpW>(ar, tab, C, e);
+#pragma unroll
+        for (int k = 0; k < kExpW; ++k) {
+          const double p = e[k] * iz;
+          w8[g4 + k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[g4 + k])) : p;
+        }
       }
     };
     double ls = 0.0;
@@ -2293,15 +2361,22 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, 
   }
   prof_record(SV_PROFILE_ROWS, 1, st);
   if (lazy) {
-    // the per-request fp64 pass decides every request and writes the outputs
+    // the per-request fp64 pass (four blocks per request), then one block per
+    // request decides it and writes the outputs
     const size_t lds2 = static_cast<size_t>(nt) * (4 * sizeof(double) + sizeof(int));
+    const PassArrays pa{e.etile, e.ptile, e.qtile};
     prof_record(SV_PROFILE_REQUEST, 0, st);
-    if (vec)
-      hipLaunchKernelGGL((request_kernel<LT, true>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<true>()), lds2,
-                         st, a, sel);
-    else
-      hipLaunchKernelGGL((request_kernel<LT, false>), dim3(static_cast<unsigned>(a.B)), dim3(req_nt<false>()), lds2,
-                         st, a, sel);
+    if (vec) {
+      hipLaunchKernelGGL((request_pass_kernel<LT, true>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
+                         dim3(kPassNT), 0, st, a, pa);
+      hipLaunchKernelGGL((request_finish_kernel<LT, true>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
+                         st, a, sel, pa);
+    } else {
+      hipLaunchKernelGGL((request_pass_kernel<LT, false>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
+                         dim3(kPassNT), 0, st, a, pa);
+      hipLaunchKernelGGL((request_finish_kernel<LT, false>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
+                         st, a, sel, pa);
+    }
     prof_record(SV_PROFILE_REQUEST, 1, st);
     return 0;
   }
