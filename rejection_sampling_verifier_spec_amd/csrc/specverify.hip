@@ -2509,7 +2509,9 @@ int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity) {
     if (!(kernel_mask & (1u << id))) continue;
     g_prof.ev[id] = new hipEvent_t[2 * static_cast<size_t>(capacity)];
     for (int i = 0; i < 2 * capacity; ++i) {
-      if (hipEventCreate(&g_prof.ev[id][i]) != hipSuccess) {
+      // timing only: no system-scope fence (cache writeback and invalidate) at
+      // each record, which would otherwise slow the work around the events
+      if (hipEventCreateWithFlags(&g_prof.ev[id][i], hipEventDisableSystemFence) != hipSuccess) {
         for (int k = 0; k < i; ++k) hipEventDestroy(g_prof.ev[id][k]);
         delete[] g_prof.ev[id];
         g_prof.ev[id] = nullptr;

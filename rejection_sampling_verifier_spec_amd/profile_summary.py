@@ -5,8 +5,8 @@
   python -m rejection_sampling_verifier_spec_amd.profile_summary traffic OUT --fetch DIR --write DIR
           --copy-fetch DIR --copy-write DIR --copy-bytes N --command CMD [--command CMD ...]
       --pmc FETCH_SIZE / WRITE_SIZE runs of the benchmark and of the copy
-      calibration -> HBM bytes per launch of the per-row and per-request
-      kernels, with the source hash of the kernels they were taken on
+      calibration -> HBM bytes per launch of the per-row kernel and the two
+      per-request kernels, with the source hash of the kernels they were taken on
 """
 
 from __future__ import annotations
@@ -22,7 +22,8 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
 
-KERNELS = {"rows": "probs_rows_kernel", "request": "request_kernel", "copy": "copyBuffer"}
+KERNELS = {"rows": "probs_rows_kernel", "request_pass": "request_pass_kernel",
+           "request_finish": "request_finish_kernel", "copy": "copyBuffer"}
 
 
 def short(name: str) -> str:
@@ -78,7 +79,7 @@ def cmd_traffic(args) -> None:
              f"copy_write_counter_per_dispatch: {cw:.1f}",
              f"fetch_scale_bytes_per_unit: {sf:.4f}",
              f"write_scale_bytes_per_unit: {sw:.4f}"]
-    for k in ("rows", "request"):
+    for k in ("rows", "request_pass", "request_finish"):
         (fv, fn), (wv, wn) = f[k], w[k]
         if fv is None or wv is None:
             continue
