@@ -8,12 +8,14 @@ rejection select). Inputs are synthetic and seeded, already resident in HBM
 when the timed region starts.
 
 Prints one JSON line. `value` is verified draft positions per second
-(B * gamma per call). The roofline object prices the dominant kernel (the
-per-row pass) against HBM: its algorithmic bytes per launch are every target
-logit row once, plus per draft row the token, its q(x), the accept uniform and
-l(x), plus the row records and the statistics it hands to the per-request
-pass; its duration is the mean of HIP events the library records on the launch
-stream around that kernel over the timed region. The per-request stage (two
+(B * gamma per call). The roofline object prices the dominant stage (the
+per-row pass, two launches per call: positions 0-1, then the rest) against
+HBM: its algorithmic bytes per call are the logits of every row it reads (a
+row after a position already known to be a certain rejection is not read),
+plus per draft row read the token, its q(x), the accept uniform and l(x), plus
+the row records and the statistics it hands to the per-request pass; its
+duration is the mean of HIP events the library records on the launch stream
+around the two launches over the timed region. The per-request stage (two
 kernels) is timed the same way in a loop after the timed region and reported
 beside it (algorithmic bytes: the logit row and, for a replacement
 draw, the q row of each request's deciding row). `traffic` is the HBM traffic
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probs_rows_kernel_peaked_bf16_b256_g7_v128256_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lazy_rows_kernel_peaked_bf16_b256_g7_v128256_traffic.txt")
 
 
 def source_sha256() -> str:
@@ -48,8 +50,9 @@ def source_sha256() -> str:
 
 
 def measured_traffic():
-    """HBM bytes per launch of the per-row pass from the committed rocprofv3
-    summary, or None when it is missing or was taken on another source."""
+    """HBM bytes per call of the per-row pass (both launches) from the
+    committed rocprofv3 summary, or None when it is missing or was taken on
+    another source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -60,7 +63,7 @@ def measured_traffic():
     if vals.get("source_sha256") != source_sha256():
         return None
     try:
-        return float(vals["rows_kernel_hbm_bytes_per_launch"])
+        return float(vals["rows_kernel_hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=256 γ=7 V=128k"
@@ -178,14 +181,23 @@ def main():
     exact_rows = int(np.count_nonzero(flags & api.SV_ROW_EXACT))
     exact_why = {name: int(np.count_nonzero(flags & bit)) for bit, name in api.SV_ROW_WHY.items()}
     bonus_drawn = int(np.count_nonzero(rec[:, g, 0] >= 0))
-    # per-row pass: logits once; per draft row x (8 B), q(x) (4), u (4), l(x); records (8 per row)
-    # and the {m, Z, bound} statistics (32 B) of every row it leaves to the per-request pass
-    handed = int(np.count_nonzero((flags & api.SV_ROW_ACCEPTED) == 0)) if q is not None else 0
-    rows_bytes = rows * V * esz + positions * (8 + 4 + 4 + esz) + rows * 8 + handed * 32
+    nacc_h = nacc.cpu().numpy()
+    # rows the per-row pass read: all but those recorded as not read (after a known rejection);
+    # the method needs rows 0 .. n of each request (n accepted drafts, then the deciding row)
+    read = (flags & api.SV_ROW_UNREAD) == 0
+    rows_read = int(np.count_nonzero(read))
+    drafts_read = int(np.count_nonzero(read[:, :g]))
+    rows_needed = int(np.sum(nacc_h + 1))
+    # per-row pass: the logits of every row read; per draft row read x (8 B), q(x) (4), u (4),
+    # l(x); records (8 per row) and the {m, Z, bound} statistics (32 B) of every row read that
+    # it leaves to the per-request pass
+    handed = int(np.count_nonzero(read & ((flags & api.SV_ROW_ACCEPTED) == 0))) if q is not None else 0
+    rows_bytes = rows_read * V * esz + drafts_read * (8 + 4 + 4 + esz) + rows * 8 + handed * 32
     # per-request pass: the deciding row's logits and, for a replacement draw, its q row
     req_bytes = residual_rows * V * (esz + 4) + bonus_drawn * V * esz
     alg_bytes = rows_bytes + req_bytes
     full_bytes = rows * V * esz + (0 if q is None else positions * V * 4)
+    needed_bytes = rows_needed * V * esz + req_bytes - (residual_rows + bonus_drawn) * V * esz
     call_s = wall / args.steps
     rows_ms, rows_n = prof[api.SV_PROFILE_ROWS]
     req_ms, req_n = prof[api.SV_PROFILE_REQUEST]
@@ -211,18 +223,23 @@ def main():
                    "global_batch": B, "gamma": g, "vocab": V, "flags": args.flags},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": None if achieved is None else achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "probs_rows_kernel (per-row pass)", "bytes_per_launch": rows_bytes,
+                     "kernel": "lazy_rows_kernel (per-row pass, two launches per call)",
+                     "bytes_per_launch": rows_bytes,
                      "launch_ms_mean": rows_s * 1e3, "launches_timed": rows_n,
-                     "note": "HIP events recorded by the library on the launch stream around the kernel"},
+                     "note": "HIP events recorded by the library on the launch stream around the per-row "
+                             "pass (both launches); bytes: the rows it read"},
         "request_pass": {"kernel": "request_pass_kernel + request_finish_kernel (per-request fp64 stage)", "bytes_per_launch": req_bytes,
                          "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
                          "achieved_GBps": req_bytes / req_s / 1e9 if req_n else None},
         "whole_call": {"bytes": alg_bytes, "ms_mean": call_s * 1e3, "achieved_GBps": alg_bytes / call_s / 1e9,
                        "note": "wall clock over the timed steps (synchronize on both sides)"},
-        "rows": {"draft": positions, "accepted_own_test": accepted_rows, "residual_drawn": residual_rows,
-                 "bonus_drawn": bonus_drawn,
+        "rows": {"draft": positions, "target_rows": rows, "read_by_per_row_pass": rows_read,
+                 "needed_by_the_method": rows_needed, "accepted_own_test": accepted_rows,
+                 "residual_drawn": residual_rows, "bonus_drawn": bonus_drawn,
                  "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item())},
         "speculative_full_bytes_per_call": full_bytes,
+        "method_minimum_bytes_per_call": needed_bytes,
+        "method_minimum_GBps_equiv": needed_bytes / call_s / 1e9,
         "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
     }
     if args.cpu_requests > 0 and q is not None:

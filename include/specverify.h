@@ -71,9 +71,12 @@ enum sv_status {
 
 /* flags for spec_verify_probs / spec_verify_ragged. The three ways of drawing
  * replacements give identical results; they differ in the bytes they read:
- *  default (lazy): pass 1 over the logits of every row decides every accept
- *    test; the residual max(0, p - q) is then drawn only at each request's
- *    first rejection (the logits and q of that one row are read again).
+ *  default (lazy): pass 1 over the logits decides the accept tests, positions
+ *    in order across the batch; a row after a position already known to be
+ *    a certain rejection is not read (rows whose earlier positions are still
+ *    undecided are read speculatively); the residual max(0, p - q) is then
+ *    drawn only at each request's first rejection (the logits and q of that
+ *    one row are read again).
  *  SV_FLAG_EAGER: every draft row whose own accept test fails draws its
  *    replacement in the same launch (speculatively; most are unused).
  *  SV_FLAG_ALL_RESIDUALS: every draft row draws its replacement. */
@@ -103,11 +106,13 @@ enum sv_status {
 #define SV_ROW_DEFERRED 0x400u     /* lazy mode: rejected (or bonus) row whose token was not needed (not drawn) */
 #define SV_ROW_UNDECIDED 0x800u    /* lazy mode: accept test left to the per-request fp64 pass, which did not
                                       need this row (an earlier row was rejected) */
+#define SV_ROW_UNREAD 0x1000u      /* lazy mode: row after a position already known to be a certain
+                                      rejection: not needed, its logits were not read */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of
- * `vocab_size` tokens: 92 bytes per row for the records, list, counters and
- * lazy-mode statistics, plus 28 * ceil(vocab_size / 2048) bytes
+ * `vocab_size` tokens: 96 bytes per row for the records, list, counters and
+ * lazy-mode statistics and marks, plus 28 * ceil(vocab_size / 2048) bytes
  * per row for fp64 tile sums, each part rounded up to 256 bytes. The greedy
  * entry point needs only the records (8 bytes per row, rounded up to 256).
  * Returns 0 for a negative row count or a vocab_size outside [1, SV_MAX_VOCAB]. */

@@ -28,6 +28,7 @@ SV_ROW_RESIDUAL = 0x4
 SV_ROW_FALLBACK = 0x8
 SV_ROW_DEFERRED = 0x400
 SV_ROW_UNDECIDED = 0x800
+SV_ROW_UNREAD = 0x1000
 SV_ROW_WHY = {0x10: "accept", 0x20: "fallback", 0x40: "search", 0x80: "margin", 0x100: "forced"}
 SV_PROFILE_ROWS = 0
 SV_PROFILE_REQUEST = 1

@@ -196,6 +196,11 @@ struct RawTile;
 template <>
 struct RawTile<uint16_t, true> {
   uint4 d[4];
+  // a tile wholly inside the row: no clamping
+  __device__ __forceinline__ void load_full(const uint16_t* __restrict__ row, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = *reinterpret_cast<const uint4*>(row + base + (r * 64 + lane) * 8);
+  }
   __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int V, int base, int lane) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -236,6 +241,10 @@ struct RawTile<uint16_t, true> {
 template <>
 struct RawTile<float, true> {
   float4 d[8];
+  __device__ __forceinline__ void load_full(const float* __restrict__ row, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) d[r] = *reinterpret_cast<const float4*>(row + base + (r * 64 + lane) * 4);
+  }
   __device__ __forceinline__ void load(const float* __restrict__ row, int V, int base, int lane) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -266,6 +275,10 @@ struct RawTile<float, true> {
 template <typename LT>
 struct RawTile<LT, false> {
   float d[kLaneElems];
+  __device__ __forceinline__ void load_full(const LT* __restrict__ row, int base, int lane) {
+#pragma unroll
+    for (int r = 0; r < kLaneElems; ++r) d[r] = to_float(row[base + r * 64 + lane]);
+  }
   __device__ __forceinline__ void load(const LT* __restrict__ row, int V, int base, int lane) {
 #pragma unroll
     for (int r = 0; r < kLaneElems; ++r) d[r] = to_float(row[min(base + r * 64 + lane, V - 1)]);
@@ -423,6 +436,44 @@ struct Task {
 };
 
 __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__ cu, int B, int gamma,
+                                            int ndraft);
+
+// Lazy mode, one launch over positions [p0, p1): blocks 0 .. B (p1 - p0) - 1
+// take position p0 + blk / B of request b = blk % B (all first drafts, then
+// all second drafts, ...); with `flat` (ragged batches, last launch) the rest
+// take the rows at positions >= pm in the flat order.
+__device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restrict__ cu, int B, int gamma,
+                                                 int ndraft, int p0, int p1, int pm, bool flat) {
+  Task t;
+  if (blk >= B * (p1 - p0)) {
+    t = decode_task(blk - B * (p1 - p0), cu, B, gamma, ndraft);
+    if (!flat || t.i < pm) t.valid = false;  // launched position-major
+    return t;
+  }
+  t.valid = true;
+  t.b = blk % B;
+  t.i = p0 + blk / B;
+  int d0, d1;
+  if (cu) {
+    d0 = cu[t.b];
+    d1 = cu[t.b + 1];
+    if (d0 < 0 || d1 < d0 || d1 > ndraft) {
+      t.valid = false;
+      d0 = d1 = 0;
+    }
+  } else {
+    d0 = t.b * gamma;
+    d1 = d0 + gamma;
+  }
+  t.g = d1 - d0;
+  if (t.i > t.g) t.valid = false;
+  t.drow = t.i < t.g ? static_cast<int64_t>(d0) + t.i : -1;
+  t.trow = static_cast<int64_t>(d0) + t.i + t.b;
+  t.srow = static_cast<int64_t>(d1) + t.b;
+  return t;
+}
+
+__device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__ cu, int B, int gamma,
                                             int ndraft) {
   Task t;
   t.valid = true;
@@ -494,9 +545,12 @@ struct ProbsArgs {
   int* xcount;    // list of rows for the fp64 path (see ExactArgs)
   ExactEntry* xlist;
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
+  int* mark;      // lazy mode, per request: kMarkBase - (first position known to be a certain rejection), or 0
+  int pm;         // lazy mode: positions 0 .. pm - 1 are launched position-major
 };
 
 struct RowShared {
+  int skip;        // lazy mode: an earlier position of the request is a certain rejection
   float wmax[16];  // per-wave maxima (blocks of up to 1024 threads)
   float m;
   double z;        // Z (e-units)
@@ -608,8 +662,10 @@ __global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
 
 constexpr uint32_t kRowNeedExact = kRowNeedExactBit;  // set by the fast kernels, cleared by the fp64 finish
 constexpr uint32_t kRowDeferred = SV_ROW_DEFERRED;
+constexpr uint32_t kRowUnread = SV_ROW_UNREAD;
 constexpr uint32_t kRowUndecided = SV_ROW_UNDECIDED;
 constexpr uint32_t kFlagLazy = 0x80000000u;  // internal: set by the host for the lazy mode
+constexpr int kMarkBase = 1 << 30;              // lazy mode: per-request mark = kMarkBase - position
 constexpr int kExactPer = kTile / kNT;      // elements per thread of one tile (8)
 constexpr double kZSlack = 1e-12;           // widening of the Z interval for fp64 rounding
 constexpr int kItemTiles = 4;               // tiles per item of the fp64 kernel
@@ -1255,11 +1311,9 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
 // all-residual modes); otherwise (lazy mode) they are deferred, and the kernel
 // has no q pass at all.
 template <typename LT, bool VEC, int NT, bool EAGER>
-__global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
+__device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
+                                          RowShared& sh) {
   constexpr int kWaves = NT / 64;
-  extern __shared__ float dyn[];
-  __shared__ BlockScratchT<NT> sc;
-  __shared__ RowShared sh;
   using L = Lay<LT, VEC>;
   using Raw = RawTile<LT, VEC>;
 
@@ -1271,8 +1325,6 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   float* EA = dyn + 3 * nt; // tile sums of e |a| (a = the exp argument), for the error bound
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const Task t = decode_task(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft);
-  if (!t.valid) return;  // request with invalid offsets: the select kernel skips it
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(V);
   const bool is_draft = t.drow >= 0;
   const float* __restrict__ qrow = (is_draft && a.q) ? a.q + t.drow * static_cast<int64_t>(V) : nullptr;
@@ -1451,6 +1503,7 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
     // the certified Z interval in fp64 units (or {0, inf} when there is none)
     if (tid == 0) {
       const uint32_t f = sh.uncertain ? kRowUndecided : ((is_draft && accepted) ? kRowAccepted : kRowDeferred);
+      if (is_draft && f == kRowDeferred) atomicMax(a.mark + t.b, kMarkBase - t.i);  // a certain rejection
       if (f != kRowAccepted) {
         double z = 0.0, dz = INFINITY;
         if (Z > 0.0 && Z < INFINITY && dZ < Z && m != -INFINITY) {
@@ -1475,6 +1528,44 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
   }
 
   sample_row<LT, VEC, NT, EAGER>(a, t, lrow, qrow, xmask, accepted, m, Z, bt, relZ, sh.px, S, M, W, sc, sh);
+}
+
+// Eager modes: one block per row (draft rows first, then bonus rows).
+template <typename LT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
+  extern __shared__ float dyn[];
+  __shared__ BlockScratchT<NT> sc;
+  __shared__ RowShared sh;
+  const Task t = decode_task(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft);
+  if (!t.valid) return;  // request with invalid offsets: the select kernel skips it
+  probs_row<LT, VEC, NT, true>(a, t, dyn, sc, sh);
+}
+
+// Lazy mode: one block per row of positions [p0, p1) (see decode_task_lazy).
+// Algorithm 1 stops at the first rejection ([READING] and [VISUAL],
+// Algorithm 1): a row after a position already known to be a certain
+// rejection is not needed and is not read (it is recorded as unread). The
+// host launches positions 0 and 1 first; the second launch then sees every
+// mark those rows set and reads only the rows of requests that survived
+// them (rows whose earlier positions are still undecided are read
+// speculatively).
+template <typename LT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
+  extern __shared__ float dyn[];
+  __shared__ BlockScratchT<NT> sc;
+  __shared__ RowShared sh;
+  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, p0, p1, a.pm, flat != 0);
+  if (!t.valid) return;
+  if (t.i > 0) {
+    if (threadIdx.x == 0)
+      sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
+    __syncthreads();
+    if (sh.skip) {
+      if (threadIdx.x == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowUnread));
+      return;
+    }
+  }
+  probs_row<LT, VEC, NT, false>(a, t, dyn, sc, sh);
 }
 
 // ----------------------------------------------------------------------------
@@ -1908,7 +1999,7 @@ __device__ __forceinline__ bool request_range(const ProbsArgs& a, int b, int& d0
 
 constexpr int kPassNT = 256;       // threads per block of the pass kernel
 constexpr int kPassWaves = kPassNT / 64;
-constexpr int kPassSlices = 3;     // blocks per request in the pass kernel (768: one round at 3 blocks per CU)
+constexpr int kPassSlices = 3;     // blocks per request in the pass kernel
 constexpr int kFinishNT = 256;     // threads per block of the finish kernel
 constexpr int kFinishWaves = kFinishNT / 64;
 
@@ -1918,6 +2009,8 @@ struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the 
   double* Q;
 };
 
+// Lazy mode, per-request pass: kPassSlices blocks per request, each over a
+// slice of the deciding row's tiles.
 // Lazy mode, per-request pass: kPassSlices blocks per request, each over a
 // slice of the deciding row's tiles.
 template <typename LT, bool VEC>
@@ -1967,6 +2060,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
   int* ulist = reinterpret_cast<int*>(rbuf + 4 * nt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
+  if (tid == 0) a.mark[b] = 0;  // the per-row kernel has finished: ready for the next call
   int d0, d1;
   if (!request_range(a, b, d0, d1)) {
     if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
@@ -2296,7 +2390,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 // arrays, then the lazy mode's per-row statistics. Every part starts on a
 // 256-byte boundary.
 struct WsLayout {
-  size_t rec, count, list, done, etile, ptile, qtile, amb, rstat, total;
+  size_t rec, count, list, done, etile, ptile, qtile, amb, rstat, mark, total;
 };
 WsLayout ws_layout(int64_t rows, int V) {
   WsLayout l;
@@ -2311,7 +2405,8 @@ WsLayout ws_layout(int64_t rows, int V) {
   l.qtile = l.ptile + align256(r * nt * sizeof(double));
   l.amb = l.qtile + align256(r * nt * sizeof(double));
   l.rstat = l.amb + align256(r * nt * sizeof(int));
-  l.total = l.rstat + align256(r * 4 * sizeof(double));
+  l.mark = l.rstat + align256(r * 4 * sizeof(double));
+  l.total = l.mark + align256(r * sizeof(int));
   return l;
 }
 size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
@@ -2319,13 +2414,25 @@ size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * size
 // Block sizes: the lazy first pass reads logits only and keeps more rows in
 // flight with small blocks; the eager modes and the per-request second pass
 // stream logits and q per row and prefer larger blocks (shorter per-row time).
-constexpr int kRowsNTLazy = 256;
+constexpr int kRowsNTLazy = 512;
+constexpr int kRaggedPositionMajor = 4;  // ragged batches: positions launched position-major
+constexpr int kLazyFirstPositions = 2;   // lazy mode: positions of the first launch
 constexpr int kRowsNTEager = 512;
 
 template <typename LT, bool VEC, int NT, bool EAGER>
 void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT, EAGER>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st,
-                     a);
+  if constexpr (EAGER) {
+    hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st, a);
+  } else {
+    // positions [0, 2), then the rest (with the flat order for ragged batches)
+    const int split = min(kLazyFirstPositions, a.pm);
+    hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT), lds, st,
+                       a, 0, split, 0);
+    const int64_t rest = static_cast<int64_t>(a.B) * (a.pm - split) + (a.cu ? rows : 0);
+    if (rest > 0)
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st, a,
+                         split, a.pm, 1);
+  }
 }
 
 // Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
@@ -2410,7 +2517,8 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     return SV_ERR_INVALID_ARGUMENT;
   if (stats && !(T > 0.0)) return SV_ERR_INVALID_ARGUMENT;
   const int64_t rows = static_cast<int64_t>(ndraft) + B;
-  if (rows > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+  // (the lazy grid of a ragged batch adds kRaggedPositionMajor blocks per request)
+  if (rows + static_cast<int64_t>(kRaggedPositionMajor) * B > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
   if (B == 0) return SV_OK;
   if (!logits || !out || !nacc) return SV_ERR_INVALID_ARGUMENT;
   if (ndraft > 0 && !x) return SV_ERR_INVALID_ARGUMENT;
@@ -2451,6 +2559,9 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
         !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EXACT)) && stats == nullptr && q != nullptr;
     p.flags = flags | (lazy ? kFlagLazy : 0u);
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
+    p.mark = reinterpret_cast<int*>(wsb + wl.mark);
+
+    p.pm = cu ? kRaggedPositionMajor : gamma + 1;
     p.xcount = xcount;
     p.xlist = reinterpret_cast<ExactEntry*>(wsb + wl.list);
     ExactArgs e;

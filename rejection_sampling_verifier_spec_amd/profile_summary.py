@@ -22,8 +22,10 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
 
-KERNELS = {"rows": "probs_rows_kernel", "request_pass": "request_pass_kernel",
+KERNELS = {"rows": "lazy_rows_kernel", "request_pass": "request_pass_kernel",
            "request_finish": "request_finish_kernel", "copy": "copyBuffer"}
+# launches per call of the verifier's default mode (the per-row pass runs as two launches)
+PER_CALL = {"rows": 2, "request_pass": 1, "request_finish": 1}
 
 
 def short(name: str) -> str:
@@ -86,7 +88,9 @@ def cmd_traffic(args) -> None:
         lines += [f"{k}_kernel_dispatches: {fn}",
                   f"{k}_kernel_fetch_counter_per_dispatch: {fv:.1f}",
                   f"{k}_kernel_write_counter_per_dispatch: {wv:.1f}",
-                  f"{k}_kernel_hbm_bytes_per_launch: {fv * sf + wv * sw:.0f}"]
+                  f"{k}_kernel_hbm_bytes_per_launch: {fv * sf + wv * sw:.0f}",
+                  f"{k}_kernel_launches_per_call: {PER_CALL[k]}",
+                  f"{k}_kernel_hbm_bytes_per_call: {(fv * sf + wv * sw) * PER_CALL[k]:.0f}"]
     open(args.out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
