@@ -443,7 +443,8 @@ __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__
 // all second drafts, ...); with `flat` (ragged batches, last launch) the rest
 // take the rows at positions >= pm in the flat order.
 __device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restrict__ cu, int B, int gamma,
-                                                 int ndraft, int p0, int p1, int pm, bool flat) {
+                                                 int ndraft, int p0, int p1, int pm, bool flat,
+                                                 const int* __restrict__ surv, int nsurv) {
   Task t;
   if (blk >= B * (p1 - p0)) {
     t = decode_task(blk - B * (p1 - p0), cu, B, gamma, ndraft);
@@ -451,8 +452,18 @@ __device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restr
     return t;
   }
   t.valid = true;
-  t.b = blk % B;
-  t.i = p0 + blk / B;
+  if (surv) {  // second launch: the listed requests' positions, request by request
+    const int k = blk / (p1 - p0);
+    if (k >= nsurv) {
+      t.valid = false;
+      return t;
+    }
+    t.b = surv[k];
+    t.i = p0 + blk % (p1 - p0);
+  } else {
+    t.b = blk % B;
+    t.i = p0 + blk / B;
+  }
   int d0, d1;
   if (cu) {
     d0 = cu[t.b];
@@ -547,10 +558,15 @@ struct ProbsArgs {
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
   int* mark;      // lazy mode, per request: kMarkBase - (first position known to be a certain rejection), or 0
   int pm;         // lazy mode: positions 0 .. pm - 1 are launched position-major
+  int* surv;      // lazy mode: requests still undecided after the first launch (count at surv_n)
+  int* surv_n;    // lazy mode: [0] the count, [16] the first launch's finished-block counter
 };
 
 struct RowShared {
   int skip;        // lazy mode: an earlier position of the request is a certain rejection
+  int last;        // lazy mode: this block is the last of the first launch to finish
+  int mark_old;    // lazy mode: the mark before this row's rejection raised it
+  int wcount[16];  // lazy mode: per-wave counts of the survivor list
   float wmax[16];  // per-wave maxima (blocks of up to 1024 threads)
   float m;
   double z;        // Z (e-units)
@@ -1503,7 +1519,11 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
     // the certified Z interval in fp64 units (or {0, inf} when there is none)
     if (tid == 0) {
       const uint32_t f = sh.uncertain ? kRowUndecided : ((is_draft && accepted) ? kRowAccepted : kRowDeferred);
-      if (is_draft && f == kRowDeferred) atomicMax(a.mark + t.b, kMarkBase - t.i);  // a certain rejection
+      // a certain rejection raises the request's mark; the atomic returns (and the
+      // value is stored) before this thread goes on, so the mark is in place
+      // before anything this thread does later (the first launch's count)
+      if (is_draft && f == kRowDeferred)
+        sh.mark_old = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (f != kRowAccepted) {
         double z = 0.0, dz = INFINITY;
         if (Z > 0.0 && Z < INFINITY && dZ < Z && m != -INFINITY) {
@@ -1549,23 +1569,78 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
 // mark those rows set and reads only the rows of requests that survived
 // them (rows whose earlier positions are still undecided are read
 // speculatively).
+// The requests still undecided after positions [0, p1) (no certain rejection
+// there) with a position >= p1, in request order: written by the last block
+// of the first launch to finish, for the second launch. The rows at
+// positions [p1, pm) of every other request are recorded as unread.
+template <int NT>
+__device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kW = NT / 64;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += NT) {
+    const int b = b0 + static_cast<int>(threadIdx.x);
+    bool keep = false;
+    if (b < a.B) {
+      int d0, d1;
+      if (a.cu) {
+        d0 = a.cu[b];
+        d1 = a.cu[b + 1];
+      } else {
+        d0 = b * a.gamma;
+        d1 = d0 + a.gamma;
+      }
+      const bool ok = !a.cu || (d0 >= 0 && d1 >= d0 && d1 <= a.ndraft);
+      keep = ok && d1 - d0 >= p1 &&
+             __hip_atomic_load(a.mark + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= kMarkBase - p1;
+      if (ok && !keep)
+        for (int i = p1; i <= min(d1 - d0, a.pm - 1); ++i)
+          a.ws[static_cast<int64_t>(d0) + b + i] = make_int2(-1, static_cast<int>(kRowUnread));
+    }
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) sh.wcount[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += sh.wcount[w];
+    if (keep) a.surv[off + __popcll(m & ((1ull << lane) - 1))] = b;
+    for (int w = 0; w < kW; ++w) base += sh.wcount[w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.surv_n[0] = base;
+}
+
 template <typename LT, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
-  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, p0, p1, a.pm, flat != 0);
-  if (!t.valid) return;
-  if (t.i > 0) {
+  const bool second = p0 > 0;
+  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, p0, p1, a.pm, flat != 0,
+                                  second ? a.surv : nullptr, second ? a.surv_n[0] : 0);
+  bool read = t.valid;
+  if (t.valid && t.i > 0) {
     if (threadIdx.x == 0)
       sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
     __syncthreads();
     if (sh.skip) {
       if (threadIdx.x == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowUnread));
-      return;
+      read = false;
     }
   }
-  probs_row<LT, VEC, NT, false>(a, t, dyn, sc, sh);
+  if (read) probs_row<LT, VEC, NT, false>(a, t, dyn, sc, sh);
+  if (second || a.pm <= p1) return;
+  // first launch: the last block to finish lists the requests the second launch
+  // reads. Marks and the count are device-scope atomics, each block's mark
+  // completed before its count (see probs_row), and the list reads the marks
+  // with atomic loads: no cache-wide fence is needed.
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sh.last = __hip_atomic_fetch_add(a.surv_n + 16, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!sh.last) return;
+  list_survivors<NT>(a, p1, sh);
+  if (threadIdx.x == 0) a.surv_n[16] = 0;  // ready for the next call
 }
 
 // ----------------------------------------------------------------------------
@@ -2390,14 +2465,14 @@ inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 // arrays, then the lazy mode's per-row statistics. Every part starts on a
 // 256-byte boundary.
 struct WsLayout {
-  size_t rec, count, list, done, etile, ptile, qtile, amb, rstat, mark, total;
+  size_t rec, count, list, done, etile, ptile, qtile, amb, rstat, mark, surv, total;
 };
 WsLayout ws_layout(int64_t rows, int V) {
   WsLayout l;
   const size_t nt = static_cast<size_t>((V + kTile - 1) / kTile);
   const size_t r = static_cast<size_t>(rows);
   l.rec = 0;
-  l.count = align256(r * sizeof(int2));  // list count at +0, finished rows at +64
+  l.count = align256(r * sizeof(int2));  // list count at +0, finished rows at +64, survivors at +128
   l.list = l.count + 256;
   l.done = l.list + align256(r * sizeof(ExactEntry));
   l.etile = l.done + align256(r * sizeof(int));
@@ -2406,7 +2481,8 @@ WsLayout ws_layout(int64_t rows, int V) {
   l.amb = l.qtile + align256(r * nt * sizeof(double));
   l.rstat = l.amb + align256(r * nt * sizeof(int));
   l.mark = l.rstat + align256(r * 4 * sizeof(double));
-  l.total = l.mark + align256(r * sizeof(int));
+  l.surv = l.mark + align256(r * sizeof(int));
+  l.total = l.surv + align256(r * sizeof(int));
   return l;
 }
 size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
@@ -2560,6 +2636,8 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.flags = flags | (lazy ? kFlagLazy : 0u);
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.mark = reinterpret_cast<int*>(wsb + wl.mark);
+    p.surv = reinterpret_cast<int*>(wsb + wl.surv);
+    p.surv_n = reinterpret_cast<int*>(wsb + wl.count + 128);
 
     p.pm = cu ? kRaggedPositionMajor : gamma + 1;
     p.xcount = xcount;

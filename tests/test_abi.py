@@ -54,9 +54,9 @@ def test_workspace_size(lib):
     # records + counters + 48-byte list entries + per-row tile counters + three fp64 and one int
     # per-tile arrays (nt = ceil(V / 2048)) + per-row {m, Z, bound, shift} + per-request marks;
     # each part 256-aligned
-    assert api.workspace_size(1, 100) == 256 * 10
+    assert api.workspace_size(1, 100) == 256 * 11
     assert api.workspace_size(2048, 128256) == (2048 * 8 + 256 + 2048 * 48 + 2048 * 4
-                                                + 3 * 2048 * 63 * 8 + 2048 * 63 * 4 + 2048 * 32 + 2048 * 4)
+                                                + 3 * 2048 * 63 * 8 + 2048 * 63 * 4 + 2048 * 32 + 2 * 2048 * 4)
     assert lib.spec_verify_workspace_size(-1, 100) == 0
     assert lib.spec_verify_workspace_size(5, 0) == 0
     assert lib.spec_verify_workspace_size(5, (1 << 21) + 1) == 0
@@ -91,7 +91,7 @@ def probs(lib, **kw):
     (dict(stats=FAKE, T=0.0), -1),
     (dict(ws=None), -4),
     (dict(wsb=8 * 7), -4),
-    (dict(wsb=2815), -4),  # 8 rows, V=100 need 2816 bytes
+    (dict(wsb=3071), -4),  # 8 rows, V=100 need 3072 bytes
     (dict(ws=ctypes.c_void_p(0x1080)), -4),
     (dict(B=0), 0),
 ])
