@@ -109,6 +109,32 @@ def cpu_baseline(w, max_requests: int):
                        f"{len(jobs)} worker processes, {dt:.2f} s wall"), flat
 
 
+def measure_loop(steps: int, dev):
+    """The synthetic end-to-end loop (bigram target and draft tables, iid
+    acceptance) at B=256, gamma=7, V=32000, T=0.7: tokens per target call
+    against Eq. (1), and the wall time per step (drafting included)."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verifier_spec_amd import loop
+
+    B, g, V, T = 256, 7, 32000, 0.7
+    pair = loop.make_bigram_pair(V, seed=11, kind="iid", dtype="bf16", temperature=T, device=dev)
+    loop.run(pair, B, g, 3, seed=10)  # warm-up
+    st = loop.run(pair, B, g, steps, seed=11)
+    p = np.exp((pair.base_target.astype(np.float64) - pair.base_target.max()) / T)
+    p /= p.sum()
+    qd = torch.softmax(torch.from_numpy(pair.base_draft).to(dev) / T, dim=-1).cpu().numpy().astype(np.float64)
+    beta = float(np.minimum(p, qd).sum())
+    mean, var = loop.eq1_tokens_per_step(beta, g)
+    return {"workload": f"bigram loop: B={B} gamma={g} V={V} T={T} bf16 target, iid tables",
+            "steps": st.steps, "tokens_per_step": st.tokens_per_step, "eq1_tokens_per_step": mean,
+            "eq1_std_error": float(np.sqrt(var / st.request_steps)), "beta": beta,
+            "ms_per_step": st.seconds / st.steps * 1e3, "tokens_per_s": st.tokens / st.seconds,
+            "note": "drafting (7 fp32 softmax + inverse-CDF draws), gathers and bookkeeping in torch; "
+                    "the verifier through the C ABI"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +144,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="SV_FLAG_* bits passed to the library (0: lazy residuals, 4: eager, 2: all residuals)")
     ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
+    ap.add_argument("--loop-steps", type=int, default=30,
+                    help="steps of the synthetic end-to-end loop measured after the timed region (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -242,6 +270,8 @@ def main():
         "method_minimum_GBps_equiv": needed_bytes / call_s / 1e9,
         "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
     }
+    if args.loop_steps > 0:
+        result["loop"] = measure_loop(args.loop_steps, dev)
     if args.cpu_requests > 0 and q is not None:
         base, ref = cpu_baseline(w, args.cpu_requests)
         o = out.cpu().numpy()

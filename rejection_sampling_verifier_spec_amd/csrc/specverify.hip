@@ -2283,14 +2283,19 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
         if (j < jt) pl += tile_val(j);
       pb = wave_sum_d(pl);
     }
-    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31);
-    // the weights are computed twice (lane sums, then the crossing lane's
-    // prefix) rather than held in registers
+    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31),
+    // loaded once (all loads in flight together); the weights are computed
+    // twice from registers (lane sums, then the crossing lane's prefix)
     const int k0 = jt * kTile + 32 * lane;
-    auto weights8 = [&](int h, double (&w8)[8]) {
-      float lv[8], qv[8];
-      load8f<LT, VEC>(lrow, V, k0 + 8 * h, lv);
-      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qv);
+    float lall[4][8], qall[4][8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      load8f<LT, VEC>(lrow, V, k0 + 8 * h, lall[h]);
+      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qall[h]);
+    }
+    auto weights8 = [&](int h, double (&w8)[8]) __attribute__((always_inline)) {
+      const float (&lv)[8] = lall[h];
+      const float (&qv)[8] = qall[h];
 #pragma unroll
       for (int g4 = 0; g4 < 8; g4 += kExpW) {
         double ar[kExpW], e[kExpW];

@@ -1,0 +1,163 @@
+"""The synthetic end-to-end loop (bigram target and draft tables).
+
+CPU tests run the loop with the oracle as the verifier, which pins the loop's
+own bookkeeping; GPU tests run it through the C ABI. Two checks, fixed before
+any run:
+
+* with the "iid" tables every draft is accepted with the same probability
+  beta = sum_x min(p(x), q(x)), so the mean number of tokens per step must
+  match (1 - beta^(gamma+1)) / (1 - beta) ([VISUAL], Eq. (1)) within 5
+  standard errors;
+* the emitted tokens must follow the target ([VISUAL], paper App. A.1): given
+  the previous token, the next one is a draw from the target row's softmax;
+  a chi-square test over all contexts (cells with expected count below 5
+  pooled per context) must not reject at p = 1e-4.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+from rejection_sampling_verifier_spec_amd import loop
+
+
+def oracle_verifier(logits, q, x, u, T):
+    """The oracle as a drop-in verifier for the loop (CPU tensors)."""
+    L = logits.float().numpy().astype(np.float64)
+    Q = q.numpy()
+    X = x.numpy()
+    U = u.numpy()
+    B, rows, _ = L.shape
+    g = rows - 1
+    out = np.full((B, rows), -1, dtype=np.int64)
+    nacc = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        p_rows = [oracle.target_probs(L[b, i], T) for i in range(rows)]
+        toks, n = oracle.verify_request(p_rows, [Q[b, i] for i in range(g)], X[b], U[b])
+        out[b, : n + 1] = toks
+        nacc[b] = n
+    return torch.from_numpy(out), torch.from_numpy(nacc)
+
+
+def beta_of(pair: loop.BigramPair, device) -> float:
+    """sum_x min(p(x), q(x)) of the iid tables' base rows, with q exactly as the
+    loop computes it (fp32 softmax) and p from the oracle."""
+    p = oracle.target_probs(pair.base_target.astype(np.float64), pair.temperature)
+    d = torch.from_numpy(pair.base_draft).to(device)
+    q = torch.softmax(d / pair.temperature, dim=-1).cpu().numpy().astype(np.float64)
+    return float(np.sum(np.minimum(p, q)))
+
+
+def target_table_probs(pair: loop.BigramPair) -> np.ndarray:
+    """Next-token distribution of every context (tables with one row per context)."""
+    t = pair.target.float().cpu().numpy().astype(np.float64)
+    assert t.shape[0] == t.shape[1]
+    return np.stack([oracle.target_probs(t[c], pair.temperature) for c in range(t.shape[0])])
+
+
+def chi_square_pvalue(counts: np.ndarray, probs: np.ndarray) -> float:
+    """Pearson chi-square of observed (prev, next) counts against the target
+    rows, summed over the contexts; per context, cells with expected count
+    below 5 are pooled into one cell."""
+    chi2, dof = 0.0, 0
+    for c in range(counts.shape[0]):
+        n = counts[c].sum()
+        if n == 0:
+            continue
+        e = n * probs[c]
+        small = e < 5.0
+        obs = list(counts[c][~small])
+        exp = list(e[~small])
+        if small.any():
+            obs.append(counts[c][small].sum())
+            exp.append(e[small].sum())
+        obs, exp = np.array(obs, dtype=np.float64), np.array(exp)
+        chi2 += float(np.sum((obs - exp) ** 2 / exp))
+        dof += len(obs) - 1
+    return float(stats.chi2.sf(chi2, dof))
+
+
+def check_eq1(st: loop.LoopStats, beta: float, gamma: int):
+    mean, var = loop.eq1_tokens_per_step(beta, gamma)
+    se = np.sqrt(var / st.request_steps)
+    assert abs(st.tokens_per_step - mean) <= 5 * se, (st.tokens_per_step, mean, se, beta)
+
+
+# ------------------------------------------------------------ CPU: formula and loop logic
+
+
+def test_eq1_matches_the_printed_closed_form_and_simulation():
+    rng = np.random.default_rng(3)
+    for beta in (0.0, 0.3, 0.62, 0.9, 0.999):
+        for gamma in (1, 4, 7):
+            mean, var = loop.eq1_tokens_per_step(beta, gamma)
+            closed = (gamma + 1.0) if beta == 1.0 else (1.0 - beta ** (gamma + 1)) / (1.0 - beta)
+            assert mean == pytest.approx(closed, rel=1e-12)
+            # simulated: accept each draft with probability beta, stop at the first rejection
+            acc = rng.random((200000, gamma)) < beta
+            n = np.where(acc.all(1), gamma, np.argmin(acc, 1))
+            assert np.mean(n + 1) == pytest.approx(mean, abs=5 * np.sqrt(var / len(n)) + 1e-12)
+            assert np.var(n + 1) == pytest.approx(var, rel=0.05, abs=1e-3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_loop_with_the_oracle_verifier(dtype):
+    dev = torch.device("cpu")
+    pair = loop.make_bigram_pair(16, seed=1, kind="iid", dtype=dtype, temperature=1.0, device=dev)
+    gamma = 4
+    st = loop.run(pair, B=32, gamma=gamma, steps=120, seed=1, verify=oracle_verifier, keep_pairs=True, device=dev)
+    assert st.tokens == int(np.sum(st.accepted_hist * np.arange(1, gamma + 2)))
+    assert st.pair_counts.sum() == st.tokens
+    check_eq1(st, beta_of(pair, dev), gamma)
+    assert chi_square_pvalue(st.pair_counts, target_table_probs(pair)) > 1e-4
+
+
+def test_iid_tables_give_the_same_beta_in_every_context():
+    dev = torch.device("cpu")
+    pair = loop.make_bigram_pair(32, seed=2, kind="iid", dtype="bf16", temperature=0.8, device=dev)
+    t = pair.target.float().numpy().astype(np.float64)
+    q = torch.softmax(pair.draft / pair.temperature, dim=-1).numpy().astype(np.float64)
+    assert t.shape == (32, 32)
+    betas = [np.sum(np.minimum(oracle.target_probs(t[c], pair.temperature), q[c])) for c in range(32)]
+    assert np.ptp(betas) < 1e-6
+    assert betas[0] == pytest.approx(beta_of(pair, dev), abs=1e-6)
+
+
+# ------------------------------------------------------------ GPU: the library in the loop
+
+
+@pytest.mark.gpu
+def test_loop_distribution_and_eq1_on_gpu():
+    dev = torch.device("cuda:0")
+    pair = loop.make_bigram_pair(16, seed=3, kind="iid", dtype="bf16", temperature=1.0, device=dev)
+    gamma = 4
+    st = loop.run(pair, B=256, gamma=gamma, steps=300, seed=3, keep_pairs=True)
+    print(f"V=16 iid: {st.tokens_per_step:.4f} tokens/step over {st.request_steps} request-steps")
+    check_eq1(st, beta_of(pair, dev), gamma)
+    assert chi_square_pvalue(st.pair_counts, target_table_probs(pair)) > 1e-4
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("V,gamma,T", [(4096, 7, 1.0), (32000, 5, 0.7)])
+def test_loop_eq1_on_gpu_large_vocab(V, gamma, T):
+    dev = torch.device("cuda:0")
+    pair = loop.make_bigram_pair(V, seed=4, kind="iid", dtype="bf16", temperature=T, device=dev)
+    st = loop.run(pair, B=256, gamma=gamma, steps=40, seed=4)
+    beta = beta_of(pair, dev)
+    print(f"V={V} iid beta={beta:.4f}: {st.tokens_per_step:.4f} tokens/step, "
+          f"Eq. (1) {loop.eq1_tokens_per_step(beta, gamma)[0]:.4f}")
+    check_eq1(st, beta, gamma)
+
+
+@pytest.mark.gpu
+def test_loop_non_iid_tables_keep_the_target_distribution():
+    dev = torch.device("cuda:0")
+    pair = loop.make_bigram_pair(16, seed=5, kind="free", dtype="bf16", temperature=1.0, device=dev)
+    st = loop.run(pair, B=256, gamma=6, steps=300, seed=5, keep_pairs=True)
+    hist = st.accepted_hist / st.accepted_hist.sum()
+    print(f"V=16 free: {st.tokens_per_step:.4f} tokens/step, accepted-draft histogram {np.round(hist, 4)}")
+    assert chi_square_pvalue(st.pair_counts, target_table_probs(pair)) > 1e-4
