@@ -9,6 +9,7 @@ the oracle shares no code with that path.
 from .verifier import (  # noqa: F401
     SAMPLE_FALLBACK_MASS,
     accept_draft,
+    adjusted_target_probs,
     inverse_cdf,
     residual_weights,
     row_statistics,

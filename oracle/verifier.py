@@ -53,6 +53,17 @@ the design notes of the repository):
 * Output layout. A request emits n accepted drafts plus one token; the
   row is padded with -1 to g + 1 entries ([GUIDE] returns a variable-length
   tensor instead).
+* top-k / top-p ([VISUAL] on paper §2.2: like the temperature, they fold into
+  an adjusted p, and the same rejection sampling runs on it; [GUIDE] asks to
+  keep them identical on both sides). The pages give no details; we take:
+  the filters act on the temperature-scaled target, top-k first, then top-p
+  on the renormalized top-k distribution; both are thresholds on the logit
+  value, ties at the threshold kept: top-k keeps every token whose logit is
+  at least the k-th largest logit (counted with multiplicity), top-p keeps
+  every token whose logit is at least t, t the largest logit value whose
+  tokens at or above it carry at least top_p of the mass; the kept tokens
+  are renormalized. top_k <= 0 or >= V, and top_p >= 1, switch a filter off.
+  q arrives already adjusted by the drafter.
 """
 
 from __future__ import annotations
@@ -79,6 +90,33 @@ def target_probs(logits_row, temperature: float) -> np.ndarray:
     s = l / float(temperature)
     e = np.exp(s - np.max(s))
     return e / np.sum(e)
+
+
+def adjusted_target_probs(logits_row, temperature: float, top_k: int = 0, top_p: float = 1.0) -> np.ndarray:
+    """Target distribution after top-k and top-p (see the module notes for the
+    readings): the kept set is {l >= tau}, with tau the larger of the top-k
+    and top-p thresholds, and p is renormalized over it. T > 0."""
+    l = np.asarray(logits_row, dtype=np.float64)
+    p = target_probs(l, temperature)
+    keep = np.ones(len(l), dtype=bool)
+    if 0 < top_k < len(l):
+        kth = np.sort(l)[::-1][top_k - 1]  # the k-th largest logit, with multiplicity
+        keep &= l >= kth
+    if not keep.all():  # renormalized only when something was removed
+        p = np.where(keep, p, 0.0)
+        p = p / np.sum(p)
+    if top_p < 1.0:
+        vals = np.unique(l[keep])[::-1]  # kept logit values, descending
+        t = vals[-1]
+        for v in vals:  # the first (largest) value whose tokens at or above it reach top_p
+            if np.sum(p[l >= v]) >= top_p:
+                t = v
+                break
+        if np.any(l[keep] < t):
+            keep &= l >= t
+            p = np.where(keep, p, 0.0)
+            p = p / np.sum(p)
+    return p
 
 
 def accept_draft(p_x: float, q_x: float, u: float) -> bool:
@@ -181,7 +219,8 @@ def row_statistics(logits_row, temperature: float, q_row, x):
     return m, lse, float(p[int(x)]), r
 
 
-def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms, temperature, with_stats=False):
+def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms, temperature, with_stats=False,
+                  top_k=0, top_p=1.0):
     """Ragged batch ([VISUAL], vLLM verification path: requests are scanned
     through cu_num_draft_tokens and each emits accepted + recovered + bonus).
 
@@ -192,8 +231,12 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
       None (one-hot drafts); draft_tokens [T_total]; uniforms [T_total + B]
       in target-row layout.
     Returns (out_tokens [T_total + B] int64, -1 padded; num_accepted [B];
-    row_stats [T_total + B, 4] or None).
+    row_stats [T_total + B, 4] or None). top_k / top_p adjust every target
+    row (adjusted_target_probs; T > 0, no row statistics).
     """
+    filtered = (0 < top_k) or top_p < 1.0
+    if filtered and (temperature == 0.0 or with_stats):
+        raise ValueError("top-k / top-p are defined here for T > 0 without row statistics")
     cu = np.asarray(cu_num_draft_tokens, dtype=np.int64)
     nreq = len(cu) - 1
     rows = int(cu[-1]) + nreq
@@ -204,7 +247,10 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
         d0, d1 = int(cu[b]), int(cu[b + 1])
         g = d1 - d0
         t0 = d0 + b
-        p_rows = [target_probs(logits[t0 + i], temperature) for i in range(g + 1)]
+        if filtered:
+            p_rows = [adjusted_target_probs(logits[t0 + i], temperature, top_k, top_p) for i in range(g + 1)]
+        else:
+            p_rows = [target_probs(logits[t0 + i], temperature) for i in range(g + 1)]
         q_rows = None if draft_probs is None else [draft_probs[d0 + i] for i in range(g)]
         x = draft_tokens[d0:d1]
         toks, n = verify_request(p_rows, q_rows, x, uniforms[t0:t0 + g + 1])
@@ -218,7 +264,7 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
     return out, nacc, stats
 
 
-def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, with_stats=False):
+def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, with_stats=False, top_k=0, top_p=1.0):
     """Dense batch: logits [B, g+1, V], draft_probs [B, g, V] or None,
     draft_tokens [B, g], uniforms [B, g+1]. The dense call is the ragged call
     with cu[b] = b * g. Returns (out_tokens [B, g+1], num_accepted [B],
@@ -229,7 +275,7 @@ def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, with_
     q = None if draft_probs is None else np.asarray(draft_probs).reshape(nreq * g, v)
     out, nacc, stats = verify_ragged(
         np.asarray(logits).reshape(nreq * g1, v), q, np.asarray(draft_tokens).reshape(-1), cu,
-        np.asarray(uniforms).reshape(-1), temperature, with_stats)
+        np.asarray(uniforms).reshape(-1), temperature, with_stats, top_k, top_p)
     return out.reshape(nreq, g1), nacc, (None if stats is None else stats.reshape(nreq, g1, 4))
 
 

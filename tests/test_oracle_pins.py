@@ -420,3 +420,128 @@ def test_onehot_draft_accepts_with_probability_p_x():
     freq = lattice_freq(lambda j: verify_request([p, p], None, [2], [1.0, lattice_u(j)])[0][0])
     assert freq == {0: N_LATTICE // 5, 1: N_LATTICE - N_LATTICE // 5} or \
         abs(freq[0] - N_LATTICE * 0.2) <= 1
+
+
+# ------------------------------------------------------------ top-k / top-p adjusted p
+
+
+def _sorted_prefix_filter(l, T, k, top_p):
+    """For rows with distinct logits: keep the k largest, then the shortest
+    prefix (by decreasing probability) whose cumulative probability reaches
+    top_p, renormalize. Written without value thresholds."""
+    order = np.argsort(-l, kind="stable")
+    idx = order[:k] if 0 < k < len(l) else order
+    w = np.exp((l[idx] - l[idx].max()) / T)
+    w = w / w.sum()
+    if top_p < 1.0:
+        c = np.cumsum(w)
+        n = int(np.argmax(c >= top_p)) + 1 if np.any(c >= top_p) else len(idx)
+        idx = idx[:n]
+    out = np.zeros(len(l))
+    out[idx] = np.exp((l[idx] - l[idx].max()) / T)
+    return out / out.sum()
+
+
+def test_adjusted_probs_off_is_softmax():
+    rng = np.random.default_rng(20)
+    l = rng.normal(0, 3, 300)
+    for T in (0.5, 1.0, 2.0):
+        np.testing.assert_array_equal(oracle.adjusted_target_probs(l, T), target_probs(l, T))
+        np.testing.assert_array_equal(oracle.adjusted_target_probs(l, T, top_k=300, top_p=1.0), target_probs(l, T))
+        np.testing.assert_array_equal(oracle.adjusted_target_probs(l, T, top_k=0, top_p=1.0), target_probs(l, T))
+
+
+def test_adjusted_probs_match_a_sorted_prefix_filter_on_distinct_logits():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        v = int(rng.integers(2, 80))
+        l = rng.normal(0, 2.5, v)
+        T = float(rng.choice([0.3, 0.7, 1.0, 1.6]))
+        k = int(rng.integers(0, v + 3))
+        top_p = float(rng.choice([1.0, 0.95, 0.8, 0.5, 0.1, 1e-9]))
+        got = oracle.adjusted_target_probs(l, T, k, top_p)
+        want = _sorted_prefix_filter(l, T, k, top_p)
+        np.testing.assert_array_equal(got > 0, want > 0)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-300)
+
+
+def test_adjusted_probs_closed_forms_and_ties():
+    l = np.array([3.0, 3.0, 1.0, 0.0, 3.0, -2.0])
+    third = np.array([1, 1, 0, 0, 1, 0]) / 3.0
+    # top-k counts with multiplicity and keeps every token tied at the k-th value
+    for k in (1, 2, 3):
+        np.testing.assert_allclose(oracle.adjusted_target_probs(l, 1.0, top_k=k), third, rtol=1e-15)
+    p4 = oracle.adjusted_target_probs(l, 1.0, top_k=4)
+    assert list(p4 > 0) == [True, True, True, False, True, False]
+    # a tiny top_p keeps the maximum's value group, a unique maximum alone
+    np.testing.assert_allclose(oracle.adjusted_target_probs(l, 0.7, top_p=1e-12), third, rtol=1e-15)
+    u = np.array([0.5, 2.0, -1.0, 1.9])
+    np.testing.assert_array_equal(oracle.adjusted_target_probs(u, 1.0, top_k=1), [0, 1, 0, 0])
+    np.testing.assert_array_equal(oracle.adjusted_target_probs(u, 1.0, top_p=1e-9), [0, 1, 0, 0])
+    # top-p applies to the renormalized top-k distribution: with the two largest kept,
+    # p = (e^2, e^1.9) / sum, and 0.5 of that mass is reached by the first alone
+    assert list(oracle.adjusted_target_probs(u, 1.0, top_k=2, top_p=0.5) > 0) == [False, True, False, False]
+    assert list(oracle.adjusted_target_probs(u, 1.0, top_k=2, top_p=0.6) > 0) == [False, True, False, True]
+
+
+def test_adjusted_probs_invariants_with_ties():
+    """Brute force over every candidate threshold on rows drawn from a few
+    values: the kept set is {l >= tau}, tau the larger of the top-k threshold
+    (largest value with at least k tokens at or above it) and the top-p one
+    (largest kept value whose tokens at or above it carry >= top_p of the
+    renormalized top-k mass), and that set is the smallest such."""
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        v = int(rng.integers(1, 12))
+        l = rng.choice([-1.0, 0.0, 0.5, 2.0, 2.5], v)
+        T = float(rng.choice([0.5, 1.0]))
+        k = int(rng.integers(0, v + 2))
+        top_p = float(rng.choice([1.0, 0.9, 0.6, 0.3, 0.05]))
+        cand = sorted(set(l.tolist()), reverse=True)
+        tk = cand[-1]
+        if 0 < k < v:
+            tk = max(t for t in cand if np.sum(l >= t) >= k)
+        base = np.where(l >= tk, np.exp((l - l.max()) / T), 0.0)
+        base /= base.sum()
+        tp = tk
+        if top_p < 1.0:
+            tp = max(t for t in cand if t >= tk and base[l >= t].sum() >= top_p)
+        tau = max(tk, tp)
+        want = np.where(l >= tau, np.exp((l - l.max()) / T), 0.0)
+        want /= want.sum()
+        got = oracle.adjusted_target_probs(l, T, k, top_p)
+        np.testing.assert_array_equal(got > 0, l >= tau)
+        np.testing.assert_allclose(got, want, rtol=1e-12)
+        assert abs(got.sum() - 1.0) < 1e-12
+        kept = sorted(set(l[got > 0].tolist()))
+        if top_p < 1.0 and len(kept) > 1:  # minimal: without the smallest kept value, below top_p
+            assert base[l > kept[0]].sum() < top_p
+
+
+def test_filtered_batch_equals_per_request_adjusted_rows():
+    rng = np.random.default_rng(23)
+    B, g, V, T = 5, 3, 40, 0.9
+    logits = rng.normal(0, 2, (B, g + 1, V))
+    q = rng.dirichlet(np.ones(V), (B, g))
+    x = np.array([[rng.choice(V, p=q[b, i]) for i in range(g)] for b in range(B)])
+    u = (rng.integers(0, N_LATTICE, (B, g + 1)) + 1) * 2.0 ** -24
+    out, nacc, _ = oracle.verify_probs(logits, q, x, u, T, top_k=7, top_p=0.8)
+    for b in range(B):
+        p_rows = [oracle.adjusted_target_probs(logits[b, i], T, 7, 0.8) for i in range(g + 1)]
+        toks, n = verify_request(p_rows, list(q[b]), x[b], u[b])
+        assert n == nacc[b] and list(out[b, : n + 1]) == toks
+
+
+def test_top_p_boundary_is_inclusive():
+    """When the tokens at or above a value carry exactly top_p of the mass,
+    top-p stops there (reading: "at least top_p")."""
+    l = np.array([5.0, 0.0, 5.0, 0.0, -1.0])
+    for T in (1.0, 0.5):
+        p = target_probs(l, T)
+        top = float(np.sum(p[l >= 5.0]))  # the exact mass of the top value group
+        got = oracle.adjusted_target_probs(l, T, top_p=top)
+        assert list(got > 0) == [True, False, True, False, False]
+        np.testing.assert_allclose(got[[0, 2]], [0.5, 0.5], rtol=1e-15)
+        # just above it, the next value group joins
+        assert list(oracle.adjusted_target_probs(l, T, top_p=np.nextafter(top, 2.0)) > 0) == [True, True, True, True,
+                                                                                             False]
