@@ -121,7 +121,7 @@ size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size);
 /* Static, human-readable text for a status code. */
 const char* spec_verify_status_string(int status);
 
-/* Library ABI version (currently 1). */
+/* Library ABI version (currently 2: the *_filtered entry points). */
 int spec_verify_version(void);
 
 /* Self-check of the one hardware property the certified fast path relies on:
@@ -218,6 +218,49 @@ int spec_verify_ragged(const void* target_logits, int logits_dtype, const float*
                        int32_t vocab_size, double temperature, uint32_t flags,
                        int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_probs_filtered / spec_verify_ragged_filtered - the same
+ * verification on a target adjusted by top-k and top-p (blog.vllbc.top, the
+ * note on paper §2.2: like the temperature, top-k and top-p fold into the
+ * adjusted p, and the rejection sampling then runs on it; the draft
+ * probabilities must arrive already adjusted by the drafter's own settings).
+ * The pages give no further detail; this library's reading:
+ *  - the filters act on the temperature-scaled target, top-k first, then
+ *    top-p on the renormalised top-k distribution;
+ *  - both are thresholds on the logit value, ties kept: top-k keeps every
+ *    token whose logit is >= the top_k-th largest logit (counted with
+ *    multiplicity); top-p then keeps every token whose logit is >= t, t the
+ *    largest logit value whose tokens at or above it carry at least top_p of
+ *    the top-k mass (the boundary inclusive);
+ *  - p = the softmax renormalised over the kept tokens and 0 elsewhere, for
+ *    every target row (draft positions and the bonus row); a draft token
+ *    outside the kept set has p(x) = 0 and is rejected.
+ *  top_k          <= 0 or >= vocab_size: no top-k.
+ *  top_p          in (0, 1]; 1: no top-p. Anything else (or NaN) is
+ *                 SV_ERR_INVALID_ARGUMENT.
+ *  temperature    > 0 and finite (greedy verification has no use for
+ *                 the filters: the argmax is always kept).
+ *  draft_probs    required (not NULL).
+ * Every other argument as in spec_verify_probs / spec_verify_ragged (no
+ * flags, no row statistics: the default lazy mode). Results equal
+ * exact-arithmetic results; the top-p comparison is certified in fp32 and
+ * settled in fp64 when within the bound, so only a top-p mass within about
+ * 1e-12 relative of the target can come out either way. Same workspace
+ * size. With both filters off the results are those of spec_verify_probs /
+ * spec_verify_ragged.
+ */
+int spec_verify_probs_filtered(const void* target_logits, int logits_dtype, const float* draft_probs,
+                               const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
+                               int32_t gamma, int32_t vocab_size, double temperature, int32_t top_k, double top_p,
+                               int64_t* out_tokens, int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                               void* stream);
+int spec_verify_ragged_filtered(const void* target_logits, int logits_dtype, const float* draft_probs,
+                                const int64_t* draft_tokens, const int32_t* cu_num_draft_tokens,
+                                const float* uniforms, int32_t num_requests, int32_t num_draft_tokens,
+                                int32_t vocab_size, double temperature, int32_t top_k, double top_p,
+                                int64_t* out_tokens, int32_t* num_accepted, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,8 @@ SV_PROFILE_REQUEST = 1
 
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
            "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
-           "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop")
+           "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop",
+           "spec_verify_probs_filtered", "spec_verify_ragged_filtered")
 
 _lib = None
 
@@ -78,6 +79,12 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_ragged.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp,
                                        sz, vp]
     lib.spec_verify_ragged.restype = ctypes.c_int
+    lib.spec_verify_probs_filtered.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, i32, f64, vp, vp,
+                                               vp, sz, vp]
+    lib.spec_verify_probs_filtered.restype = ctypes.c_int
+    lib.spec_verify_ragged_filtered.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f64, i32, f64, vp,
+                                                vp, vp, sz, vp]
+    lib.spec_verify_ragged_filtered.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -212,6 +219,67 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_ragged")
     return out, nacc, stats, workspace
+
+
+def verify_probs_filtered(logits, draft_probs, draft_tokens, uniforms, temperature, top_k=0, top_p=1.0,
+                          workspace=None, stream=None):
+    """verify_probs on the target adjusted by top-k (top_k <= 0 or >= V: off)
+    and top-p (in (0, 1], 1: off); draft_probs required. Returns
+    (out_tokens [B, g+1] int64, num_accepted [B] int32, workspace)."""
+    lib = load()
+    dev = logits.device
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, g1, V = logits.shape
+    g = g1 - 1
+    _check(logits, "logits", device=dev)
+    _check(draft_probs, "draft_probs", torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    _check(uniforms, "uniforms", torch.float32, dev)
+    if draft_probs is None or tuple(draft_probs.shape) != (B, g, V):
+        raise ValueError("draft_probs must be [B, gamma, V]")
+    if tuple(draft_tokens.shape) != (B, g) or tuple(uniforms.shape) != (B, g1):
+        raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
+    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    workspace, need = _workspace(B * g1, V, dev, workspace)
+    rc = lib.spec_verify_probs_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                        _ptr(uniforms), B, g, V, float(temperature), int(top_k), float(top_p),
+                                        _ptr(out), _ptr(nacc), _ptr(workspace), workspace.numel(),
+                                        _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_probs_filtered")
+    return out, nacc, workspace
+
+
+def verify_ragged_filtered(logits, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms, temperature, top_k=0,
+                           top_p=1.0, workspace=None, stream=None):
+    """verify_ragged on the target adjusted by top-k and top-p (see
+    verify_probs_filtered). Returns (out_tokens [T+B], num_accepted [B], workspace)."""
+    lib = load()
+    dev = logits.device
+    nb = cu_num_draft_tokens.numel() - 1
+    T = draft_tokens.numel()
+    V = logits.shape[-1]
+    _check(logits, "logits", device=dev)
+    _check(draft_probs, "draft_probs", torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    _check(cu_num_draft_tokens, "cu_num_draft_tokens", torch.int32, dev)
+    _check(uniforms, "uniforms", torch.float32, dev)
+    if tuple(logits.shape) != (T + nb, V) or uniforms.numel() != T + nb:
+        raise ValueError("logits must be [T+B, V] and uniforms [T+B]")
+    if draft_probs is None or tuple(draft_probs.shape) != (T, V):
+        raise ValueError("draft_probs must be [T, V]")
+    out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
+    nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
+    workspace, need = _workspace(T + nb, V, dev, workspace)
+    rc = lib.spec_verify_ragged_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                         _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature),
+                                         int(top_k), float(top_p), _ptr(out), _ptr(nacc), _ptr(workspace),
+                                         workspace.numel(), _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_ragged_filtered")
+    return out, nacc, workspace
 
 
 def selftest_exp2(device=None, stream=None):

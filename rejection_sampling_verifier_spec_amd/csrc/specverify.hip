@@ -422,6 +422,25 @@ __device__ void block_scan(double v, BlockScratchT<NT>& s, double& excl, double&
   __syncthreads();
 }
 
+// Sum over a wave by an xor butterfly: every lane ends with the same value
+// (a + b == b + a), in a fixed association.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive scan over the 64 lanes (lane order), fixed association.
+__device__ __forceinline__ double wave_scan_incl_d(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 // ----------------------------------------------------------------------------
 // row task decoding (dense: cu == nullptr)
 
@@ -560,6 +579,8 @@ struct ProbsArgs {
   int pm;         // lazy mode: positions 0 .. pm - 1 are launched position-major
   int* surv;      // lazy mode: requests still undecided after the first launch (count at surv_n)
   int* surv_n;    // lazy mode: [0] the count, [16] the first launch's finished-block counter
+  int top_k;      // filtered lazy mode: keep the top_k largest logits (with ties); off unless 0 < top_k < V
+  double top_p;   // filtered lazy mode: keep the smallest top set of mass >= top_p; off when >= 1
 };
 
 struct RowShared {
@@ -680,7 +701,8 @@ constexpr uint32_t kRowNeedExact = kRowNeedExactBit;  // set by the fast kernels
 constexpr uint32_t kRowDeferred = SV_ROW_DEFERRED;
 constexpr uint32_t kRowUnread = SV_ROW_UNREAD;
 constexpr uint32_t kRowUndecided = SV_ROW_UNDECIDED;
-constexpr uint32_t kFlagLazy = 0x80000000u;  // internal: set by the host for the lazy mode
+constexpr uint32_t kFlagLazy = 0x80000000u;    // internal: set by the host for the lazy mode
+constexpr uint32_t kFlagFilter = 0x40000000u;  // internal: lazy mode with top-k / top-p
 constexpr int kMarkBase = 1 << 30;              // lazy mode: per-request mark = kMarkBase - position
 constexpr int kExactPer = kTile / kNT;      // elements per thread of one tile (8)
 constexpr double kZSlack = 1e-12;           // widening of the Z interval for fp64 rounding
@@ -1326,9 +1348,446 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
 // EAGER: rejected draft rows with q draw their replacement here (eager and
 // all-residual modes); otherwise (lazy mode) they are deferred, and the kernel
 // has no q pass at all.
-template <typename LT, bool VEC, int NT, bool EAGER>
+// ----------------------------------------------------------------------------
+// top-k / top-p: the threshold on the logit value (lazy mode)
+//
+// blog.vllbc.top, note on paper §2.2: top-k and top-p, like the temperature,
+// fold into an adjusted target p on which the same rejection sampling runs
+// (q arrives already adjusted by the drafter). The pages give no further
+// detail; the reading taken: both filters act on the temperature-scaled
+// target, top-k first, then top-p on the renormalised top-k distribution,
+// and both are thresholds on the logit value with ties kept. tau_k is the
+// k-th largest logit, counted with multiplicity; tau_p is the largest logit
+// value v >= tau_k such that the tokens with l >= v carry at least top_p of
+// the top-k mass Z_K. The kept set is {l >= tau}, tau = max(tau_k, tau_p),
+// and p is renormalised over it: p(x) = e_x / Z_tau if l_x >= tau, else 0.
+//
+// Both thresholds come out of a radix select over a monotone 32-bit key of
+// the logit, 8-bit digits from the top (two levels for bf16 logits, whose key
+// is fixed by its top 16 bits; four for fp32), one sweep over the row per
+// level, with per-digit histograms in LDS:
+//  * top-k counts the elements per digit (integer atomics: exact, whatever
+//    the order in which they land);
+//  * top-p sums per digit the masses e = 2^((l - m) s) of the elements with
+//    key >= key(tau_k), computed in fp32 exactly as in pass 1 (same error
+//    model), as 64-bit fixed-point integers (order-independent sums), with
+//    e |a| beside them for the error bound. A digit is taken when the
+//    cumulative mass clears the target top_p Z_K by more than the bound;
+//    otherwise fp64 sweeps in a fixed order compute the cumulative mass at up
+//    to eight undecided digit boundaries and Z_K, and decide.
+// Z_tau and its bound are the sums of the masses taken on the way down.
+
+constexpr int kSelDigits = 256;
+constexpr int kSelCand = 8;  // digit boundaries per fp64 sweep
+
+struct FilterShared {
+  unsigned long long mass[kSelDigits];  // per digit: fixed-point sum of e
+  unsigned long long mea[kSelDigits];   // per digit: fixed-point sum of e |a|
+  uint32_t cnt[kSelDigits];             // per digit: elements
+  int pos;                              // chosen position of the level (digit 255 - pos), -1: undecided
+  int amb_lo, amb_hi;                   // undecided positions (pos == -1)
+  uint32_t above;                       // top-k: elements above the chosen digit
+  unsigned long long m_above, e_above;  // sums over the digits above the chosen one
+  unsigned long long m_at, e_at;        // sums of the chosen digit
+};
+struct NoFilterShared {};
+
+// Monotone key of a logit: a < b iff key(a) < key(b); -0 and +0 share a key.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// floor(v 2^F) for a finite v >= 0 (denormals count as 0): v = mt 2^(ex - 150).
+__device__ __forceinline__ unsigned long long to_fixed(float v, int F) {
+  const uint32_t b = __float_as_uint(v);
+  const int ex = static_cast<int>(b >> 23);
+  const unsigned long long mt = static_cast<unsigned long long>((b & 0x7fffffu) | 0x800000u);
+  const int sh = ex - 150 + F;
+  const unsigned long long up = mt << min(max(sh, 0), 63);
+  const unsigned long long dn = mt >> min(max(-sh, 0), 63);
+  return ex == 0 ? 0ull : (sh >= 0 ? up : dn);
+}
+
+// Bound on |fixed-point mass - exact mass| of a set of elements whose
+// fixed-point sums are M (of e) and EA (of e |a|), in e-units: the relative
+// error C1 |a| + C0 of each fp32 term (pass 1's model), the flooring of each
+// term to 2^-F (quant = V 2^-F covers any set), and the rounding of the
+// conversions to fp64.
+__device__ __forceinline__ double fixed_bound(double M, double EA, double quant) {
+  return kSafety * 1.01 * (kC1 * (EA + quant) + kC0 * (M + quant)) + quant + 1e-14 * M;
+}
+
+// Calls f(v) for every element of the row: wave w visits tiles w, w + waves,
+// ..., with the next tile's loads in flight while one is visited.
+template <typename LT, bool VEC, int NT, typename Fn>
+__device__ __forceinline__ void sweep_row(const LT* __restrict__ lrow, int V, Fn&& f) {
+  constexpr int kW = NT / 64;
+  using L = Lay<LT, VEC>;
+  using Raw = RawTile<LT, VEC>;
+  const int lane = threadIdx.x & 63;
+  const int nt = (V + kTile - 1) / kTile;
+  int j = threadIdx.x >> 6;
+  if (j >= nt) return;
+  Raw ra, rb;
+  ra.load(lrow, V, j * kTile, lane);
+  auto visit = [&](const Raw& r, int jj) {
+    const int base = jj * kTile;
+    const bool full = base + kTile <= V;
+#pragma unroll
+    for (int k = 0; k < kLaneElems; ++k)
+      if (full || L::index(base, lane, k) < V) f(r.get(k));
+  };
+  while (true) {
+    rb.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+    visit(ra, j);
+    j += kW;
+    if (j >= nt) break;
+    ra.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+    visit(rb, j);
+    j += kW;
+    if (j >= nt) break;
+  }
+}
+
+// Positions t = 0..255 stand for the digits 255 - t, in descending key order;
+// lane l of wave 0 holds positions 4l .. 4l + 3.
+
+// Wave 0: the position at which the count from the top first reaches kk
+// (1 <= kk <= the level's total), and the count above it.
+__device__ void pick_count(FilterShared& fs, uint32_t kk) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) c[r] = fs.cnt[255 - 4 * lane - r];
+  const uint32_t ls = (c[0] + c[1]) + (c[2] + c[3]);
+  uint32_t incl = ls;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const uint32_t excl = incl - ls;
+  if (excl < kk && incl >= kk) {  // exactly one lane
+    uint32_t cum = excl;
+    int t = 4 * lane + 3;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (cum + c[r] >= kk) {
+        t = 4 * lane + r;
+        break;
+      }
+      cum += c[r];
+    }
+    fs.pos = t;
+    fs.above = cum;
+  }
+}
+
+// Wave 0: fixed-point sums over the positions before t, and of position t
+// (t = 256: the level's totals in m_above, e_above).
+__device__ void level_take(FilterShared& fs, int t) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long ma = 0, ea = 0, mt = 0, et = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = 4 * lane + r;
+    const unsigned long long mv = fs.mass[255 - p], ev = fs.mea[255 - p];
+    if (p < t) {
+      ma += mv;
+      ea += ev;
+    } else if (p == t) {
+      mt = mv;
+      et = ev;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ma += __shfl_xor(ma, o);
+    ea += __shfl_xor(ea, o);
+    mt += __shfl_xor(mt, o);
+    et += __shfl_xor(et, o);
+  }
+  if (lane == 0) {
+    fs.m_above = ma;
+    fs.e_above = ea;
+    fs.m_at = mt;
+    fs.e_at = et;
+  }
+}
+
+// Wave 0: top-p at one level. With C (mass above the level's prefix, bound
+// Cerr) and the target tgt (bound tgterr), position t is certainly below the
+// target when C + cum(t) + err(t) < tgt and certainly at or above it when
+// C + cum(t) - err(t) >= tgt (cum(t) = mass of positions 0..t). The crossing
+// is the first position at or above; when some positions are neither, their
+// range is left to the fp64 sweeps (pos = -1).
+__device__ void pick_mass(FilterShared& fs, double C, double Cerr, double tgt, double tgterr, double inv,
+                          double quant) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long mv[4], ev[4], ls = 0, le = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mv[r] = fs.mass[255 - 4 * lane - r];
+    ev[r] = fs.mea[255 - 4 * lane - r];
+    ls += mv[r];
+    le += ev[r];
+  }
+  unsigned long long im = ls, ie = le;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long ym = __shfl_up(im, o), ye = __shfl_up(ie, o);
+    if (lane >= o) {
+      im += ym;
+      ie += ye;
+    }
+  }
+  unsigned long long cm = im - ls, ce = ie - le;
+  int hat = 256, alo = 256, ahi = -1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    cm += mv[r];
+    ce += ev[r];
+    const double mc = static_cast<double>(cm) * inv;
+    const double v = C + mc;
+    const double err = Cerr + fixed_bound(mc, static_cast<double>(ce) * inv, quant) + tgterr;
+    const int t = 4 * lane + r;
+    if (v >= tgt) hat = min(hat, t);
+    if (!(v + err < tgt) && !(v - err >= tgt)) {
+      alo = min(alo, t);
+      ahi = max(ahi, t);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    hat = min(hat, __shfl_xor(hat, o));
+    alo = min(alo, __shfl_xor(alo, o));
+    ahi = max(ahi, __shfl_xor(ahi, o));
+  }
+  if (lane == 0) {
+    if (ahi < 0 && hat < 256) {
+      fs.pos = hat;
+    } else {  // undecided positions (or, defensively, no crossing found: all of them)
+      fs.pos = -1;
+      fs.amb_lo = ahi < 0 ? 0 : alo;
+      fs.amb_hi = ahi < 0 ? 255 : ahi;
+    }
+  }
+}
+
+// N fixed-order block sums with one pair of barriers (s.d holds N * waves).
+template <int NT, int N>
+__device__ void block_sum_nt(double (&v)[N], BlockScratchT<NT>& s) {
+  constexpr int kW = NT / 64;
+  static_assert(N * kW <= NT, "scratch too small");
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) s.d[i * kW + wave] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double r = 0.0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) r += s.d[i * kW + w];
+    v[i] = r;
+  }
+  __syncthreads();
+}
+
+// fp64 sweep in a fixed order (per thread in element order, then a fixed
+// block reduction): acc[c] = mass of the elements with key >= max(B[c], klo)
+// for c < kSelCand, acc[kSelCand] = Z_K (key >= klo); masses 2^((l - m) s64).
+template <typename LT, bool VEC, int NT>
+__device__ void exact_masses(const LT* __restrict__ lrow, int V, float m, double s64, uint32_t klo,
+                             const uint32_t (&B)[kSelCand], double (&acc)[kSelCand + 1], BlockScratchT<NT>& sc) {
+#pragma unroll
+  for (int c = 0; c <= kSelCand; ++c) acc[c] = 0.0;
+  const double md = static_cast<double>(m);
+  sweep_row<LT, VEC, NT>(lrow, V, [&](float v) {
+    const uint32_t key = order_key(v);
+    if (key >= klo) {
+      const double e = exp2((static_cast<double>(v) - md) * s64);
+#pragma unroll
+      for (int c = 0; c < kSelCand; ++c) acc[c] += key >= B[c] ? e : 0.0;
+      acc[kSelCand] += e;
+    }
+  });
+  block_sum_nt<NT, kSelCand + 1>(acc, sc);
+}
+
+// The key of tau for a prefix of `levels` digits (bf16: the key whose top 16
+// bits are the prefix and whose low bits are those of a bf16 value).
+__device__ __forceinline__ uint32_t prefix_key(uint32_t prefix, int levels) {
+  if (levels == 4) return prefix;
+  return (prefix << 16) | ((prefix & 0x8000u) ? 0u : 0xffffu);
+}
+
+// Threshold tau of one row and Z_tau with the bound on its error (e-units of
+// pass 1, carrying 2^D). m is the row max; called by every thread of the block.
+template <typename LT, bool VEC, int NT>
+__device__ void row_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, float m, double shift,
+                              FilterShared& fs, BlockScratchT<NT>& sc, float& tau, double& Zt, double& dZt) {
+  constexpr int kLevels = sizeof(LT) == 2 ? 2 : 4;
+  const int V = a.V, tid = threadIdx.x;
+  const float s = a.s32, cm = -(m * s);
+  const int F = 62 - (V > 1 ? 32 - __clz(V - 1) : 0);  // V terms <= 1 (+ rounding) stay below 2^63
+  const double inv = ldexp(1.0, -F);
+  const double quant = static_cast<double>(V) * inv;
+  const bool use_k = a.top_k > 0 && a.top_k < V;
+  const bool use_p = a.top_p < 1.0;
+  auto add_mass = [&](float v, uint32_t d) {
+    const float arg = fmaxf(fmaf(v, s, cm), -4096.f);
+    const float e = fexp2(arg);
+    atomicAdd(&fs.mass[d], to_fixed(e, F));
+    atomicAdd(&fs.mea[d], to_fixed(e * fabsf(arg), F));
+  };
+  uint32_t klo = 0;
+  double Z = 0.0, dZ = 0.0;
+  if (use_k) {
+    const bool wm = !use_p;  // top-k alone: Z_tau comes out of these sweeps
+    uint32_t prefix = 0, kk = static_cast<uint32_t>(a.top_k);
+    for (int lv = 0; lv < kLevels; ++lv) {
+      const int shift_d = 24 - 8 * lv, hs = shift_d + 8;
+      for (int d = tid; d < kSelDigits; d += NT) {
+        fs.cnt[d] = 0u;
+        fs.mass[d] = 0ull;
+        fs.mea[d] = 0ull;
+      }
+      if (tid == 0) {
+        fs.pos = kSelDigits - 1;
+        fs.above = 0u;
+      }
+      __syncthreads();
+      sweep_row<LT, VEC, NT>(lrow, V, [&](float v) {
+        const uint32_t key = order_key(v);
+        if (hs >= 32 || (key >> hs) == prefix) {
+          const uint32_t d = (key >> shift_d) & 255u;
+          atomicAdd(&fs.cnt[d], 1u);
+          if (wm) add_mass(v, d);
+        }
+      });
+      __syncthreads();
+      if (tid < 64) pick_count(fs, kk);
+      __syncthreads();
+      const int t = fs.pos;
+      kk -= fs.above;
+      prefix = (prefix << 8) | static_cast<uint32_t>(255 - t);
+      if (wm) {
+        if (tid < 64) level_take(fs, t);
+        __syncthreads();
+        const double ma = static_cast<double>(fs.m_above) * inv, ea = static_cast<double>(fs.e_above) * inv;
+        Z += ma;
+        dZ += fixed_bound(ma, ea, quant);
+        if (lv == kLevels - 1) {
+          const double mt = static_cast<double>(fs.m_at) * inv, et = static_cast<double>(fs.e_at) * inv;
+          Z += mt;
+          dZ += fixed_bound(mt, et, quant);
+        }
+      }
+      __syncthreads();  // fs is cleared by the next level
+    }
+    klo = prefix_key(prefix, kLevels);
+  }
+  uint32_t kt = klo;
+  if (use_p) {
+    uint32_t prefix = 0;
+    double C = 0.0, Cerr = 0.0, tgt = 0.0, tgterr = 0.0;
+    for (int lv = 0; lv < kLevels; ++lv) {
+      const int shift_d = 24 - 8 * lv, hs = shift_d + 8;
+      for (int d = tid; d < kSelDigits; d += NT) {
+        fs.mass[d] = 0ull;
+        fs.mea[d] = 0ull;
+      }
+      __syncthreads();
+      sweep_row<LT, VEC, NT>(lrow, V, [&](float v) {
+        const uint32_t key = order_key(v);
+        if (key >= klo && (hs >= 32 || (key >> hs) == prefix)) add_mass(v, (key >> shift_d) & 255u);
+      });
+      __syncthreads();
+      if (lv == 0) {  // Z_K: the mass of every element with key >= key(tau_k)
+        if (tid < 64) level_take(fs, kSelDigits);
+        __syncthreads();
+        const double zk = static_cast<double>(fs.m_above) * inv;
+        tgt = a.top_p * zk;
+        tgterr = a.top_p * fixed_bound(zk, static_cast<double>(fs.e_above) * inv, quant);
+        __syncthreads();
+      }
+      if (tid < 64) pick_mass(fs, C, Cerr, tgt, tgterr, inv, quant);
+      __syncthreads();
+      int t = fs.pos;
+      if (t < 0) {
+        // fp64 sweeps: t lies in [lo, hi + 1], position hi + 1 (if any) at or
+        // above the target; candidates split the range evenly, the last is hi
+        int lo = fs.amb_lo, hi = fs.amb_hi;
+        double te = 0.0;
+        for (int guard = 0; guard < 8; ++guard) {  // the range shrinks 8-fold per sweep
+          const int n = min(kSelCand, hi - lo + 1);
+          int cand[kSelCand];
+          uint32_t B[kSelCand];
+#pragma unroll
+          for (int c = 0; c < kSelCand; ++c) {
+            cand[c] = c < n ? lo + ((hi - lo + 1) * (c + 1)) / n - 1 : hi;
+            B[c] = (((prefix << 8) | static_cast<uint32_t>(255 - cand[c])) << shift_d);
+          }
+          double acc[kSelCand + 1];
+          exact_masses<LT, VEC, NT>(lrow, V, m, a.s64, klo, B, acc, sc);
+          te = a.top_p * acc[kSelCand];
+          int c1 = n;
+          for (int c = n - 1; c >= 0; --c)
+            if (acc[c] >= te) c1 = c;
+          if (c1 == n) {
+            t = min(hi + 1, kSelDigits - 1);
+            break;
+          }
+          const int prev = c1 == 0 ? lo - 1 : cand[c1 - 1];
+          if (cand[c1] - prev == 1) {
+            t = cand[c1];
+            break;
+          }
+          lo = prev + 1;
+          hi = cand[c1] - 1;
+          t = cand[c1];  // at or above the target (taken if the guard runs out)
+        }
+        // the exact Z_K replaces the fixed-point target below this level
+        tgt = te * exp2(shift);
+        tgterr = 1e-11 * tgt;
+      }
+      if (tid < 64) level_take(fs, t);
+      __syncthreads();
+      const double ma = static_cast<double>(fs.m_above) * inv, ea = static_cast<double>(fs.e_above) * inv;
+      C += ma;
+      Cerr += fixed_bound(ma, ea, quant);
+      prefix = (prefix << 8) | static_cast<uint32_t>(255 - t);
+      if (lv == kLevels - 1) {
+        const double mt = static_cast<double>(fs.m_at) * inv, et = static_cast<double>(fs.e_at) * inv;
+        Z = C + mt;
+        dZ = Cerr + fixed_bound(mt, et, quant);
+      }
+      __syncthreads();  // fs is cleared by the next level
+    }
+    kt = prefix_key(prefix, kLevels);
+  }
+  tau = key_value(kt);
+  Zt = Z;
+  dZt = dZ;
+}
+
+template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
 __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
-                                          RowShared& sh) {
+                                          RowShared& sh,
+                                          std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr) {
+  static_assert(!(EAGER && FILTER), "top-k / top-p run in the lazy mode only");
   constexpr int kWaves = NT / 64;
   using L = Lay<LT, VEC>;
   using Raw = RawTile<LT, VEC>;
@@ -1485,9 +1944,14 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   double Z, sea;
   block_sum2(zl, eal, sc, Z, sea);
   const double bt = bound_terms(Z, sea);
-  const double dZ = bt + kSumErr * Z;  // |Z~ - 2^D Z|
-  const double relZ = dZ / Z;
+  double dZ = bt + kSumErr * Z;  // |Z~ - 2^D Z|
   const double shift = static_cast<double>(cm) + static_cast<double>(m) * static_cast<double>(s);  // D, exact
+  // top-k / top-p: the threshold tau, and Z over the kept set {l >= tau}
+  float tau = -INFINITY;
+  if constexpr (FILTER) {
+    if (m != -INFINITY && Z > 0.0 && Z < INFINITY) row_threshold<LT, VEC, NT>(a, lrow, m, shift, *fsp, sc, tau, Z, dZ);
+  }
+  const double relZ = dZ / Z;
 
   // ---------------- accept test of a draft row (fp64 p(x), certified)
   if (tid == 0) {
@@ -1497,11 +1961,12 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
     uint32_t why = 0;
     double px = 0.0;
     if (is_draft) {
-      if (x_ok) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64 + shift) / Z;
+      const bool kept = x_ok && lx >= tau;  // p(x) = 0 exactly for a token outside the kept set
+      if (kept) px = exp2((static_cast<double>(lx) - static_cast<double>(m)) * a.s64 + shift) / Z;
       const double qx = onehot ? 1.0 : static_cast<double>(qx_in);
       const double lhs = static_cast<double>(u_acc) * qx;
       accepted = (x_ok && px > 0.0 && lhs <= px) ? 1 : 0;
-      if (x_ok) {
+      if (kept) {
         const double dpx = kSafety * (px * relZ * 1.01) + 1e-300;
         if (fabs(lhs - px) <= 2.0 * dpx || px < 1e-30) why |= kWhyAccept;
       }
@@ -1531,7 +1996,7 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
           z = Z * unshift;
           dz = dZ * unshift;
         }
-        a.rstat[t.trow] = make_double4(static_cast<double>(m), z, dz, 0.0);
+        a.rstat[t.trow] = make_double4(static_cast<double>(m), z, dz, static_cast<double>(tau));
       }
       a.ws[t.trow] = make_int2(-1, static_cast<int>(f));
     }
@@ -1609,11 +2074,12 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
   if (threadIdx.x == 0) a.surv_n[0] = base;
 }
 
-template <typename LT, bool VEC, int NT>
+template <typename LT, bool VEC, int NT, bool FILTER>
 __global__ __launch_bounds__(NT) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
+  __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
   const bool second = p0 > 0;
   const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, p0, p1, a.pm, flat != 0,
                                   second ? a.surv : nullptr, second ? a.surv_n[0] : 0);
@@ -1627,7 +2093,7 @@ __global__ __launch_bounds__(NT) void lazy_rows_kernel(ProbsArgs a, int p0, int 
       read = false;
     }
   }
-  if (read) probs_row<LT, VEC, NT, false>(a, t, dyn, sc, sh);
+  if (read) probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
   if (second || a.pm <= p1) return;
   // first launch: the last block to finish lists the requests the second launch
   // reads. Marks and the count are device-scope atomics, each block's mark
@@ -1731,14 +2197,6 @@ __device__ __forceinline__ void exp2_negN(const double (&a)[N], const double* __
     p = fma(p, r[k], 1.0);
     e[k] = ldexp(p * tv[k], J[k] >> 6);
   }
-}
-
-// Sum over a wave by an xor butterfly: every lane ends with the same value
-// (a + b == b + a), in a fixed association.
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
 }
 
 // Chunk c (0..3) of a lane's part of the tile at `base`: the lane's elements
@@ -1888,17 +2346,6 @@ struct RawChunk<LT, false> {
   }
 };
 
-// Inclusive scan over the 64 lanes (lane order), fixed association.
-__device__ __forceinline__ double wave_scan_incl_d(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  return v;
-}
-
 // 8 consecutive elements from k0 (a multiple of 8), as fp32 logits (-inf past
 // the end of the row) or q (0 past the end; q == nullptr: zeros, with
 // fallback[0] read instead so that the loads need no branch). Loads are
@@ -1971,11 +2418,13 @@ struct ReqShared {
 // raw chunks keeps the loads of the next three chunks in flight while one is
 // computed. Per tile it writes E_j (sum of e_k) and, for a draft row, Q_j and
 // P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
-// interval leaves an element undecided (LDS or global, indexed by tile).
-template <typename LT, bool VEC>
+// interval leaves an element undecided (LDS or global, indexed by tile). With
+// MASK, logits below tau (outside the top-k / top-p kept set) count as -inf.
+template <typename LT, bool VEC, bool MASK>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
-                              const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q) {
+                              const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
+                              float tau) {
   const int lane = threadIdx.x & 63;
   const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
   using Chunk = RawChunk<LT, VEC>;
@@ -1992,7 +2441,11 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     for (int h = 0; h < 8; h += kExpW) {
       double ar[kExpW], e[kExpW];
 #pragma unroll
-      for (int k = 0; k < kExpW; ++k) ar[k] = fma(static_cast<double>(ring[slot].template get_l<PD>(h + k, V)), s, nms);
+      for (int k = 0; k < kExpW; ++k) {
+        float l = ring[slot].template get_l<PD>(h + k, V);
+        if constexpr (MASK) l = l < tau ? -INFINITY : l;
+        ar[k] = fma(static_cast<double>(l), s, nms);
+      }
       exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
       for (int k = 0; k < kExpW; ++k) es += e[k];
@@ -2088,7 +2541,7 @@ struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the 
 // slice of the deciding row's tiles.
 // Lazy mode, per-request pass: kPassSlices blocks per request, each over a
 // slice of the deciding row's tiles.
-template <typename LT, bool VEC>
+template <typename LT, bool VEC, bool FILTER>
 __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, PassArrays pa) {
   __shared__ double tab[kExp2Tab];
   __shared__ int slot;
@@ -2111,8 +2564,8 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
   const int per = (nt + kPassSlices - 1) / kPassSlices;
   const int j0 = sl * per, j1 = min(nt, j0 + per);
   const int64_t o = static_cast<int64_t>(b) * nt;
-  fp64_row_pass<LT, VEC>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, draft, j0 + wave, j1, kPassWaves, tab, C,
-                         pa.E + o, pa.P + o, pa.Q + o);
+  fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, draft, j0 + wave, j1, kPassWaves, tab,
+                                 C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
 }
 
 // Lazy mode, per-request finish: one block per request. Z from the pass's
@@ -2120,7 +2573,7 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
 // after all, the next open row gets its fp64 pass here, in LDS); residual tile
 // sums W_j = P_j / Z - Q_j, tiles with undecided elements summed again with
 // Z; then wave 0 draws the token and writes the request's outputs.
-template <typename LT, bool VEC>
+template <typename LT, bool VEC, bool FILTER>
 __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa) {
   extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
   __shared__ BlockScratchT<kFinishNT> sc;
@@ -2159,6 +2612,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     const double4 st = a.rstat[trow];
     const double m = st.x;
     const double nms = -(m * s);
+    const float keep_min = static_cast<float>(st.w);  // top-k / top-p threshold tau (-inf: no filter)
+    auto masked = [&](float l) { return (FILTER && l < keep_min) ? -INFINITY : l; };
     const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
     const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
     if (from_pass) {
@@ -2170,7 +2625,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       }
     } else {  // a later row (an undecided accept test turned out accepted): its pass here
       const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
-      fp64_row_pass<LT, VEC>(lrow, qrow, V, nt, m, s, zhi, zlo, draft, wave, nt, kFinishWaves, tab, C, E, P, Q);
+      fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, m, s, zhi, zlo, draft, wave, nt, kFinishWaves, tab, C, E, P,
+                                     Q, keep_min);
     }
     __syncthreads();
     for (int j = tid; j < nt; j += kFinishNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
@@ -2183,7 +2639,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     if (undecided) {
       const int64_t x = a.x[d0 + n];
       const bool x_ok = x >= 0 && x < V;
-      const double px = x_ok ? exp2_neg(fma(static_cast<double>(to_float(lrow[x])), s, nms), tab) * iz : 0.0;
+      const double px =
+          x_ok ? exp2_neg(fma(static_cast<double>(masked(to_float(lrow[x]))), s, nms), tab) * iz : 0.0;
       const double qx = x_ok ? static_cast<double>(qrow[x]) : 0.0;
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
         if (tid == 0) a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags));
@@ -2216,7 +2673,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
           for (int g4 = 0; g4 < 8; g4 += kExpW) {
             double ar[kExpW], e[kExpW];
 #pragma unroll
-            for (int kk = 0; kk < kExpW; ++kk) ar[kk] = fma(static_cast<double>(lv[g4 + kk]), s, nms);
+            for (int kk = 0; kk < kExpW; ++kk) ar[kk] = fma(static_cast<double>(masked(lv[g4 + kk])), s, nms);
             exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
             for (int kk = 0; kk < kExpW; ++kk) ws += fmax(0.0, e[kk] * iz - static_cast<double>(qv[g4 + kk]));
@@ -2292,6 +2749,10 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     for (int h = 0; h < 4; ++h) {
       load8f<LT, VEC>(lrow, V, k0 + 8 * h, lall[h]);
       load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qall[h]);
+      if constexpr (FILTER) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) lall[h][k] = masked(lall[h][k]);
+      }
     }
     auto weights8 = [&](int h, double (&w8)[8]) __attribute__((always_inline)) {
       const float (&lv)[8] = lall[h];
@@ -2500,20 +2961,30 @@ constexpr int kRaggedPositionMajor = 4;  // ragged batches: positions launched p
 constexpr int kLazyFirstPositions = 2;   // lazy mode: positions of the first launch
 constexpr int kRowsNTEager = 512;
 
-template <typename LT, bool VEC, int NT, bool EAGER>
+template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
 void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
   if constexpr (EAGER) {
     hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st, a);
   } else {
     // positions [0, 2), then the rest (with the flat order for ragged batches)
     const int split = min(kLazyFirstPositions, a.pm);
-    hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT), lds, st,
-                       a, 0, split, 0);
+    hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
+                       lds, st, a, 0, split, 0);
     const int64_t rest = static_cast<int64_t>(a.B) * (a.pm - split) + (a.cu ? rows : 0);
     if (rest > 0)
-      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st, a,
-                         split, a.pm, 1);
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st,
+                         a, split, a.pm, 1);
   }
+}
+
+// The per-request stage of the lazy mode: the fp64 pass (kPassSlices blocks
+// per request), then one block per request decides it and writes the outputs.
+template <typename LT, bool VEC, bool FILTER>
+void launch_request(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2, hipStream_t st) {
+  hipLaunchKernelGGL((request_pass_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
+                     dim3(kPassNT), 0, st, a, pa);
+  hipLaunchKernelGGL((request_finish_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
+                     st, a, sel, pa);
 }
 
 // Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
@@ -2539,31 +3010,28 @@ int launch_probs(const ProbsArgs& a, const ExactArgs& e, const SelectArgs& sel, 
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0 &&
                    (a.q == nullptr || (aligned16(a.q) && (a.V % 4) == 0));
   const bool lazy = (a.flags & kFlagLazy) != 0;
+  const bool filter = (a.flags & kFlagFilter) != 0;
   prof_record(SV_PROFILE_ROWS, 0, st);
   if (vec) {
-    if (lazy) launch_rows<LT, true, kRowsNTLazy, false>(a, rows, lds, st);
+    if (filter) launch_rows<LT, true, kRowsNTLazy, false, true>(a, rows, lds, st);
+    else if (lazy) launch_rows<LT, true, kRowsNTLazy, false>(a, rows, lds, st);
     else launch_rows<LT, true, kRowsNTEager, true>(a, rows, lds, st);
   } else {
-    if (lazy) launch_rows<LT, false, kRowsNTLazy, false>(a, rows, lds, st);
+    if (filter) launch_rows<LT, false, kRowsNTLazy, false, true>(a, rows, lds, st);
+    else if (lazy) launch_rows<LT, false, kRowsNTLazy, false>(a, rows, lds, st);
     else launch_rows<LT, false, kRowsNTEager, true>(a, rows, lds, st);
   }
   prof_record(SV_PROFILE_ROWS, 1, st);
   if (lazy) {
-    // the per-request fp64 pass (four blocks per request), then one block per
-    // request decides it and writes the outputs
     const size_t lds2 = static_cast<size_t>(nt) * (4 * sizeof(double) + sizeof(int));
     const PassArrays pa{e.etile, e.ptile, e.qtile};
     prof_record(SV_PROFILE_REQUEST, 0, st);
     if (vec) {
-      hipLaunchKernelGGL((request_pass_kernel<LT, true>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
-                         dim3(kPassNT), 0, st, a, pa);
-      hipLaunchKernelGGL((request_finish_kernel<LT, true>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
-                         st, a, sel, pa);
+      if (filter) launch_request<LT, true, true>(a, sel, pa, lds2, st);
+      else launch_request<LT, true, false>(a, sel, pa, lds2, st);
     } else {
-      hipLaunchKernelGGL((request_pass_kernel<LT, false>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
-                         dim3(kPassNT), 0, st, a, pa);
-      hipLaunchKernelGGL((request_finish_kernel<LT, false>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
-                         st, a, sel, pa);
+      if (filter) launch_request<LT, false, true>(a, sel, pa, lds2, st);
+      else launch_request<LT, false, false>(a, sel, pa, lds2, st);
     }
     prof_record(SV_PROFILE_REQUEST, 1, st);
     return 0;
@@ -2586,14 +3054,22 @@ int launch_greedy(const GreedyArgs& a, int64_t rows, hipStream_t st) {
 int finish_launch() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH; }
 
 // Shared implementation of the three entry points.
+// Filter settings of the *_filtered entry points (filtered = false: none).
+struct FilterArgs {
+  bool filtered = false;
+  int32_t top_k = 0;
+  double top_p = 1.0;
+};
+
 int verify_common(const void* logits, int dtype, const float* q, const int64_t* x, const int32_t* cu,
                   const float* u, int32_t B, int32_t gamma, int32_t ndraft, int32_t V, double T, uint32_t flags,
                   int64_t* out, int32_t* nacc, float* stats, void* ws, size_t ws_size, void* stream,
-                  bool greedy_only) {
+                  bool greedy_only, FilterArgs fa = FilterArgs{}) {
   if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_UNSUPPORTED;
   if (B < 0 || gamma < 0 || ndraft < 0 || V < 1) return SV_ERR_INVALID_ARGUMENT;
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!(T >= 0.0) || !isfinite(T)) return SV_ERR_INVALID_ARGUMENT;
+  if (fa.filtered && (!(T > 0.0) || !(fa.top_p > 0.0 && fa.top_p <= 1.0))) return SV_ERR_INVALID_ARGUMENT;
   if (flags & ~static_cast<uint32_t>(SV_FLAG_EXACT | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EAGER))
     return SV_ERR_INVALID_ARGUMENT;
   if (stats && !(T > 0.0)) return SV_ERR_INVALID_ARGUMENT;
@@ -2604,6 +3080,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
   if (!logits || !out || !nacc) return SV_ERR_INVALID_ARGUMENT;
   if (ndraft > 0 && !x) return SV_ERR_INVALID_ARGUMENT;
   if (!greedy_only && T > 0.0 && !u) return SV_ERR_INVALID_ARGUMENT;
+  if (fa.filtered && !q) return SV_ERR_INVALID_ARGUMENT;
   const bool greedy = greedy_only || T == 0.0;
   const WsLayout wl = ws_layout(rows, V);
   if (!ws || ws_size < (greedy ? ws_bytes(rows) : wl.total) || (reinterpret_cast<uintptr_t>(ws) & 255u))
@@ -2638,7 +3115,10 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     // lazy (default): with q, no statistics, and not every row forced through the fp64 path
     const bool lazy =
         !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EXACT)) && stats == nullptr && q != nullptr;
-    p.flags = flags | (lazy ? kFlagLazy : 0u);
+    const bool filter = fa.filtered && ((fa.top_k > 0 && fa.top_k < V) || fa.top_p < 1.0);
+    p.flags = flags | (lazy ? kFlagLazy : 0u) | (filter ? kFlagFilter : 0u);
+    p.top_k = filter ? fa.top_k : 0;
+    p.top_p = filter ? fa.top_p : 1.0;
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.mark = reinterpret_cast<int*>(wsb + wl.mark);
     p.surv = reinterpret_cast<int*>(wsb + wl.surv);
@@ -2690,7 +3170,7 @@ const char* spec_verify_status_string(int status) {
   }
 }
 
-int spec_verify_version(void) { return 1; }
+int spec_verify_version(void) { return 2; }
 
 double spec_verify_exp2_error_bound(void) { return kEpsExp; }
 
@@ -2789,6 +3269,39 @@ int spec_verify_ragged(const void* target_logits, int logits_dtype, const float*
   return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms,
                        num_requests, 0, num_draft_tokens, vocab_size, temperature, flags, out_tokens, num_accepted,
                        row_stats, workspace, workspace_bytes, stream, false);
+}
+
+int spec_verify_probs_filtered(const void* target_logits, int logits_dtype, const float* draft_probs,
+                               const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
+                               int32_t gamma, int32_t vocab_size, double temperature, int32_t top_k, double top_p,
+                               int64_t* out_tokens, int32_t* num_accepted, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (num_requests < 0 || gamma < 0) return SV_ERR_INVALID_ARGUMENT;
+  const int64_t nd = static_cast<int64_t>(num_requests) * gamma;
+  if (nd > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+  FilterArgs fa;
+  fa.filtered = true;
+  fa.top_k = top_k;
+  fa.top_p = top_p;
+  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, nullptr, uniforms, num_requests,
+                       gamma, static_cast<int32_t>(nd), vocab_size, temperature, 0u, out_tokens, num_accepted,
+                       nullptr, workspace, workspace_bytes, stream, false, fa);
+}
+
+int spec_verify_ragged_filtered(const void* target_logits, int logits_dtype, const float* draft_probs,
+                                const int64_t* draft_tokens, const int32_t* cu_num_draft_tokens,
+                                const float* uniforms, int32_t num_requests, int32_t num_draft_tokens,
+                                int32_t vocab_size, double temperature, int32_t top_k, double top_p,
+                                int64_t* out_tokens, int32_t* num_accepted, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (num_requests > 0 && !cu_num_draft_tokens) return SV_ERR_INVALID_ARGUMENT;
+  FilterArgs fa;
+  fa.filtered = true;
+  fa.top_k = top_k;
+  fa.top_p = top_p;
+  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, cu_num_draft_tokens, uniforms,
+                       num_requests, 0, num_draft_tokens, vocab_size, temperature, 0u, out_tokens, num_accepted,
+                       nullptr, workspace, workspace_bytes, stream, false, fa);
 }
 
 }  // extern "C"

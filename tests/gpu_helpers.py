@@ -7,7 +7,9 @@ verifier's target states - an accept flip is tolerated when |u - p(x)/q(x)|
 <= 1e-6, a sampled-token flip when the uniform lies within 1e-6 of a CDF
 boundary of the oracle's (normalised) sampling distribution - and such
 tolerated flips must stay below 1e-4 of the rows checked; anything else is a
-hard failure. Row statistics: max(l/T) within 1e-6 relative, ln Z within
+hard failure. With top-k / top-p (`filt` = (top_k, top_p)) the oracle's
+target rows are its adjusted distributions and the same rule applies. Row
+statistics: max(l/T) within 1e-6 relative, ln Z within
 1e-5 absolute (Z within 1e-5 relative), p(x) within 1e-5 relative (floor
 1e-30), R within 1e-5 relative plus 2e-6 absolute.
 """
@@ -58,6 +60,29 @@ def run_gpu(w, flags=0, stats=False, t=None):
     return (out.cpu().numpy(), nacc.cpu().numpy(), None if st is None else st.cpu().numpy(), rec)
 
 
+def run_gpu_filtered(w, top_k, top_p, t=None):
+    """Run the filtered HIP path; returns numpy (out, nacc, None, records)."""
+    t = t or dev_inputs(w)
+    if w["kind"] == "ragged":
+        out, nacc, ws = api.verify_ragged_filtered(t["logits"], t["q"], t["x"], t["cu"], t["u"], w["temperature"],
+                                                   top_k, top_p)
+    else:
+        out, nacc, ws = api.verify_probs_filtered(t["logits"], t["q"], t["x"], t["u"], w["temperature"], top_k,
+                                                  top_p)
+    torch.cuda.synchronize()
+    rec = api.row_records(ws, out.numel()).cpu().numpy()
+    return out.cpu().numpy(), nacc.cpu().numpy(), None, rec
+
+
+def target_rows(l, T, filt=None, rows=None):
+    """The oracle's target distributions of the rows of l (adjusted by top-k /
+    top-p when filt = (top_k, top_p))."""
+    rows = range(len(l)) if rows is None else rows
+    if filt is None:
+        return [oracle.target_probs(l[i], T) for i in rows]
+    return [oracle.adjusted_target_probs(l[i], T, filt[0], filt[1]) for i in rows]
+
+
 def request_view(w, b):
     """(logits rows [g+1, V], q rows [g, V] or None, x [g], u [g+1], slice of target rows)."""
     if w["kind"] == "ragged":
@@ -71,7 +96,7 @@ def request_view(w, b):
     return w["logits"][b], q, w["draft_tokens"][b], w["uniforms"][b], b
 
 
-def oracle_request(w, b, stats=False):
+def oracle_request(w, b, stats=False, filt=None):
     l, q, x, u, _ = request_view(w, b)
     T = w["temperature"]
     g = len(x)
@@ -79,7 +104,7 @@ def oracle_request(w, b, stats=False):
         r_out, r_n = oracle.verify_greedy(l[None], np.asarray(x)[None])
         toks = [int(v) for v in r_out[0][: r_n[0] + 1]]
         return toks, int(r_n[0]), None
-    p_rows = [oracle.target_probs(l[i], T) for i in range(g + 1)]
+    p_rows = target_rows(l, T, filt, range(g + 1))
     toks, n = oracle.verify_request(p_rows, None if q is None else [q[i] for i in range(g)], x, u)
     st = None
     if stats:
@@ -88,12 +113,12 @@ def oracle_request(w, b, stats=False):
     return toks, n, st
 
 
-def _flip_tolerated(w, b, gpu_toks, gpu_n, ref_toks, ref_n):
+def _flip_tolerated(w, b, gpu_toks, gpu_n, ref_toks, ref_n, filt=None):
     """Classify one mismatching request; returns True for a tolerated flip."""
     l, q, x, u, _ = request_view(w, b)
     T = w["temperature"]
     g = len(x)
-    p_rows = [oracle.target_probs(l[i], T) for i in range(g + 1)]
+    p_rows = target_rows(l, T, filt, range(g + 1))
     if gpu_n != ref_n:
         i = min(gpu_n, ref_n)  # first position whose decision differs
         qx = 1.0 if q is None else float(q[i][int(x[i])])
@@ -116,7 +141,7 @@ def _flip_tolerated(w, b, gpu_toks, gpu_n, ref_toks, ref_n):
     return (lo - 1e-6) < us <= c[gt] + 1e-6
 
 
-def compare(w, gpu, reqs=None, stats=False, label=""):
+def compare(w, gpu, reqs=None, stats=False, label="", filt=None):
     """Compare GPU results with the oracle on requests `reqs` (all if None)."""
     out, nacc, gst, _ = gpu
     reqs = range(w["B"]) if reqs is None else reqs
@@ -125,7 +150,7 @@ def compare(w, gpu, reqs=None, stats=False, label=""):
         l, q, x, u, sl = request_view(w, b)
         g = len(x)
         rows += g + 1
-        ref_toks, ref_n, rst = oracle_request(w, b, stats)
+        ref_toks, ref_n, rst = oracle_request(w, b, stats, filt)
         go = out[sl] if w["kind"] == "ragged" else out[b]
         gn = int(nacc[b])
         gtoks = [int(v) for v in go[: gn + 1]]
@@ -133,7 +158,7 @@ def compare(w, gpu, reqs=None, stats=False, label=""):
         if not pad_ok:
             hard.append((b, "padding", go.tolist()))
         if gtoks != ref_toks or gn != ref_n:
-            if _flip_tolerated(w, b, gtoks, gn, ref_toks, ref_n):
+            if _flip_tolerated(w, b, gtoks, gn, ref_toks, ref_n, filt):
                 flips += 1
             else:
                 hard.append((b, gtoks, ref_toks, gn, ref_n))

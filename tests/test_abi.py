@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert sorted(declared_functions()) == sorted(api.EXPORTS)
-    assert lib.spec_verify_version() == 1
+    assert lib.spec_verify_version() == 2
 
 
 def test_status_strings(lib):
@@ -110,6 +110,43 @@ def test_greedy_and_ragged_validation(lib):
     assert r(FAKE, 1, FAKE, FAKE, None, FAKE, 2, 5, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
     assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, -1, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
     assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, 100, 1.0, 0, FAKE, FAKE, None, FAKE, 0, None) == 0
+
+
+def filtered(lib, **kw):
+    a = dict(logits=FAKE, dtype=1, q=FAKE, x=FAKE, u=FAKE, B=2, g=3, V=100, T=1.0, k=10, p=0.9, out=FAKE, nacc=FAKE,
+             ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.spec_verify_probs_filtered(a["logits"], a["dtype"], a["q"], a["x"], a["u"], a["B"], a["g"], a["V"],
+                                          a["T"], a["k"], a["p"], a["out"], a["nacc"], a["ws"], a["wsb"],
+                                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0.0), -1),          # greedy verification takes no filters
+    (dict(T=-1.0), -1),
+    (dict(p=0.0), -1),
+    (dict(p=-0.5), -1),
+    (dict(p=1.5), -1),
+    (dict(p=float("nan")), -1),
+    (dict(q=None), -1),         # the filters need q (already adjusted by the drafter)
+    (dict(u=None), -1),
+    (dict(V=0), -1),
+    (dict(dtype=5), -2),
+    (dict(ws=None), -4),
+    (dict(wsb=3071), -4),
+    (dict(B=0), 0),
+    (dict(B=0, k=-3, p=1.0), 0),
+])
+def test_filtered_argument_validation(lib, kw, status):
+    assert filtered(lib, **kw) == status
+
+
+def test_ragged_filtered_validation(lib):
+    r = lib.spec_verify_ragged_filtered
+    assert r(FAKE, 1, FAKE, FAKE, None, FAKE, 2, 5, 100, 1.0, 5, 0.9, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 5, 100, 1.0, 5, 0.0, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert r(FAKE, 1, None, FAKE, FAKE, FAKE, 2, 5, 100, 1.0, 5, 0.9, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, 100, 1.0, 5, 0.9, FAKE, FAKE, FAKE, 0, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
