@@ -135,6 +135,32 @@ def measure_loop(steps: int, dev):
                     "the verifier through the C ABI"}
 
 
+def measure_filtered(steps, logits, q, x, u, T, ws, stream, top_k=50, top_p=0.9):
+    """The same batch through spec_verify_probs_filtered (top-k then top-p on
+    the target): wall time per call and the per-row pass's event time."""
+    import torch
+
+    from rejection_sampling_verifier_spec_amd import api
+
+    def call():
+        return api.verify_probs_filtered(logits, q, x, u, T, top_k, top_p, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    api.profile_start((api.SV_PROFILE_ROWS,), capacity=steps)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out, nacc, _ = call()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    rows_ms, rows_n = api.profile_stop()[api.SV_PROFILE_ROWS]
+    B, g = x.shape
+    return {"top_k": top_k, "top_p": top_p, "steps": steps, "ms_per_call": wall * 1e3,
+            "positions_per_s": B * g / wall, "per_row_pass_ms_mean": rows_ms / max(rows_n, 1),
+            "mean_accepted": float(nacc.float().mean().item())}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +170,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="SV_FLAG_* bits passed to the library (0: lazy residuals, 4: eager, 2: all residuals)")
     ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
+    ap.add_argument("--filtered-steps", type=int, default=30,
+                    help="calls of the top-k / top-p entry point timed after the timed region (0: skip)")
     ap.add_argument("--loop-steps", type=int, default=30,
                     help="steps of the synthetic end-to-end loop measured after the timed region (0: skip)")
     args = ap.parse_args()
@@ -270,6 +298,8 @@ def main():
         "method_minimum_GBps_equiv": needed_bytes / call_s / 1e9,
         "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
     }
+    if args.filtered_steps > 0 and q is not None and T > 0:
+        result["filtered"] = measure_filtered(args.filtered_steps, logits, q, x, u, T, ws, stream)
     if args.loop_steps > 0:
         result["loop"] = measure_loop(args.loop_steps, dev)
     if args.cpu_requests > 0 and q is not None:

@@ -1379,11 +1379,33 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
 
 constexpr int kSelDigits = 256;
 constexpr int kSelCand = 8;  // digit boundaries per fp64 sweep
+constexpr int kHeadCap = 4096;  // elements of the gathered head (see head_threshold)
+// Cutoffs of the gathered head: pass 1 gathers {l >= ref - kHeadH1 / s}
+// (ref the block maximum of the first tiles); a head gathered by its own
+// sweeps takes the lowest cutoff m - kCutLadder[i] / s (e >= 2^-H relative to
+// the row max) whose elements fit the buffer.
+constexpr float kHeadH1 = 16.f;
+constexpr int kHeadFix = 50;  // fraction bits of the head masses: kHeadCap terms <= 1 stay below 2^63
+constexpr int kCutLadderLen = 8;
+__constant__ float kCutLadder[kCutLadderLen] = {64.f, 40.f, 28.f, 20.f, 14.f, 9.f, 5.f, 0.f};
 
 struct FilterShared {
-  unsigned long long mass[kSelDigits];  // per digit: fixed-point sum of e
-  unsigned long long mea[kSelDigits];   // per digit: fixed-point sum of e |a|
-  uint32_t cnt[kSelDigits];             // per digit: elements
+  union {
+    struct {
+      unsigned long long mass[kSelDigits];  // radix select, per digit: fixed-point sum of e
+      unsigned long long mea[kSelDigits];   // per digit: fixed-point sum of e |a|
+      uint32_t cnt[kSelDigits];             // per digit: elements
+    };
+    uint32_t head2[kHeadCap];  // head gather: compaction buffer
+  };
+  uint32_t head[kHeadCap];              // keys of the head elements
+  unsigned long long hfix[kHeadCap];    // their masses 2^((l - m) s64) as fixed point (kHeadFix bits)
+  int wcnt[16];                         // per-wave counts
+  float cut1;                           // pass 1's head cutoff
+  int ik, ip;                           // head indices: end of tau_k's tie group, top-p crossing
+  int amb;                              // top-p: first tie-group end within the bound of the target
+  double zk;                            // exact Z_K (head sum) when top-k is on
+  double zt;                            // exact mass at the crossing
   int pos;                              // chosen position of the level (digit 255 - pos), -1: undecided
   int amb_lo, amb_hi;                   // undecided positions (pos == -1)
   uint32_t above;                       // top-k: elements above the chosen digit
@@ -1423,7 +1445,9 @@ __device__ __forceinline__ double fixed_bound(double M, double EA, double quant)
 }
 
 // Calls f(v) for every element of the row: wave w visits tiles w, w + waves,
-// ..., with the next tile's loads in flight while one is visited.
+// ... Used by the rare paths of the threshold (radix select, fp64 sweeps):
+// one tile in flight and a partly unrolled visit keep their registers below
+// those of pass 1, so that they do not set the kernel's occupancy.
 template <typename LT, bool VEC, int NT, typename Fn>
 __device__ __forceinline__ void sweep_row(const LT* __restrict__ lrow, int V, Fn&& f) {
   constexpr int kW = NT / 64;
@@ -1431,26 +1455,14 @@ __device__ __forceinline__ void sweep_row(const LT* __restrict__ lrow, int V, Fn
   using Raw = RawTile<LT, VEC>;
   const int lane = threadIdx.x & 63;
   const int nt = (V + kTile - 1) / kTile;
-  int j = threadIdx.x >> 6;
-  if (j >= nt) return;
-  Raw ra, rb;
-  ra.load(lrow, V, j * kTile, lane);
-  auto visit = [&](const Raw& r, int jj) {
-    const int base = jj * kTile;
+  for (int j = threadIdx.x >> 6; j < nt; j += kW) {
+    Raw r;
+    r.load(lrow, V, j * kTile, lane);
+    const int base = j * kTile;
     const bool full = base + kTile <= V;
-#pragma unroll
+#pragma unroll 4
     for (int k = 0; k < kLaneElems; ++k)
       if (full || L::index(base, lane, k) < V) f(r.get(k));
-  };
-  while (true) {
-    rb.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
-    visit(ra, j);
-    j += kW;
-    if (j >= nt) break;
-    ra.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
-    visit(rb, j);
-    j += kW;
-    if (j >= nt) break;
   }
 }
 
@@ -1631,6 +1643,350 @@ __device__ void exact_masses(const LT* __restrict__ lrow, int V, float m, double
 __device__ __forceinline__ uint32_t prefix_key(uint32_t prefix, int levels) {
   if (levels == 4) return prefix;
   return (prefix << 16) | ((prefix & 0x8000u) ? 0u : 0xffffu);
+}
+
+// Append inside pass 1: each wave fills its own slice of the head buffer
+// (`slice` entries from `dst`), counting in `cnt` (wave-uniform), one element
+// slot at a time with a ballot: no atomics. cnt counts every element offered;
+// cnt > slice after the sweep means the slice overflowed.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void head_append_wave(const RawTile<LT, VEC>& r, int base, int V, int lane, float c,
+                                                 uint32_t* dst, int slice, int& cnt) {
+  using L = Lay<LT, VEC>;
+  const bool full = base + kTile <= V;
+#pragma unroll
+  for (int g = 0; g < kLaneElems; g += 8) {  // groups of 8 slots, skipped when no lane has a candidate
+    float gm = r.get(g);
+#pragma unroll
+    for (int k = g + 1; k < g + 8; ++k) gm = fmaxf(gm, r.get(k));
+    if (!__any(gm >= c)) continue;
+#pragma unroll
+    for (int k = g; k < g + 8; ++k) {
+      const float v = r.get(k);
+      const bool in = (full || L::index(base, lane, k) < V) && v >= c;
+      const uint64_t mk = __ballot(in);
+      if (mk) {
+        const int at = cnt + static_cast<int>(__popcll(mk & ((1ull << lane) - 1)));
+        if (in && at < slice) dst[at] = order_key(v);
+        cnt += static_cast<int>(__popcll(mk));
+      }
+    }
+  }
+}
+
+// The per-wave slices of the head buffer (counts in fs.wcnt) made
+// contiguous through head2; returns the head size, or kHeadCap + 1 when some
+// slice overflowed (its count above the slice). Called by every thread.
+template <int NT>
+__device__ int compact_slices(FilterShared& fs) {
+  constexpr int kW = NT / 64;
+  constexpr int kSlice = kHeadCap / kW;
+  int n = 0, off = 0;
+  bool over = false;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int c = fs.wcnt[w];
+    over = over || c > kSlice;
+    if (w < wave) off += c;
+    n += c;
+  }
+  if (over) {
+    __syncthreads();
+    return kHeadCap + 1;
+  }
+  const int mine = fs.wcnt[wave];
+  for (int i = threadIdx.x & 63; i < mine; i += 64) fs.head2[off + i] = fs.head[wave * kSlice + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += NT) fs.head[i] = fs.head2[i];
+  __syncthreads();
+  return n;
+}
+
+// A head gathered by its own two sweeps, after pass 1 (m known): the first
+// counts, per wave, the elements at or above each of the kCutLadderLen
+// cutoffs m - kCutLadder[i] / s (registers only); the lowest cutoff whose
+// per-wave counts all fit a wave's slice of the buffer is taken, and the
+// second sweep appends the elements at or above it to the per-wave slices,
+// which are then made contiguous. Returns the head size, or -1 if no cutoff
+// fits (even the row max's tie group overflows a slice). min_cut: a cutoff
+// at or above it gains nothing (-1 is returned too).
+template <typename LT, bool VEC, int NT>
+__device__ int gather_head(const LT* __restrict__ lrow, int V, float m, float s, float min_cut, FilterShared& fs) {
+  constexpr int kW = NT / 64;
+  constexpr int kSlice = kHeadCap / kW;
+  using L = Lay<LT, VEC>;
+  using Raw = RawTile<LT, VEC>;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nt = (V + kTile - 1) / kTile;
+  float cuts[kCutLadderLen];
+#pragma unroll
+  for (int i = 0; i < kCutLadderLen; ++i) cuts[i] = m - kCutLadder[i] / s;
+  // ---- counts per cutoff (the ladder is increasing in cutoff)
+  int cnt[kCutLadderLen];
+#pragma unroll
+  for (int i = 0; i < kCutLadderLen; ++i) cnt[i] = 0;
+  {
+    Raw ra, rb;
+    int j = wave;
+    auto tally = [&](const Raw& r, int jj) {
+      const int base = jj * kTile;
+      const bool full = base + kTile <= V;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) {
+        const float v = r.get(k);
+        const bool in = full || L::index(base, lane, k) < V;
+#pragma unroll
+        for (int i = 0; i < kCutLadderLen; ++i) cnt[i] += (in && v >= cuts[i]) ? 1 : 0;
+      }
+    };
+    if (j < nt) {
+      ra.load(lrow, V, j * kTile, lane);
+      while (true) {
+        rb.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+        tally(ra, j);
+        j += kW;
+        if (j >= nt) break;
+        ra.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+        tally(rb, j);
+        j += kW;
+        if (j >= nt) break;
+      }
+    }
+  }
+  // the lowest cutoff whose count fits in every wave's slice
+  int ok_from = kCutLadderLen;  // first ladder index that fits this wave
+#pragma unroll
+  for (int i = kCutLadderLen - 1; i >= 0; --i) {
+    int c = cnt[i];
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (c <= kSlice && ok_from == i + 1) ok_from = i;
+  }
+  if (lane == 0) fs.wcnt[wave] = ok_from;
+  __syncthreads();
+  int li = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) li = max(li, fs.wcnt[w]);
+  __syncthreads();
+  if (li >= kCutLadderLen) return -1;
+  const float cut = m - kCutLadder[li] / s;
+  if (cut >= min_cut) return -1;
+  // ---- gather into the per-wave slices
+  int hc = 0;
+  {
+    Raw ra, rb;
+    int j = wave;
+    uint32_t* dst = fs.head + wave * kSlice;
+    if (j < nt) {
+      ra.load(lrow, V, j * kTile, lane);
+      while (true) {
+        rb.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+        head_append_wave<LT, VEC>(ra, j * kTile, V, lane, cut, dst, kSlice, hc);
+        j += kW;
+        if (j >= nt) break;
+        ra.load(lrow, V, min(j + kW, nt - 1) * kTile, lane);
+        head_append_wave<LT, VEC>(rb, j * kTile, V, lane, cut, dst, kSlice, hc);
+        j += kW;
+        if (j >= nt) break;
+      }
+    }
+  }
+  if (lane == 0) fs.wcnt[wave] = hc;
+  __syncthreads();
+  return compact_slices<NT>(fs);
+}
+
+// floor(x 2^F) for 0 <= x < 2^(63 - F), x in fp64.
+__device__ __forceinline__ unsigned long long to_fixed64(double x, int F) {
+  const double y = ldexp(x, F);
+  const uint32_t hi = static_cast<uint32_t>(y * 0x1p-32);
+  const uint32_t lo = static_cast<uint32_t>(fma(static_cast<double>(hi), -4294967296.0, y));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Histograms over the head's keys (LDS) at one level of the select: counts,
+// and with `masses` the fixed-point masses, of the elements with key >= klo
+// whose key starts with `prefix` (lv digits).
+template <int NT>
+__device__ void head_hist(FilterShared& fs, int n, int lv, uint32_t prefix, uint32_t klo, bool masses) {
+  const int tid = threadIdx.x;
+  const int shift_d = 24 - 8 * lv, hs = shift_d + 8;
+  for (int d = tid; d < kSelDigits; d += NT) {
+    fs.cnt[d] = 0u;
+    fs.mass[d] = 0ull;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t key = fs.head[i];
+    if (key >= klo && (hs >= 32 || (key >> hs) == prefix)) {
+      const uint32_t d = (key >> shift_d) & 255u;
+      atomicAdd(&fs.cnt[d], 1u);
+      if (masses) atomicAdd(&fs.mass[d], fs.hfix[i]);
+    }
+  }
+  __syncthreads();
+}
+
+// Wave 0: top-p at one level over exact (fixed-point) masses. Position t is
+// at or above the target when C + cum(t) >= thi and below it when
+// C + cum(t) < tlo (thi == tlo when Z_K is exact); the crossing is the first
+// position at or above, unless a position in between is undecided
+// (pos = -1). Values in units of 2^-kHeadFix.
+__device__ void pick_head_mass(FilterShared& fs, double C, double tlo, double thi) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long mv[4], ls = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mv[r] = fs.mass[255 - 4 * lane - r];
+    ls += mv[r];
+  }
+  unsigned long long im = ls;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(im, o);
+    if (lane >= o) im += y;
+  }
+  unsigned long long cm = im - ls;
+  int hat = 256, und = 256;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    cm += mv[r];
+    const double v = C + static_cast<double>(cm);
+    const int t = 4 * lane + r;
+    if (v >= thi) hat = min(hat, t);
+    else if (v >= tlo) und = min(und, t);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    hat = min(hat, __shfl_xor(hat, o));
+    und = min(und, __shfl_xor(und, o));
+  }
+  if (lane == 0) fs.pos = (und < hat || hat >= 256) ? -1 : hat;
+}
+
+// Decides the thresholds from a gathered head of n elements, {l >= c} for
+// some cutoff c. Every element >= c is in the head, so the mass at or above
+// any head value is a sum over the head: each element's mass 2^((l - m) s64)
+// is computed once in fp64 and kept as a 64-bit fixed-point integer, so that
+// sums in any order are equal (to n 2^-kHeadFix, below 4e-12 of the row max's
+// mass). tau_k and tau_p come out of a radix select over the head's keys (as
+// the row select, but in LDS). top-k needs k <= n; top-p needs its crossing
+// in the head (with top-k off, Z_K is the whole row's Z: pass 1's certified
+// value, or an fp64 sweep when the bound cannot decide). Returns false when
+// the head cannot decide. Called by every thread; the result is uniform.
+template <typename LT, bool VEC, int NT>
+__device__ bool decide_head(const ProbsArgs& a, const LT* __restrict__ lrow, float m, double shift, double Zp,
+                            double dZp, int n, FilterShared& fs, BlockScratchT<NT>& sc, float& tau, double& Zt,
+                            double& dZt) {
+  constexpr int kLevels = sizeof(LT) == 2 ? 2 : 4;
+  const int V = a.V, tid = threadIdx.x;
+  const bool use_k = a.top_k > 0 && a.top_k < V;
+  const bool use_p = a.top_p < 1.0;
+  if (n < 1 || n > kHeadCap || (use_k && a.top_k > n)) return false;
+  const double md = static_cast<double>(m);
+  for (int i = tid; i < n; i += NT)
+    fs.hfix[i] = to_fixed64(exp2((static_cast<double>(key_value(fs.head[i])) - md) * a.s64), kHeadFix);
+  __syncthreads();
+  // ---- top-k: counts
+  uint32_t klo = 0;
+  if (use_k) {
+    uint32_t prefix = 0, kk = static_cast<uint32_t>(a.top_k);
+    for (int lv = 0; lv < kLevels; ++lv) {
+      if (tid == 0) {
+        fs.pos = kSelDigits - 1;
+        fs.above = 0u;
+      }
+      head_hist<NT>(fs, n, lv, prefix, 0u, false);
+      if (tid < 64) pick_count(fs, kk);
+      __syncthreads();
+      kk -= fs.above;
+      prefix = (prefix << 8) | static_cast<uint32_t>(255 - fs.pos);
+      __syncthreads();
+    }
+    klo = prefix_key(prefix, kLevels);
+  }
+  // ---- Z_K over the head (exact when top-k is on or the head is the whole row)
+  unsigned long long zpart = 0;
+  for (int i = tid; i < n; i += NT)
+    if (fs.head[i] >= klo) zpart += fs.hfix[i];
+  for (int o = 32; o > 0; o >>= 1) zpart += __shfl_xor(zpart, o);
+  if ((tid & 63) == 0) fs.m_at = 0;
+  __syncthreads();
+  if ((tid & 63) == 0) atomicAdd(&fs.m_at, zpart);
+  __syncthreads();
+  const double zhead = static_cast<double>(fs.m_at);  // units of 2^-kHeadFix
+  __syncthreads();
+  const double scale = ldexp(1.0, kHeadFix);
+  const double unshift = exp2(-shift);  // 2^-D: pass 1's units to fp64 units
+  bool zexact = use_k || n == V;
+  double zk = zexact ? zhead : Zp * unshift * scale;
+  double dzk = zexact ? 0.0 : dZp * unshift * scale * 1.01;
+  double z_tau = zhead;  // Z_tau (top-k alone: Z_K)
+  uint32_t kt = klo;
+  if (use_p) {
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      const double qerr = static_cast<double>(n) + 1.0;  // flooring of the terms, in units of 2^-kHeadFix
+      const double thi = a.top_p * (zk + dzk) + qerr, tlo = a.top_p * (zk - dzk) - qerr;
+      const double texact = a.top_p * zk;
+      uint32_t prefix = 0;
+      double C = 0.0;
+      bool undecided = false;
+      for (int lv = 0; lv < kLevels; ++lv) {
+        head_hist<NT>(fs, n, lv, prefix, klo, true);
+        if (tid < 64) pick_head_mass(fs, C, zexact ? texact : tlo, zexact ? texact : thi);
+        __syncthreads();
+        const int t = fs.pos;
+        if (t < 0) {
+          undecided = true;
+          break;
+        }
+        if (tid < 64) level_take(fs, t);
+        __syncthreads();
+        C += static_cast<double>(fs.m_above);
+        prefix = (prefix << 8) | static_cast<uint32_t>(255 - t);
+        if (lv == kLevels - 1) z_tau = C + static_cast<double>(fs.m_at);
+        __syncthreads();
+      }
+      if (!undecided) {
+        kt = prefix_key(prefix, kLevels);
+        break;
+      }
+      // undecided: either the crossing lies below the head, or Z_K is not
+      // known well enough
+      if (zexact || attempt == 1) return false;
+      if (!(zhead >= tlo)) return false;  // (cannot reach even the lowest target)
+      uint32_t B[kSelCand];
+#pragma unroll
+      for (int cc = 0; cc < kSelCand; ++cc) B[cc] = 0xffffffffu;
+      double acc[kSelCand + 1];
+      exact_masses<LT, VEC, NT>(lrow, V, m, a.s64, 0u, B, acc, sc);
+      zk = acc[kSelCand] * scale;
+      dzk = 0.0;
+      zexact = true;
+    }
+  }
+  tau = key_value(kt);
+  Zt = z_tau / scale / unshift;  // back to pass 1's units
+  dZt = Zt * 4e-12 + static_cast<double>(n + 1) / scale / unshift;
+  return true;
+}
+
+// Fast path of the threshold, in two tiers: the head pass 1 gathered (cutoff
+// ref - kHeadH1 / s, ref the block maximum of the first tiles, n1 elements
+// offered), then, if that head overflowed or cannot decide, a head gathered
+// by its own sweep from a much lower cutoff. Returns false when neither
+// decides (the radix select then runs).
+template <typename LT, bool VEC, int NT>
+__device__ bool head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, float m, double shift, double Zp,
+                               double dZp, FilterShared& fs, BlockScratchT<NT>& sc, float& tau, double& Zt,
+                               double& dZt) {
+  const int n1 = compact_slices<NT>(fs);  // pass 1's slices (> kHeadCap: one overflowed)
+  if (n1 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n1, fs, sc, tau, Zt, dZt)) return true;
+  // a head of its own: below pass 1's cutoff when that head was too small
+  // (the crossing or the k-th element lay below it), above it when it overflowed
+  const float cut1 = fs.cut1;
+  const int n2 = gather_head<LT, VEC, NT>(lrow, a.V, m, a.s32, n1 <= kHeadCap ? cut1 : INFINITY, fs);
+  return n2 >= 0 && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt);
 }
 
 // Threshold tau of one row and Z_tau with the bound on its error (e-units of
@@ -1849,6 +2205,8 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
     ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
   };
   float ref = -INFINITY;
+  float cut1 = -INFINITY;  // top-k / top-p: pass 1 gathers the head {l >= cut1}
+  int hcnt = 0;            // (into per-wave slices, hcnt elements offered by this wave)
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
     const float c = -(ref * s);
@@ -1863,6 +2221,11 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
       const float e = fexp2(arg);
       e4[k & 3] += e;
       a4[k & 3] = fmaf(e, arg, a4[k & 3]);
+    }
+    if constexpr (FILTER) {
+      if (__any(lm >= cut1))
+        head_append_wave<LT, VEC>(r, base, V, lane, cut1, fsp->head + wave * (kHeadCap / kWaves), kHeadCap / kWaves,
+                                  hcnt);
     }
     float es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
     float ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
@@ -1899,6 +2262,7 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ref = fmaxf(ref, sh.wmax[w]);
+    if constexpr (FILTER) cut1 = ref - kHeadH1 / s;
     if (j < nt) {
       while (true) {
         rb.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
@@ -1910,6 +2274,10 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
         j += kWaves;
         if (j >= nt) break;
       }
+    }
+    if constexpr (FILTER) {
+      if (lane == 0) fsp->wcnt[wave] = hcnt;
+      if (tid == 0) fsp->cut1 = cut1;
     }
   }
   __syncthreads();
@@ -1949,7 +2317,10 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   // top-k / top-p: the threshold tau, and Z over the kept set {l >= tau}
   float tau = -INFINITY;
   if constexpr (FILTER) {
-    if (m != -INFINITY && Z > 0.0 && Z < INFINITY) row_threshold<LT, VEC, NT>(a, lrow, m, shift, *fsp, sc, tau, Z, dZ);
+    if (m != -INFINITY && Z > 0.0 && Z < INFINITY) {
+      if (!head_threshold<LT, VEC, NT>(a, lrow, m, shift, Z, dZ, *fsp, sc, tau, Z, dZ))
+        row_threshold<LT, VEC, NT>(a, lrow, m, shift, *fsp, sc, tau, Z, dZ);
+    }
   }
   const double relZ = dZ / Z;
 
@@ -2074,8 +2445,10 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
   if (threadIdx.x == 0) a.surv_n[0] = base;
 }
 
+// (FILTER: at least four waves per SIMD, two blocks per CU as without it;
+// the rare radix-select path of the threshold may then spill)
 template <typename LT, bool VEC, int NT, bool FILTER>
-__global__ __launch_bounds__(NT) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
+__global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;

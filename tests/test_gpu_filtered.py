@@ -102,12 +102,16 @@ def test_filtered_ties(dtype, top_k, top_p):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("side", [-1.0, 1.0])
-def test_top_p_next_to_a_group_boundary(dtype, side):
+@pytest.mark.parametrize("V", [4096, 8192])
+def test_top_p_next_to_a_group_boundary(dtype, side, V):
     """top_p a relative 1e-9 below or above the exact mass of the top group:
-    far inside the fp32 bound, so the fp64 sweeps decide; the top group alone
-    is kept below the boundary, the next group joins above it."""
+    far inside the fp32 bound, so fp64 sums decide; the top group alone is
+    kept below the boundary, the next group joins above it. V=4096: the whole
+    row fits the gathered head; V=8192: it does not (the head cutoff rises to
+    the top group, Z of the row comes from an fp64 sweep, and above the
+    boundary the radix select takes over)."""
     gh = _gh()
-    B, g, V, T = 6, 3, 4096, 1.0
+    B, g, T = 6, 3, 1.0
     rng = np.random.default_rng(14)
     lf = np.full((B, g + 1, V), -1.0, dtype=np.float32)
     lf[..., : V // 2] = -3.0
@@ -205,3 +209,15 @@ def test_filtered_f32_four_level_select():
     w = make_workload("dense_f32", 1, B=8)
     for k, p in ((40, 1.0), (0, 0.9), (2000, 0.99)):
         gh.compare(w, gh.run_gpu_filtered(w, k, p), filt=(k, p), label=f"dense_f32 k{k} p{p}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("top_k,top_p", [(10000, 1.0), (0, 0.9), (9000, 0.95), (30, 0.999)])
+def test_filtered_flat_rows(dtype, top_k, top_p):
+    """Nearly flat rows (sigma 0.3) of 20000 ids: the kept set does not fit
+    the gathered head, so the radix select over the whole row decides."""
+    gh = _gh()
+    w = make_dense_custom(19, B=6, gamma=3, V=20000, dtype=dtype, temperature=1.0, logit_sigma=0.3)
+    w = adjusted_drafts(w, top_k, top_p, seed=19, noise=0.2)
+    gh.compare(w, gh.run_gpu_filtered(w, top_k, top_p), filt=(top_k, top_p),
+               label=f"flat {dtype} k{top_k} p{top_p}")
