@@ -108,6 +108,11 @@ enum sv_status {
                                       need this row (an earlier row was rejected) */
 #define SV_ROW_UNREAD 0x1000u      /* lazy mode: row after a position already known to be a certain
                                       rejection: not needed, its logits were not read */
+/* top-k / top-p (the *_filtered entry points): how the row's threshold was
+ * found when the head gathered during the first pass over the row (its
+ * largest logits) could not decide it: */
+#define SV_ROW_HEAD2 0x2000u       /* from a second, larger or smaller, gathered head */
+#define SV_ROW_ROW_SELECT 0x4000u  /* from a radix select over the whole row */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of

@@ -700,6 +700,8 @@ __global__ __launch_bounds__(kSelectNT) void select_kernel(SelectArgs a) {
 constexpr uint32_t kRowNeedExact = kRowNeedExactBit;  // set by the fast kernels, cleared by the fp64 finish
 constexpr uint32_t kRowDeferred = SV_ROW_DEFERRED;
 constexpr uint32_t kRowUnread = SV_ROW_UNREAD;
+constexpr uint32_t kRowHead2 = SV_ROW_HEAD2;
+constexpr uint32_t kRowRowSelect = SV_ROW_ROW_SELECT;
 constexpr uint32_t kRowUndecided = SV_ROW_UNDECIDED;
 constexpr uint32_t kFlagLazy = 0x80000000u;    // internal: set by the host for the lazy mode
 constexpr uint32_t kFlagFilter = 0x40000000u;  // internal: lazy mode with top-k / top-p
@@ -1972,21 +1974,20 @@ __device__ bool decide_head(const ProbsArgs& a, const LT* __restrict__ lrow, flo
 }
 
 // Fast path of the threshold, in two tiers: the head pass 1 gathered (cutoff
-// ref - kHeadH1 / s, ref the block maximum of the first tiles, n1 elements
-// offered), then, if that head overflowed or cannot decide, a head gathered
-// by its own sweep from a much lower cutoff. Returns false when neither
-// decides (the radix select then runs).
+// ref - kHeadH1 / s, ref the block maximum of the first tiles), then, if that
+// head overflowed or cannot decide, a head gathered by its own sweeps.
+// Returns the tier that decided (1, 2), or 0 (the radix select then runs).
 template <typename LT, bool VEC, int NT>
-__device__ bool head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, float m, double shift, double Zp,
+__device__ int head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, float m, double shift, double Zp,
                                double dZp, FilterShared& fs, BlockScratchT<NT>& sc, float& tau, double& Zt,
                                double& dZt) {
   const int n1 = compact_slices<NT>(fs);  // pass 1's slices (> kHeadCap: one overflowed)
-  if (n1 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n1, fs, sc, tau, Zt, dZt)) return true;
+  if (n1 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n1, fs, sc, tau, Zt, dZt)) return 1;
   // a head of its own: below pass 1's cutoff when that head was too small
   // (the crossing or the k-th element lay below it), above it when it overflowed
   const float cut1 = fs.cut1;
   const int n2 = gather_head<LT, VEC, NT>(lrow, a.V, m, a.s32, n1 <= kHeadCap ? cut1 : INFINITY, fs);
-  return n2 >= 0 && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt);
+  return (n2 >= 0 && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt)) ? 2 : 0;
 }
 
 // Threshold tau of one row and Z_tau with the bound on its error (e-units of
@@ -2316,10 +2317,16 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   const double shift = static_cast<double>(cm) + static_cast<double>(m) * static_cast<double>(s);  // D, exact
   // top-k / top-p: the threshold tau, and Z over the kept set {l >= tau}
   float tau = -INFINITY;
+  uint32_t tier = 0;  // record bits: how tau was found (beyond pass 1's head)
   if constexpr (FILTER) {
     if (m != -INFINITY && Z > 0.0 && Z < INFINITY) {
-      if (!head_threshold<LT, VEC, NT>(a, lrow, m, shift, Z, dZ, *fsp, sc, tau, Z, dZ))
+      const int h = head_threshold<LT, VEC, NT>(a, lrow, m, shift, Z, dZ, *fsp, sc, tau, Z, dZ);
+      if (h == 0) {
         row_threshold<LT, VEC, NT>(a, lrow, m, shift, *fsp, sc, tau, Z, dZ);
+        tier = kRowHead2 | kRowRowSelect;
+      } else if (h == 2) {
+        tier = kRowHead2;
+      }
     }
   }
   const double relZ = dZ / Z;
@@ -2369,7 +2376,7 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
         }
         a.rstat[t.trow] = make_double4(static_cast<double>(m), z, dz, static_cast<double>(tau));
       }
-      a.ws[t.trow] = make_int2(-1, static_cast<int>(f));
+      a.ws[t.trow] = make_int2(-1, static_cast<int>(f | tier));
     }
     return;
   }
@@ -3016,7 +3023,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
           x_ok ? exp2_neg(fma(static_cast<double>(masked(to_float(lrow[x]))), s, nms), tab) * iz : 0.0;
       const double qx = x_ok ? static_cast<double>(qrow[x]) : 0.0;
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
-        if (tid == 0) a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags));
+        if (tid == 0)
+          a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags | (f0 & (kRowHead2 | kRowRowSelect))));
         start = n + 1;
         from_pass = false;
         __syncthreads();
@@ -3188,7 +3196,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     }
     if (lane == 0) {
       sel.nacc[b] = n;
-      a.ws[trow] = make_int2(token, static_cast<int>(rflags));
+      a.ws[trow] = make_int2(token, static_cast<int>(rflags | (f0 & (kRowHead2 | kRowRowSelect))));
     }
     return;
   }

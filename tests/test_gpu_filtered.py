@@ -48,6 +48,16 @@ def adjusted_drafts(w, top_k, top_p, seed, noise=1.0):
     return dict(w, draft_probs=q, draft_tokens=x)
 
 
+def tier_counts(gpu):
+    """Rows (read by the per-row pass) by the tier that found their threshold."""
+    flags = gpu[3][..., 1].reshape(-1).astype(np.int64)
+    read = (flags & api.SV_ROW_UNREAD) == 0
+    sel = (flags & api.SV_ROW_ROW_SELECT) != 0
+    h2 = ((flags & api.SV_ROW_HEAD2) != 0) & ~sel
+    return {"head": int(np.count_nonzero(read & ~sel & ~h2)), "head2": int(np.count_nonzero(h2)),
+            "row_select": int(np.count_nonzero(sel))}
+
+
 def with_logits(w, lf):
     """w with new target logits (fp32 values, exact in the workload's dtype)."""
     w = dict(w)
@@ -128,6 +138,8 @@ def test_top_p_next_to_a_group_boundary(dtype, side, V):
     w = adjusted_drafts(w, 0, top_p, seed=14, noise=0.3)
     gpu = gh.run_gpu_filtered(w, 0, top_p)
     gh.compare(w, gpu, filt=(0, top_p), label=f"boundary {dtype} {side:+}")
+    if V == 8192 and side > 0:  # the kept set reaches below every head that fits
+        assert tier_counts(gpu)["row_select"] > 0
     # the bonus row of request 0 (when reached) samples from the kept set alone
     out, nacc, _, _ = gpu
     if nacc[0] == g:
@@ -193,8 +205,15 @@ def test_filtered_full_size_sampled(top_k, top_p):
     gh = _gh()
     w = make_workload("peaked_bf16", 0)
     out, nacc, _, _ = gpu = gh.run_gpu_filtered(w, top_k, top_p)
+    tiers = tier_counts(gpu)
+    print(f"peaked full k{top_k} p{top_p}: rows by threshold tier {tiers}")
     reqs = sorted(set(np.linspace(0, w["B"] - 1, 6).round().astype(int).tolist()))
+    # the sampled requests, and the requests with a row whose threshold needed a second head
+    flags = gpu[3][:, 1].reshape(w["B"], w["gamma"] + 1)
+    reqs = sorted(set(reqs) | set(np.nonzero((flags & api.SV_ROW_HEAD2).any(axis=1))[0][:4].tolist()))
     gh.compare(w, gpu, reqs=reqs, filt=(top_k, top_p), label=f"peaked full k{top_k} p{top_p}")
+    if top_k == 50:
+        assert tiers["head2"] > 0  # (rows whose max stands far above the rest)
     g = w["gamma"]
     for b in range(w["B"]):
         n = int(nacc[b])
@@ -219,5 +238,7 @@ def test_filtered_flat_rows(dtype, top_k, top_p):
     gh = _gh()
     w = make_dense_custom(19, B=6, gamma=3, V=20000, dtype=dtype, temperature=1.0, logit_sigma=0.3)
     w = adjusted_drafts(w, top_k, top_p, seed=19, noise=0.2)
-    gh.compare(w, gh.run_gpu_filtered(w, top_k, top_p), filt=(top_k, top_p),
-               label=f"flat {dtype} k{top_k} p{top_p}")
+    gpu = gh.run_gpu_filtered(w, top_k, top_p)
+    gh.compare(w, gpu, filt=(top_k, top_p), label=f"flat {dtype} k{top_k} p{top_p}")
+    if (top_k, top_p) != (30, 0.999):  # (k = 30 fits a gathered head)
+        assert tier_counts(gpu)["row_select"] > 0
