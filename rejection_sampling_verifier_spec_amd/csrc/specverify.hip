@@ -2814,7 +2814,7 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
   };
   double es = 0.0, ps = 0.0, qs = 0.0;
-  bool und = false;
+  uint64_t und = 0;  // lanes with an undecided element (wave masks: scalar operations)
   auto compute = [&](int slot, auto pad) {
     constexpr bool PD = decltype(pad)::value;
 #pragma unroll
@@ -2837,7 +2837,7 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
           const double w = pos ? 1.0 : 0.0;
           ps = fma(e[k], w, ps);
           qs = fma(q, w, qs);
-          und = und || (!pos && e[k] > q * zlo);
+          und |= __ballot(e[k] > q * zlo) & ~__ballot(pos);
         }
       }
     }
@@ -2849,14 +2849,14 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
       tp = wave_sum_d(ps);
       tq = wave_sum_d(qs);
     }
-    const bool tu = __any(und);
+    const bool tu = und != 0;
     if (lane == 0) {
       E[jj] = te;
       P[jj] = tu ? -1.0 : tp;
       Q[jj] = tq;
     }
     es = ps = qs = 0.0;
-    und = false;
+    und = 0;
   };
   int j = j0;
   if (j >= j1) return;
