@@ -11,6 +11,7 @@ from .verifier import (  # noqa: F401
     accept_draft,
     adjusted_target_probs,
     inverse_cdf,
+    inverse_cdf_many,
     residual_weights,
     row_statistics,
     target_probs,

@@ -155,6 +155,14 @@ def inverse_cdf(w: np.ndarray, u: float) -> int:
     return int(np.searchsorted(c, u * c[-1], side="left"))
 
 
+def inverse_cdf_many(w: np.ndarray, us) -> np.ndarray:
+    """inverse_cdf for many uniforms at once (one cumulative sum): the same
+    C = cumsum(w) in float64 and the same smallest k with C[k] >= u * C[-1]
+    for every u in `us`."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    return np.searchsorted(c, np.asarray(us, dtype=np.float64) * c[-1], side="left").astype(np.int64)
+
+
 def _onehot(v: int, x: int) -> np.ndarray:
     q = np.zeros(v, dtype=np.float64)
     q[x] = 1.0

@@ -545,3 +545,16 @@ def test_top_p_boundary_is_inclusive():
         # just above it, the next value group joins
         assert list(oracle.adjusted_target_probs(l, T, top_p=np.nextafter(top, 2.0)) > 0) == [True, True, True, True,
                                                                                              False]
+
+
+def test_inverse_cdf_many_equals_the_scalar_draw():
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        v = int(rng.integers(1, 300))
+        w = rng.random(v) * (rng.random(v) < 0.7)
+        if w.sum() == 0:
+            w[0] = 1.0
+        us = (rng.integers(0, N_LATTICE, 200) + 1) * 2.0 ** -24
+        us[:2] = [2.0 ** -24, 1.0]
+        got = oracle.inverse_cdf_many(w, us)
+        assert got.tolist() == [oracle.inverse_cdf(w, float(u)) for u in us]
