@@ -12,7 +12,9 @@ of the loop, for B independent sequences:
      inverse CDF with seeded uniforms;
   2. gather the target logit rows of the gamma + 1 contexts (prev, x_1 ..
      x_gamma) into a [B, gamma + 1, V] batch;
-  3. verify the batch (by default through the C ABI, spec_verify_probs);
+  3. verify the batch (by default through the C ABI, spec_verify_probs, or
+     spec_verify_probs_filtered when top-k / top-p are set: the emitted
+     tokens then follow the adjusted target, whatever the drafter's q);
   4. append x_1 .. x_n and the drawn token; the last one is the next context.
 
 The loop keeps the bookkeeping the pages use: tokens emitted per target call
@@ -86,13 +88,18 @@ def make_bigram_pair(V: int, seed: int, kind: str = "iid", dtype: str = "bf16", 
     return BigramPair(t, torch.from_numpy(drf).to(device), float(temperature), kind, base_t, base_d)
 
 
-def hip_verifier(workspace_rows: int, V: int, device):
-    """The library's verifier with one workspace reused across steps."""
+def hip_verifier(workspace_rows: int, V: int, device, top_k: int = 0, top_p: float = 1.0):
+    """The library's verifier with one workspace reused across steps (with
+    top-k / top-p: the filtered entry point)."""
     ws = torch.zeros(api.workspace_size(workspace_rows, V), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
+    filtered = (0 < top_k < V) or top_p < 1.0
 
     def verify(logits, q, x, u, T):
-        out, nacc, _, _ = api.verify_probs(logits, q, x, u, T, workspace=ws, stream=stream)
+        if filtered:
+            out, nacc, _ = api.verify_probs_filtered(logits, q, x, u, T, top_k, top_p, workspace=ws, stream=stream)
+        else:
+            out, nacc, _, _ = api.verify_probs(logits, q, x, u, T, workspace=ws, stream=stream)
         return out, nacc
 
     return verify
@@ -136,13 +143,14 @@ class LoopStats:
 
 
 def run(pair: BigramPair, B: int, gamma: int, steps: int, seed: int = 0, verify=None, keep_pairs: bool = False,
-        device=None) -> LoopStats:
-    """Run `steps` draft-and-verify steps for B sequences from random contexts."""
+        device=None, top_k: int = 0, top_p: float = 1.0) -> LoopStats:
+    """Run `steps` draft-and-verify steps for B sequences from random contexts
+    (top_k / top_p: the library's filtered verifier, when `verify` is None)."""
     device = device or pair.target.device
     R, V = pair.target.shape
     gen = torch.Generator(device=device)
     gen.manual_seed(7919 * seed + 17)
-    verify = verify or hip_verifier(B * (gamma + 1), V, device)
+    verify = verify or hip_verifier(B * (gamma + 1), V, device, top_k, top_p)
     ctx = torch.randint(0, V, (B,), generator=gen, device=device, dtype=torch.int64)
     st = LoopStats(accepted_hist=np.zeros(gamma + 1, dtype=np.int64),
                    pair_counts=np.zeros((V, V), dtype=np.int64) if keep_pairs else None)

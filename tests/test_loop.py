@@ -43,37 +43,48 @@ def oracle_verifier(logits, q, x, u, T):
     return torch.from_numpy(out), torch.from_numpy(nacc)
 
 
-def beta_of(pair: loop.BigramPair, device) -> float:
+def beta_of(pair: loop.BigramPair, device, filt=None) -> float:
     """sum_x min(p(x), q(x)) of the iid tables' base rows, with q exactly as the
-    loop computes it (fp32 softmax) and p from the oracle."""
-    p = oracle.target_probs(pair.base_target.astype(np.float64), pair.temperature)
+    loop computes it (fp32 softmax) and p from the oracle (adjusted by top-k /
+    top-p when filt = (top_k, top_p))."""
+    if filt is None:
+        p = oracle.target_probs(pair.base_target.astype(np.float64), pair.temperature)
+    else:
+        p = oracle.adjusted_target_probs(pair.base_target.astype(np.float64), pair.temperature, *filt)
     d = torch.from_numpy(pair.base_draft).to(device)
     q = torch.softmax(d / pair.temperature, dim=-1).cpu().numpy().astype(np.float64)
     return float(np.sum(np.minimum(p, q)))
 
 
-def target_table_probs(pair: loop.BigramPair) -> np.ndarray:
-    """Next-token distribution of every context (tables with one row per context)."""
+def target_table_probs(pair: loop.BigramPair, filt=None) -> np.ndarray:
+    """Next-token distribution of every context (tables with one row per
+    context), adjusted by top-k / top-p when filt = (top_k, top_p)."""
     t = pair.target.float().cpu().numpy().astype(np.float64)
     assert t.shape[0] == t.shape[1]
-    return np.stack([oracle.target_probs(t[c], pair.temperature) for c in range(t.shape[0])])
+    if filt is None:
+        return np.stack([oracle.target_probs(t[c], pair.temperature) for c in range(t.shape[0])])
+    return np.stack([oracle.adjusted_target_probs(t[c], pair.temperature, *filt) for c in range(t.shape[0])])
 
 
 def chi_square_pvalue(counts: np.ndarray, probs: np.ndarray) -> float:
     """Pearson chi-square of observed (prev, next) counts against the target
     rows, summed over the contexts; per context, cells with expected count
-    below 5 are pooled into one cell."""
+    below 5 are pooled into one cell. A token of probability 0 must never be
+    emitted (checked separately: it would make the statistic infinite)."""
+    assert not np.any(counts[probs == 0.0]), "a token outside the target's support was emitted"
     chi2, dof = 0.0, 0
     for c in range(counts.shape[0]):
         n = counts[c].sum()
         if n == 0:
             continue
-        e = n * probs[c]
+        live = probs[c] > 0.0  # (zero-probability cells carry no count: checked above)
+        e = n * probs[c][live]
+        cnt = counts[c][live]
         small = e < 5.0
-        obs = list(counts[c][~small])
+        obs = list(cnt[~small])
         exp = list(e[~small])
         if small.any():
-            obs.append(counts[c][small].sum())
+            obs.append(cnt[small].sum())
             exp.append(e[small].sum())
         obs, exp = np.array(obs, dtype=np.float64), np.array(exp)
         chi2 += float(np.sum((obs - exp) ** 2 / exp))
@@ -161,3 +172,21 @@ def test_loop_non_iid_tables_keep_the_target_distribution():
     hist = st.accepted_hist / st.accepted_hist.sum()
     print(f"V=16 free: {st.tokens_per_step:.4f} tokens/step, accepted-draft histogram {np.round(hist, 4)}")
     assert chi_square_pvalue(st.pair_counts, target_table_probs(pair)) > 1e-4
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("filt", [(5, 1.0), (0, 0.8), (6, 0.7)])
+def test_loop_with_top_k_top_p_on_gpu(filt):
+    """With top-k / top-p the emitted tokens follow the adjusted target (the
+    drafter's q is the plain softmax: rejection sampling needs nothing of q),
+    no token outside the kept set is ever emitted, and iid tables still give
+    Eq. (1) with beta = sum min(p_adjusted, q)."""
+    dev = torch.device("cuda:0")
+    pair = loop.make_bigram_pair(16, seed=6, kind="iid", dtype="bf16", temperature=1.0, device=dev)
+    gamma = 4
+    st = loop.run(pair, B=256, gamma=gamma, steps=300, seed=6, keep_pairs=True, top_k=filt[0], top_p=filt[1])
+    beta = beta_of(pair, dev, filt)
+    print(f"V=16 iid top_k={filt[0]} top_p={filt[1]}: beta={beta:.4f}, {st.tokens_per_step:.4f} tokens/step, "
+          f"Eq. (1) {loop.eq1_tokens_per_step(beta, gamma)[0]:.4f}")
+    check_eq1(st, beta, gamma)
+    assert chi_square_pvalue(st.pair_counts, target_table_probs(pair, filt)) > 1e-4
