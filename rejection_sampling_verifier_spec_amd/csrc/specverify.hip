@@ -1382,14 +1382,16 @@ __device__ void sample_row(const ProbsArgs& a, const Task& t, const LT* __restri
 constexpr int kSelDigits = 256;
 constexpr int kSelCand = 8;  // digit boundaries per fp64 sweep
 constexpr int kHeadCap = 4096;  // elements of the gathered head (see head_threshold)
-// Cutoffs of the gathered head: pass 1 gathers {l >= ref - kHeadH1 / s}
-// (ref the block maximum of the first tiles); a head gathered by its own
-// sweeps takes the lowest cutoff m - kCutLadder[i] / s (e >= 2^-H relative to
-// the row max) whose elements fit the buffer.
+// Cutoffs of the gathered head: pass 1 gathers {l >= c1}, c1 = ref - kHeadH1 / s
+// (ref the block maximum of the first tiles, so e >= 2^-16 relative to it);
+// a head gathered by its own sweeps takes the lowest of kRungs cutoffs whose
+// elements fit the buffer: c1 - kRungBelow[i] / s when pass 1's head was too
+// small, c1 + (m - c1) kRungAbove[i] when it overflowed.
 constexpr float kHeadH1 = 16.f;
 constexpr int kHeadFix = 50;  // fraction bits of the head masses: kHeadCap terms <= 1 stay below 2^63
-constexpr int kCutLadderLen = 8;
-__constant__ float kCutLadder[kCutLadderLen] = {64.f, 40.f, 28.f, 20.f, 14.f, 9.f, 5.f, 0.f};
+constexpr int kRungs = 4;
+__constant__ float kRungBelow[kRungs] = {48.f, 32.f, 16.f, 8.f};
+__constant__ float kRungAbove[kRungs] = {0.25f, 0.5f, 0.75f, 1.f};
 
 struct FilterShared {
   union {
@@ -1706,28 +1708,23 @@ __device__ int compact_slices(FilterShared& fs) {
 }
 
 // A head gathered by its own two sweeps, after pass 1 (m known): the first
-// counts, per wave, the elements at or above each of the kCutLadderLen
-// cutoffs m - kCutLadder[i] / s (registers only); the lowest cutoff whose
-// per-wave counts all fit a wave's slice of the buffer is taken, and the
-// second sweep appends the elements at or above it to the per-wave slices,
-// which are then made contiguous. Returns the head size, or -1 if no cutoff
-// fits (even the row max's tie group overflows a slice). min_cut: a cutoff
-// at or above it gains nothing (-1 is returned too).
+// counts, per wave, the elements at or above each of kRungs increasing
+// cutoffs (registers only); the lowest cutoff whose per-wave counts all fit a
+// wave's slice of the buffer is taken, and the second sweep appends the
+// elements at or above it to the per-wave slices, which are then made
+// contiguous. Returns the head size, or -1 if no cutoff fits.
 template <typename LT, bool VEC, int NT>
-__device__ int gather_head(const LT* __restrict__ lrow, int V, float m, float s, float min_cut, FilterShared& fs) {
+__device__ int gather_head(const LT* __restrict__ lrow, int V, const float (&cuts)[kRungs], FilterShared& fs) {
   constexpr int kW = NT / 64;
   constexpr int kSlice = kHeadCap / kW;
   using L = Lay<LT, VEC>;
   using Raw = RawTile<LT, VEC>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = (V + kTile - 1) / kTile;
-  float cuts[kCutLadderLen];
+  // ---- counts per cutoff
+  int cnt[kRungs];
 #pragma unroll
-  for (int i = 0; i < kCutLadderLen; ++i) cuts[i] = m - kCutLadder[i] / s;
-  // ---- counts per cutoff (the ladder is increasing in cutoff)
-  int cnt[kCutLadderLen];
-#pragma unroll
-  for (int i = 0; i < kCutLadderLen; ++i) cnt[i] = 0;
+  for (int i = 0; i < kRungs; ++i) cnt[i] = 0;
   {
     Raw ra, rb;
     int j = wave;
@@ -1739,7 +1736,7 @@ __device__ int gather_head(const LT* __restrict__ lrow, int V, float m, float s,
         const float v = r.get(k);
         const bool in = full || L::index(base, lane, k) < V;
 #pragma unroll
-        for (int i = 0; i < kCutLadderLen; ++i) cnt[i] += (in && v >= cuts[i]) ? 1 : 0;
+        for (int i = 0; i < kRungs; ++i) cnt[i] += (in && v >= cuts[i]) ? 1 : 0;
       }
     };
     if (j < nt) {
@@ -1757,9 +1754,9 @@ __device__ int gather_head(const LT* __restrict__ lrow, int V, float m, float s,
     }
   }
   // the lowest cutoff whose count fits in every wave's slice
-  int ok_from = kCutLadderLen;  // first ladder index that fits this wave
+  int ok_from = kRungs;  // first rung that fits this wave
 #pragma unroll
-  for (int i = kCutLadderLen - 1; i >= 0; --i) {
+  for (int i = kRungs - 1; i >= 0; --i) {
     int c = cnt[i];
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
     if (c <= kSlice && ok_from == i + 1) ok_from = i;
@@ -1770,9 +1767,8 @@ __device__ int gather_head(const LT* __restrict__ lrow, int V, float m, float s,
 #pragma unroll
   for (int w = 0; w < kW; ++w) li = max(li, fs.wcnt[w]);
   __syncthreads();
-  if (li >= kCutLadderLen) return -1;
-  const float cut = m - kCutLadder[li] / s;
-  if (cut >= min_cut) return -1;
+  if (li >= kRungs) return -1;
+  const float cut = cuts[li];
   // ---- gather into the per-wave slices
   int hc = 0;
   {
@@ -1986,7 +1982,11 @@ __device__ int head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
   // a head of its own: below pass 1's cutoff when that head was too small
   // (the crossing or the k-th element lay below it), above it when it overflowed
   const float cut1 = fs.cut1;
-  const int n2 = gather_head<LT, VEC, NT>(lrow, a.V, m, a.s32, n1 <= kHeadCap ? cut1 : INFINITY, fs);
+  float cuts[kRungs];
+#pragma unroll
+  for (int i = 0; i < kRungs; ++i)
+    cuts[i] = n1 <= kHeadCap ? cut1 - kRungBelow[i] / a.s32 : cut1 + (m - cut1) * kRungAbove[i];
+  const int n2 = gather_head<LT, VEC, NT>(lrow, a.V, cuts, fs);
   return (n2 >= 0 && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt)) ? 2 : 0;
 }
 
