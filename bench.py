@@ -135,6 +135,78 @@ def measure_loop(steps: int, dev):
                     "the verifier through the C ABI"}
 
 
+OTHER_CONFIGS = ("dense_f32", "ragged_bf16", "greedy_bf16", "onehot_bf16")
+
+
+def measure_config(name: str, steps: int, dev):
+    """One of the other workloads (fp32 batch, ragged batch, greedy argmax,
+    one-hot drafts), `steps` calls after 3 warm-up calls: wall time per call,
+    verified positions per second and the bytes the call reads against HBM
+    peak. Bytes, as for the headline workload: the logit rows the per-row pass
+    reads (rows recorded as not read are left out) and the draft tokens, then
+    in sampling modes the deciding rows read again (a replacement draw: logits
+    and q, or logits only with one-hot drafts; a bonus draw: logits)."""
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verifier_spec_amd import api
+    from rejection_sampling_verifier_spec_amd.workloads import make_workload
+
+    w = make_workload(name, 0)
+    V, T, B = w["V"], w["temperature"], w["B"]
+    esz = 2 if w["dtype"] == "bf16" else 4
+    if w["dtype"] == "bf16":
+        logits = torch.from_numpy(w["logits_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        logits = torch.from_numpy(w["logits"]).to(dev)
+    q = None if w["draft_probs"] is None else torch.from_numpy(w["draft_probs"]).to(dev)
+    x = torch.from_numpy(w["draft_tokens"]).to(dev)
+    u = torch.from_numpy(w["uniforms"]).to(dev)
+    ragged = w["kind"] == "ragged"
+    cu = torch.from_numpy(w["cu"].astype(np.int32)).to(dev) if ragged else None
+    rows = logits.shape[0] if ragged else B * (w["gamma"] + 1)
+    positions = int(x.numel())
+    ws = torch.zeros(api.workspace_size(rows, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        if ragged:
+            return api.verify_ragged(logits, q, x, cu, u, T, workspace=ws, stream=stream)[:2]
+        if T == 0.0:
+            return api.verify_greedy(logits, x, workspace=ws, stream=stream)[:2]
+        return api.verify_probs(logits, q, x, u, T, workspace=ws, stream=stream)[:2]
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        out, nacc = call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    rec = api.row_records(ws, rows).cpu().numpy().astype(np.int64)
+    flags = rec[:, 1]
+    read = int(np.count_nonzero((flags & api.SV_ROW_UNREAD) == 0))
+    if ragged:
+        cu_h = w["cu"].astype(np.int64)
+        last = cu_h[1:] + np.arange(B)
+    else:
+        last = np.arange(B) * (w["gamma"] + 1) + w["gamma"]
+    # the rows the per-row pass read, then (sampling modes) the deciding rows read
+    # again: a replacement draw reads logits and q (one-hot drafts: logits only), a
+    # bonus draw the last row's logits
+    nbytes = read * V * esz + positions * 8
+    if T > 0:
+        resid = int(np.count_nonzero(flags & api.SV_ROW_RESIDUAL))
+        bonus = int(np.count_nonzero(rec[last, 0] >= 0))
+        nbytes += resid * V * (esz + (4 if q is not None else 0)) + bonus * V * esz
+    mode = "greedy argmax" if T == 0.0 else ("one-hot drafts" if q is None else "lazy")
+    return {"workload": f"{name}: B={B} V={V} T={T} {w['dtype']} logits, {mode}", "steps": steps,
+            "ms_per_call": dt * 1e3, "positions_per_s": positions / dt, "rows_read": read, "target_rows": rows,
+            "bytes_per_call": nbytes, "achieved_GBps": nbytes / dt / 1e9, "frac_of_hbm_peak": nbytes / dt / 1e9 / HBM_PEAK_GBS,
+            "mean_accepted": float(nacc.float().mean().item())}
+
+
 def measure_filtered(steps, logits, q, x, u, T, ws, stream, top_k=50, top_p=0.9):
     """The same batch through spec_verify_probs_filtered (top-k then top-p on
     the target): wall time per call and the per-row pass's event time."""
@@ -170,6 +242,8 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="SV_FLAG_* bits passed to the library (0: lazy residuals, 4: eager, 2: all residuals)")
     ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="calls timed for each of the other workloads after the timed region (0: skip)")
     ap.add_argument("--filtered-steps", type=int, default=30,
                     help="calls of the top-k / top-p entry point timed after the timed region (0: skip)")
     ap.add_argument("--loop-steps", type=int, default=30,
@@ -309,6 +383,13 @@ def main():
         mism = sum(1 for b, (toks, n) in enumerate(ref) if n != na[b] or list(o[b, :n + 1]) != toks)
         base["parity_mismatches_in_sample"] = mism
         result["cpu_baseline"] = base
+    if args.config_steps > 0:
+        del logits, q, x, u, ws, w
+        torch.cuda.empty_cache()
+        result["other_configs"] = []
+        for n in OTHER_CONFIGS:
+            print(f"bench: {n}", file=sys.stderr, flush=True)
+            result["other_configs"].append(measure_config(n, args.config_steps, dev))
     print(json.dumps(result))
 
 

@@ -2667,6 +2667,11 @@ struct RawChunk<uint16_t, true> {
     const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
     return (!PAD || i0 + e < V) ? v : 0.f;
   }
+  // q = onehot(hot) over the chunk's elements (hot < 0: zeros)
+  __device__ __forceinline__ void set_onehot(int hot) {
+    q0 = make_float4(i0 == hot, i0 + 1 == hot, i0 + 2 == hot, i0 + 3 == hot);
+    q1 = make_float4(i0 + 4 == hot, i0 + 5 == hot, i0 + 6 == hot, i0 + 7 == hot);
+  }
 };
 template <>
 struct RawChunk<float, true> {
@@ -2699,6 +2704,10 @@ struct RawChunk<float, true> {
     const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
     return (!PAD || idx(e) < V) ? v : 0.f;
   }
+  __device__ __forceinline__ void set_onehot(int hot) {
+    q0 = make_float4(idx(0) == hot, idx(1) == hot, idx(2) == hot, idx(3) == hot);
+    q1 = make_float4(idx(4) == hot, idx(5) == hot, idx(6) == hot, idx(7) == hot);
+  }
 };
 template <typename LT>
 struct RawChunk<LT, false> {
@@ -2723,6 +2732,10 @@ struct RawChunk<LT, false> {
   template <bool PAD>
   __device__ __forceinline__ float get_q(int e, int V) const {
     return (!PAD || Lay<LT, false>::index(base, lane, 8 * c + e) < V) ? q[e] : 0.f;
+  }
+  __device__ __forceinline__ void set_onehot(int hot) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = Lay<LT, false>::index(base, lane, 8 * c + e) == hot ? 1.f : 0.f;
   }
 };
 
@@ -2800,18 +2813,22 @@ struct ReqShared {
 // P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
 // interval leaves an element undecided (LDS or global, indexed by tile). With
 // MASK, logits below tau (outside the top-k / top-p kept set) count as -inf.
+// A draft row without a q row (one-hot draft) takes q = onehot(hot), zeros
+// when hot < 0 (a draft token outside the vocabulary).
 template <typename LT, bool VEC, bool MASK>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
                               const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
-                              float tau) {
+                              float tau, int hot) {
   const int lane = threadIdx.x & 63;
   const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
   using Chunk = RawChunk<LT, VEC>;
   Chunk ring[4];
+  const bool onehot = draft && qrow == nullptr;
   auto load = [&](int slot, int jj, int c) {
     // chunks past the wave's last tile re-read the row's last tile (in bounds, unused)
-    ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
+    ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, qrow != nullptr);
+    if (onehot) ring[slot].set_onehot(hot);
   };
   double es = 0.0, ps = 0.0, qs = 0.0;
   uint64_t und = 0;  // lanes with an undecided element (wave masks: scalar operations)
@@ -2911,6 +2928,14 @@ constexpr int kPassSlices = 3;     // blocks per request in the pass kernel
 constexpr int kFinishNT = 256;     // threads per block of the finish kernel
 constexpr int kFinishWaves = kFinishNT / 64;
 
+// One-hot drafts (no q rows): the draft token of draft row d when it lies in
+// the vocabulary, else -1; -1 for a bonus row or when q rows are given.
+__device__ __forceinline__ int onehot_index(const ProbsArgs& a, bool draft, int64_t d) {
+  if (!draft || a.q) return -1;
+  const int64_t x = a.x[d];
+  return (x >= 0 && x < a.V) ? static_cast<int>(x) : -1;
+}
+
 struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the fp64 path's tile arrays)
   double* E;
   double* P;
@@ -2940,12 +2965,13 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
   const double4 st = a.rstat[trow];
   const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
-  const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+  const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+  const int hot = onehot_index(a, draft, d0 + n);
   const int per = (nt + kPassSlices - 1) / kPassSlices;
   const int j0 = sl * per, j1 = min(nt, j0 + per);
   const int64_t o = static_cast<int64_t>(b) * nt;
   fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, draft, j0 + wave, j1, kPassWaves, tab,
-                                 C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
+                                 C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w), hot);
 }
 
 // Lazy mode, per-request finish: one block per request. Z from the pass's
@@ -2995,7 +3021,9 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     const float keep_min = static_cast<float>(st.w);  // top-k / top-p threshold tau (-inf: no filter)
     auto masked = [&](float l) { return (FILTER && l < keep_min) ? -INFINITY : l; };
     const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
-    const float* __restrict__ qrow = draft ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+    const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+    const int hot = onehot_index(a, draft, d0 + n);
+    const bool onehot = draft && !a.q;
     if (from_pass) {
       const int64_t o = static_cast<int64_t>(b) * nt;
       for (int j = tid; j < nt; j += kFinishNT) {
@@ -3006,7 +3034,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     } else {  // a later row (an undecided accept test turned out accepted): its pass here
       const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
       fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, m, s, zhi, zlo, draft, wave, nt, kFinishWaves, tab, C, E, P,
-                                     Q, keep_min);
+                                     Q, keep_min, hot);
     }
     __syncthreads();
     for (int j = tid; j < nt; j += kFinishNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
@@ -3021,7 +3049,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       const bool x_ok = x >= 0 && x < V;
       const double px =
           x_ok ? exp2_neg(fma(static_cast<double>(masked(to_float(lrow[x]))), s, nms), tab) * iz : 0.0;
-      const double qx = x_ok ? static_cast<double>(qrow[x]) : 0.0;
+      const double qx = x_ok ? (onehot ? 1.0 : static_cast<double>(qrow[x])) : 0.0;
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
         if (tid == 0)
           a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags | (f0 & (kRowHead2 | kRowRowSelect))));
@@ -3050,6 +3078,10 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
         for (int c = 0; c < 4; ++c) {
           float lv[8], qv[8];
           load_chunk<LT, VEC, true>(lrow, qrow, V, base, lane, c, lv, qv);
+          if (onehot) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = Lay<LT, VEC>::index(base, lane, 8 * c + e) == hot ? 1.f : 0.f;
+          }
 #pragma unroll
           for (int g4 = 0; g4 < 8; g4 += kExpW) {
             double ar[kExpW], e[kExpW];
@@ -3130,6 +3162,10 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     for (int h = 0; h < 4; ++h) {
       load8f<LT, VEC>(lrow, V, k0 + 8 * h, lall[h]);
       load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qall[h]);
+      if (mode == 1 && onehot) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qall[h][k] = k0 + 8 * h + k == hot ? 1.f : 0.f;
+      }
       if constexpr (FILTER) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) lall[h][k] = masked(lall[h][k]);
@@ -3493,9 +3529,8 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.gamma = gamma;
     p.ndraft = ndraft;
     p.V = V;
-    // lazy (default): with q, no statistics, and not every row forced through the fp64 path
-    const bool lazy =
-        !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EXACT)) && stats == nullptr && q != nullptr;
+    // lazy (default): no statistics, and not every row forced through the fp64 path
+    const bool lazy = !(flags & (SV_FLAG_EAGER | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EXACT)) && stats == nullptr;
     const bool filter = fa.filtered && ((fa.top_k > 0 && fa.top_k < V) || fa.top_p < 1.0);
     p.flags = flags | (lazy ? kFlagLazy : 0u) | (filter ? kFlagFilter : 0u);
     p.top_k = filter ? fa.top_k : 0;

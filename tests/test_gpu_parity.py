@@ -145,7 +145,7 @@ def test_exact_flag_gives_same_results(name):
     assert np.array_equal(g1[0], g2[0]) and np.array_equal(g1[1], g2[1])
 
 
-@pytest.mark.parametrize("name,B", [("peaked_bf16", 24), ("dense_f32", 16), ("ragged_bf16", 24)])
+@pytest.mark.parametrize("name,B", [("peaked_bf16", 24), ("dense_f32", 16), ("ragged_bf16", 24), ("onehot_bf16", 40)])
 def test_modes_give_identical_outputs_and_are_deterministic(name, B):
     """Lazy (default), eager and all-residuals modes differ only in which rows
     draw a replacement; outputs must be identical, and repeatable bit for bit."""
@@ -184,6 +184,16 @@ def test_ragged_equals_dense():
     d = gh.run_gpu(w)
     r = gh.run_gpu(dense_as_ragged(w))
     assert np.array_equal(d[0].reshape(-1), r[0]) and np.array_equal(d[1], r[1])
+
+
+def test_ragged_one_hot_equals_dense():
+    gh = _gh()
+    w = make_workload("onehot_bf16", 3, B=12, V=9000)
+    d = gh.run_gpu(w)
+    wr = dense_as_ragged(w)
+    r = gh.run_gpu(wr)
+    assert np.array_equal(d[0].reshape(-1), r[0]) and np.array_equal(d[1], r[1])
+    gh.compare(wr, r, label="ragged one-hot")
 
 
 def test_temperature_zero_probs_equals_greedy():
@@ -301,6 +311,26 @@ def test_out_of_range_draft_token_is_rejected():
     torch.cuda.synchronize()
     assert torch.all(nacc == 0)
     assert torch.all((out[:, 0] >= 0) & (out[:, 0] < 1000))
+
+
+def test_out_of_range_one_hot_draft_token_draws_from_p():
+    """One-hot drafts (no q rows) with a token outside the vocabulary: p(x) = 0,
+    so the draft is rejected, and the residual max(0, p - onehot(x)) is p
+    itself (no element is removed): the replacement is the inverse-CDF draw
+    from p of that row, in the default (lazy) and eager modes."""
+    import oracle
+    gh = _gh()
+    w = make_dense_custom(11, B=6, gamma=2, V=1000, dtype="f32", temperature=1.0, q_kind="onehot")
+    t = gh.dev_inputs(w)
+    t["x"][:, 0] = 5000
+    for flags in (0, api.SV_FLAG_EAGER):
+        out, nacc, _, _ = api.verify_probs(t["logits"], None, t["x"], t["u"], 1.0, flags=flags)
+        torch.cuda.synchronize()
+        assert torch.all(nacc == 0)
+        o = out.cpu().numpy()
+        for b in range(w["B"]):
+            ref = oracle.inverse_cdf(oracle.target_probs(w["logits"][b, 0], 1.0), float(w["uniforms"][b, -1]))
+            assert o[b, 0] == ref and np.all(o[b, 1:] == -1), (flags, b)
 
 
 def test_hardware_exp2_within_the_assumed_bound():
