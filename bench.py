@@ -135,6 +135,75 @@ def measure_loop(steps: int, dev):
                     "the verifier through the C ABI"}
 
 
+def call_percentiles(call, steps, stream):
+    """Per-call times (ms) of `steps` further calls, each bracketed by a pair of
+    events on the launch stream: {p10, p50, p90}."""
+    import numpy as np
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)), "p90": float(np.percentile(t, 90)),
+            "calls": steps}
+
+
+def measured_beta(lrows, qrows, xs, T, chunk=256):
+    """Mean over draft rows of beta = sum_k min(p_k, q_k) (the row's accept
+    probability), with p = softmax(l / T) in fp32 by torch (a reported
+    statistic of the synthetic workload, not part of the verifier); one-hot
+    drafts (qrows None): beta = p(x)."""
+    import torch
+
+    tot, n = 0.0, lrows.shape[0]
+    for i in range(0, n, chunk):
+        p = torch.softmax(lrows[i:i + chunk].float() / T, dim=-1)
+        if qrows is None:
+            b = p.gather(1, xs[i:i + chunk].clamp(0, p.shape[1] - 1).view(-1, 1)).view(-1)
+        else:
+            b = torch.minimum(p, qrows[i:i + chunk]).sum(-1)
+        tot += float(b.double().sum().item())
+    return tot / max(n, 1)
+
+
+def draft_views(logits, q, x, cu, B, g, V):
+    """(target rows of the draft positions [N, V], q rows [N, V] or None, x [N])."""
+    import torch
+
+    if cu is None:
+        return logits[:, :g].reshape(-1, V), None if q is None else q.reshape(-1, V), x.reshape(-1)
+    n = x.numel()
+    req = torch.repeat_interleave(torch.arange(B, device=x.device), (cu[1:] - cu[:-1]).long())
+    return logits[torch.arange(n, device=x.device) + req], q, x
+
+
+def copy_ceiling(dev, mib=2048, reps=10):
+    """Practical HBM ceilings as context: a read-only reduction (torch amax
+    over fp32) and a device-to-device copy (bytes read + written)."""
+    import torch
+
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("read_amax", lambda: a.amax(), 4 * n), ("copy", lambda: b.copy_(a), 8 * n)):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = nbytes * reps / (time.perf_counter() - t0) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    out["buffer_MiB"] = mib
+    return out
+
+
 OTHER_CONFIGS = ("dense_f32", "ragged_bf16", "greedy_bf16", "onehot_bf16")
 
 
@@ -184,6 +253,7 @@ def measure_config(name: str, steps: int, dev):
         out, nacc = call()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+    pct = call_percentiles(call, steps, stream)
     rec = api.row_records(ws, rows).cpu().numpy().astype(np.int64)
     flags = rec[:, 1]
     read = int(np.count_nonzero((flags & api.SV_ROW_UNREAD) == 0))
@@ -204,7 +274,8 @@ def measure_config(name: str, steps: int, dev):
     return {"workload": f"{name}: B={B} V={V} T={T} {w['dtype']} logits, {mode}", "steps": steps,
             "ms_per_call": dt * 1e3, "positions_per_s": positions / dt, "rows_read": read, "target_rows": rows,
             "bytes_per_call": nbytes, "achieved_GBps": nbytes / dt / 1e9, "frac_of_hbm_peak": nbytes / dt / 1e9 / HBM_PEAK_GBS,
-            "mean_accepted": float(nacc.float().mean().item())}
+            "mean_accepted": float(nacc.float().mean().item()), "call_ms": pct,
+            "beta_mean": (measured_beta(*draft_views(logits, q, x, cu, B, w["gamma"], V), T) if T > 0 else None)}
 
 
 def measure_filtered(steps, logits, q, x, u, T, ws, stream, top_k=50, top_p=0.9):
@@ -301,6 +372,7 @@ def main():
         step()
     torch.cuda.synchronize()
     prof[api.SV_PROFILE_REQUEST] = api.profile_stop()[api.SV_PROFILE_REQUEST]
+    pct = call_percentiles(step, args.steps, stream)
     positions = B * g
 
     rec = api.row_records(ws, rows).cpu().numpy().reshape(B, g + 1, 2)
@@ -362,11 +434,14 @@ def main():
                          "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
                          "achieved_GBps": req_bytes / req_s / 1e9 if req_n else None},
         "whole_call": {"bytes": alg_bytes, "ms_mean": call_s * 1e3, "achieved_GBps": alg_bytes / call_s / 1e9,
-                       "note": "wall clock over the timed steps (synchronize on both sides)"},
+                       "ms_event_percentiles": pct,
+                       "note": "ms_mean: wall clock over the timed steps (synchronize on both sides); percentiles: "
+                               "further calls, one event pair each on the launch stream"},
         "rows": {"draft": positions, "target_rows": rows, "read_by_per_row_pass": rows_read,
                  "needed_by_the_method": rows_needed, "accepted_own_test": accepted_rows,
                  "residual_drawn": residual_rows, "bonus_drawn": bonus_drawn,
-                 "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item())},
+                 "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item()),
+                 "beta_mean": measured_beta(*draft_views(logits, q, x, None, B, g, V), T) if T > 0 else None},
         "speculative_full_bytes_per_call": full_bytes,
         "method_minimum_bytes_per_call": needed_bytes,
         "method_minimum_GBps_equiv": needed_bytes / call_s / 1e9,
@@ -386,6 +461,7 @@ def main():
     if args.config_steps > 0:
         del logits, q, x, u, ws, w
         torch.cuda.empty_cache()
+        result["hbm_ceiling_context"] = copy_ceiling(dev)
         result["other_configs"] = []
         for n in OTHER_CONFIGS:
             print(f"bench: {n}", file=sys.stderr, flush=True)

@@ -3241,6 +3241,11 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
 // ----------------------------------------------------------------------------
 // greedy verification (argmax, lowest index on ties)
 
+// Threads per row block of the greedy kernel: 16 waves per row, two rows per
+// CU at a time (measured: 2-3% faster than 4 or 8 waves per row at
+// B = 1024, gamma = 4, V = 128256; loading two tiles per step was slower).
+constexpr int kGreedyNT = 1024;
+
 struct GreedyArgs {
   const void* logits;
   const int64_t* x;
@@ -3257,9 +3262,10 @@ __device__ __forceinline__ void argmax_combine(float& v, int& i, float v2, int i
 }
 
 template <typename LT, bool VEC>
-__global__ __launch_bounds__(kNT) void greedy_rows_kernel(GreedyArgs a) {
-  __shared__ float bv[kWaves];
-  __shared__ int bi[kWaves];
+__global__ __launch_bounds__(kGreedyNT) void greedy_rows_kernel(GreedyArgs a) {
+  constexpr int kW = kGreedyNT / 64;
+  __shared__ float bv[kW];
+  __shared__ int bi[kW];
   using L = Lay<LT, VEC>;
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
@@ -3268,12 +3274,11 @@ __global__ __launch_bounds__(kNT) void greedy_rows_kernel(GreedyArgs a) {
   if (!t.valid) return;
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(V);
 
+  // each lane visits its elements in increasing index order, so a strict >
+  // keeps the lowest index among equal values
   float best = -INFINITY;
   int bidx = 0x7fffffff;
-  for (int j = wave; j < nt; j += kWaves) {
-    const int base = j * kTile;
-    float v[kLaneElems];
-    load_logits<LT, VEC>(lrow, V, base, lane, v);
+  auto scan = [&](const float (&v)[kLaneElems], int base) {
 #pragma unroll
     for (int k = 0; k < kLaneElems; ++k) {
       if (v[k] > best) {
@@ -3281,6 +3286,11 @@ __global__ __launch_bounds__(kNT) void greedy_rows_kernel(GreedyArgs a) {
         bidx = L::index(base, lane, k);
       }
     }
+  };
+  for (int j = wave; j < nt; j += kW) {
+    float v[kLaneElems];
+    load_logits<LT, VEC>(lrow, V, j * kTile, lane, v);
+    scan(v, j * kTile);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -3296,7 +3306,7 @@ __global__ __launch_bounds__(kNT) void greedy_rows_kernel(GreedyArgs a) {
   if (tid == 0) {
     float v = bv[0];
     int i = bi[0];
-    for (int w = 1; w < kWaves; ++w) argmax_combine(v, i, bv[w], bi[w]);
+    for (int w = 1; w < kW; ++w) argmax_combine(v, i, bv[w], bi[w]);
     if (i == 0x7fffffff) i = 0;  // every entry -inf: the first index
     int acc = 0;
     if (t.drow >= 0) acc = (a.x[t.drow] == static_cast<int64_t>(i)) ? 1 : 0;
@@ -3462,9 +3472,9 @@ template <typename LT>
 int launch_greedy(const GreedyArgs& a, int64_t rows, hipStream_t st) {
   const bool vec = aligned16(a.logits) && (static_cast<int64_t>(a.V) * sizeof(LT)) % 16 == 0;
   if (vec)
-    hipLaunchKernelGGL((greedy_rows_kernel<LT, true>), dim3(static_cast<unsigned>(rows)), dim3(kNT), 0, st, a);
+    hipLaunchKernelGGL((greedy_rows_kernel<LT, true>), dim3(static_cast<unsigned>(rows)), dim3(kGreedyNT), 0, st, a);
   else
-    hipLaunchKernelGGL((greedy_rows_kernel<LT, false>), dim3(static_cast<unsigned>(rows)), dim3(kNT), 0, st, a);
+    hipLaunchKernelGGL((greedy_rows_kernel<LT, false>), dim3(static_cast<unsigned>(rows)), dim3(kGreedyNT), 0, st, a);
   return 0;
 }
 
