@@ -333,6 +333,20 @@ def test_out_of_range_one_hot_draft_token_draws_from_p():
             assert o[b, 0] == ref and np.all(o[b, 1:] == -1), (flags, b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_vocabulary(dtype):
+    """V = SV_MAX_VOCAB (2^21): the largest rows the library accepts (1024
+    tiles per row, the largest LDS tile arrays), in the default mode with q
+    rows and with one-hot drafts, and through the top-k / top-p entry point."""
+    gh = _gh()
+    V = 1 << 21
+    w = make_dense_custom(12 + (dtype == "f32"), B=3, gamma=2, V=V, dtype=dtype, temperature=0.8)
+    gh.compare(w, gh.run_gpu(w), label=f"V=2^21 {dtype}")
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label=f"V=2^21 {dtype} one-hot")
+    gh.compare(w, gh.run_gpu_filtered(w, 50, 0.9), label=f"V=2^21 {dtype} filtered", filt=(50, 0.9))
+
+
 def test_hardware_exp2_within_the_assumed_bound():
     """The certified fast path assumes the fp32 exp2 instruction is accurate to
     a stated relative error; measure it exhaustively on [-126, 0]."""
