@@ -2667,11 +2667,6 @@ struct RawChunk<uint16_t, true> {
     const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
     return (!PAD || i0 + e < V) ? v : 0.f;
   }
-  // q = onehot(hot) over the chunk's elements (hot < 0: zeros)
-  __device__ __forceinline__ void set_onehot(int hot) {
-    q0 = make_float4(i0 == hot, i0 + 1 == hot, i0 + 2 == hot, i0 + 3 == hot);
-    q1 = make_float4(i0 + 4 == hot, i0 + 5 == hot, i0 + 6 == hot, i0 + 7 == hot);
-  }
 };
 template <>
 struct RawChunk<float, true> {
@@ -2704,10 +2699,6 @@ struct RawChunk<float, true> {
     const float v = k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
     return (!PAD || idx(e) < V) ? v : 0.f;
   }
-  __device__ __forceinline__ void set_onehot(int hot) {
-    q0 = make_float4(idx(0) == hot, idx(1) == hot, idx(2) == hot, idx(3) == hot);
-    q1 = make_float4(idx(4) == hot, idx(5) == hot, idx(6) == hot, idx(7) == hot);
-  }
 };
 template <typename LT>
 struct RawChunk<LT, false> {
@@ -2732,10 +2723,6 @@ struct RawChunk<LT, false> {
   template <bool PAD>
   __device__ __forceinline__ float get_q(int e, int V) const {
     return (!PAD || Lay<LT, false>::index(base, lane, 8 * c + e) < V) ? q[e] : 0.f;
-  }
-  __device__ __forceinline__ void set_onehot(int hot) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = Lay<LT, false>::index(base, lane, 8 * c + e) == hot ? 1.f : 0.f;
   }
 };
 
@@ -2813,22 +2800,18 @@ struct ReqShared {
 // P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
 // interval leaves an element undecided (LDS or global, indexed by tile). With
 // MASK, logits below tau (outside the top-k / top-p kept set) count as -inf.
-// A draft row without a q row (one-hot draft) takes q = onehot(hot), zeros
-// when hot < 0 (a draft token outside the vocabulary).
 template <typename LT, bool VEC, bool MASK>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
                               const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
-                              float tau, int hot) {
+                              float tau) {
   const int lane = threadIdx.x & 63;
   const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
   using Chunk = RawChunk<LT, VEC>;
   Chunk ring[4];
-  const bool onehot = draft && qrow == nullptr;
   auto load = [&](int slot, int jj, int c) {
     // chunks past the wave's last tile re-read the row's last tile (in bounds, unused)
-    ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, qrow != nullptr);
-    if (onehot) ring[slot].set_onehot(hot);
+    ring[slot].load(lrow, qrow, V, min(jj, nt - 1) * kTile, lane, c, draft);
   };
   double es = 0.0, ps = 0.0, qs = 0.0;
   uint64_t und = 0;  // lanes with an undecided element (wave masks: scalar operations)
@@ -2966,12 +2949,13 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
   const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
   const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
-  const int hot = onehot_index(a, draft, d0 + n);
   const int per = (nt + kPassSlices - 1) / kPassSlices;
   const int j0 = sl * per, j1 = min(nt, j0 + per);
   const int64_t o = static_cast<int64_t>(b) * nt;
-  fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, draft, j0 + wave, j1, kPassWaves, tab,
-                                 C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w), hot);
+  // a one-hot draft row needs only the tile sums of e (its residual is p
+  // without x's element, taken out of its tile by the finish kernel)
+  fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1, kPassWaves,
+                                 tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
 }
 
 // Lazy mode, per-request finish: one block per request. Z from the pass's
@@ -3033,8 +3017,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       }
     } else {  // a later row (an undecided accept test turned out accepted): its pass here
       const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
-      fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, m, s, zhi, zlo, draft, wave, nt, kFinishWaves, tab, C, E, P,
-                                     Q, keep_min, hot);
+      fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, m, s, zhi, zlo, qrow != nullptr, wave, nt, kFinishWaves, tab,
+                                     C, E, P, Q, keep_min);
     }
     __syncthreads();
     for (int j = tid; j < nt; j += kFinishNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
@@ -3062,7 +3046,16 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
 
     // ---- tile values: residual (draft row) or p (bonus row, or fallback)
     int mode = draft ? 1 : 0;
-    if (draft) {
+    if (onehot) {
+      // q = onehot(x): the residual max(0, p - q) is p without x's element
+      // (p(x) <= 1), so W_j = E_j / Z except in x's tile, which loses e_x
+      // (computed as in the pass); a token outside the vocabulary removes
+      // nothing
+      const int jx = hot >= 0 ? hot / kTile : -1;
+      const double ex = hot >= 0 ? exp2_neg(fma(static_cast<double>(to_float(lrow[hot])), s, nms), tab) : 0.0;
+      for (int j = tid; j < nt; j += kFinishNT) W[j] = (j == jx ? fmax(0.0, E[j] - ex) : E[j]) * iz;
+      __syncthreads();
+    } else if (draft) {
       if (tid == 0) rs.nund = 0;
       __syncthreads();
       for (int j = tid; j < nt; j += kFinishNT) {
@@ -3078,10 +3071,6 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
         for (int c = 0; c < 4; ++c) {
           float lv[8], qv[8];
           load_chunk<LT, VEC, true>(lrow, qrow, V, base, lane, c, lv, qv);
-          if (onehot) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = Lay<LT, VEC>::index(base, lane, 8 * c + e) == hot ? 1.f : 0.f;
-          }
 #pragma unroll
           for (int g4 = 0; g4 < 8; g4 += kExpW) {
             double ar[kExpW], e[kExpW];
