@@ -319,6 +319,9 @@ def main():
                     help="calls of the top-k / top-p entry point timed after the timed region (0: skip)")
     ap.add_argument("--loop-steps", type=int, default=30,
                     help="steps of the synthetic end-to-end loop measured after the timed region (0: skip)")
+    ap.add_argument("--only-config", choices=OTHER_CONFIGS, default=None,
+                    help="measure only this one of the other workloads (--steps calls) and print its object "
+                         "(for profiling it alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -334,6 +337,9 @@ def main():
     api.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only_config:
+        print(json.dumps(measure_config(args.only_config, args.steps, dev)))
+        return
     w = make_workload(args.workload, 0)
     B, g, V, T = w["B"], w["gamma"], w["V"], w["temperature"]
     if w["dtype"] == "bf16":
