@@ -299,9 +299,14 @@ def measure_filtered(steps, logits, q, x, u, T, ws, stream, top_k=50, top_p=0.9)
     wall = (time.perf_counter() - t0) / steps
     rows_ms, rows_n = api.profile_stop()[api.SV_PROFILE_ROWS]
     B, g = x.shape
+    flags = api.row_records(ws, B * (g + 1))[:, 1].cpu().numpy()
+    read = (flags & api.SV_ROW_UNREAD) == 0
+    tiers = {"rows_read": int(read.sum()),
+             "second_tier": int(((flags & api.SV_ROW_HEAD2) != 0).sum()),
+             "row_select": int(((flags & api.SV_ROW_ROW_SELECT) != 0).sum())}
     return {"top_k": top_k, "top_p": top_p, "steps": steps, "ms_per_call": wall * 1e3,
             "positions_per_s": B * g / wall, "per_row_pass_ms_mean": rows_ms / max(rows_n, 1),
-            "mean_accepted": float(nacc.float().mean().item())}
+            "mean_accepted": float(nacc.float().mean().item()), "threshold_tiers": tiers}
 
 
 def main():
