@@ -2510,48 +2510,49 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
 // then writes the request's outputs.
 
 constexpr int kExpW = 4;  // exps in flight per lane in the fp64 pass
-constexpr int kExp2Tab = 64;  // 2^(j/64), j = 0..63
+constexpr int kExp2Bits = 8;                  // table index bits
+constexpr int kExp2Tab = 1 << kExp2Bits;      // 2^(j/256), j = 0..255 (2 KB of LDS)
+constexpr double kExp2Scale = kExp2Tab;       // 256
+constexpr double kExp2InvScale = -1.0 / kExp2Tab;
 
-// 2^a in fp64 for a <= 0 (or -inf), to about 1 ulp. J = round(64 a) comes out
+// 2^a in fp64 for a <= 0 (or -inf), to about 1 ulp (measured on the host
+// against long double: at most 3.5e-16 relative). J = round(256 a) comes out
 // of one fma with 1.5 * 2^52 (the integer is left in the low word), so
-// a = J / 64 + r with |r| <= 1/128 exactly; J = 64 n + j with 0 <= j < 64;
-// 2^r from its Taylor series to degree 5 (truncation < 4e-17 relative),
-// 2^(j/64) from `tab` (an LDS copy), 2^n by ldexp. Arguments below -1100 (and
-// -inf) give 0.
+// a = J / 256 + r with |r| <= 1/512 exactly; J = 256 n + j with 0 <= j < 256;
+// 2^r from its Taylor series to degree 4 (truncation < 4e-17 relative:
+// (ln 2 / 512)^5 / 5!), 2^(j/256) from `tab` (an LDS copy), 2^n by ldexp.
+// Arguments below -1100 (and -inf) give 0. (A 64-entry table with degree 5
+// is as accurate and one fma slower per element.)
 __device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
   constexpr double kRnd = 6755399441055744.0;  // 1.5 * 2^52
   constexpr double c1 = 0.6931471805599453, c2 = 0.2402265069591007, c3 = 0.05550410866482158,
-                   c4 = 0.009618129107628477, c5 = 0.0013333558146428443;
+                   c4 = 0.009618129107628477;
   a = fmax(a, -1100.0);
-  const double t = fma(a, 64.0, kRnd);
-  const double r = fma(t - kRnd, -0.015625, a);  // a - J / 64, exact
+  const double t = fma(a, kExp2Scale, kRnd);
+  const double r = fma(t - kRnd, kExp2InvScale, a);  // a - J / 256, exact
   const int J = __double2loint(t);
-  double p = fma(c5, r, c4);
-  p = fma(p, r, c3);
+  double p = fma(c4, r, c3);
   p = fma(p, r, c2);
   p = fma(p, r, c1);
   p = fma(p, r, 1.0);
-  return ldexp(p * tab[J & 63], J >> 6);
+  return ldexp(p * tab[J & (kExp2Tab - 1)], J >> kExp2Bits);
 }
 
-// The constants of exp2_neg, held in VGPRs (read from LDS once per thread):
-// an fp64 instruction can take only one scalar operand, so two uniform
-// constants in one fma would otherwise be copied into VGPRs at every use.
-struct Exp2Consts {
-  double rnd, c64, cinv64, lo, c1, c2, c3, c4, c5;
-};
-constexpr int kExp2Consts = 9;
-__device__ __forceinline__ void exp2_consts_init(double* lds) {
-  const double v[kExp2Consts] = {6755399441055744.0, 64.0, -0.015625, -1100.0, 0.6931471805599453,
-                                 0.2402265069591007, 0.05550410866482158, 0.009618129107628477,
-                                 0.0013333558146428443};
-#pragma unroll
-  for (int i = 0; i < kExp2Consts; ++i) lds[i] = v[i];
+// Fill the table of exp2_neg (every thread of the block takes part).
+__device__ __forceinline__ void exp2_table_init(double* tab) {
+  for (int i = threadIdx.x; i < kExp2Tab; i += blockDim.x) tab[i] = exp2(static_cast<double>(i) / kExp2Scale);
 }
-__device__ __forceinline__ Exp2Consts exp2_consts_load(const double* lds) {
-  (void)lds;  // compile-time constants: scalar operands or rematerialised, no VGPRs held
-  return Exp2Consts{6755399441055744.0, 64.0, -0.015625, -1100.0, 0.6931471805599453, 0.2402265069591007,
-                    0.05550410866482158, 0.009618129107628477, 0.0013333558146428443};
+
+// The constants of exp2_neg as fp64 instruction operands: an fp64 instruction
+// can take only one scalar operand, so two uniform constants in one fma would
+// otherwise be copied into VGPRs at every use; as compile-time constants the
+// compiler keeps or rematerialises them without holding VGPRs.
+struct Exp2Consts {
+  double rnd, scale, inv_scale, lo, c1, c2, c3, c4;
+};
+__device__ __forceinline__ Exp2Consts exp2_consts_load() {
+  return Exp2Consts{6755399441055744.0, kExp2Scale, kExp2InvScale, -1100.0, 0.6931471805599453, 0.2402265069591007,
+                    0.05550410866482158, 0.009618129107628477};
 }
 
 // exp2_neg of N arguments at once, in phases (all table reads, then all
@@ -2560,25 +2561,24 @@ template <int N>
 __device__ __forceinline__ void exp2_negN(const double (&a)[N], const double* __restrict__ tab, const Exp2Consts& C,
                                           double (&e)[N]) {
   const double kRnd = C.rnd;
-  const double c1 = C.c1, c2 = C.c2, c3 = C.c3, c4 = C.c4, c5 = C.c5;
+  const double c1 = C.c1, c2 = C.c2, c3 = C.c3, c4 = C.c4;
   double r[N], tv[N];
   int J[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const double ak = fmax(a[k], C.lo);
-    const double t = fma(ak, C.c64, kRnd);
-    r[k] = fma(t - kRnd, C.cinv64, ak);
+    const double t = fma(ak, C.scale, kRnd);
+    r[k] = fma(t - kRnd, C.inv_scale, ak);
     J[k] = __double2loint(t);
-    tv[k] = tab[J[k] & 63];
+    tv[k] = tab[J[k] & (kExp2Tab - 1)];
   }
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    double p = fma(c5, r[k], c4);
-    p = fma(p, r[k], c3);
+    double p = fma(c4, r[k], c3);
     p = fma(p, r[k], c2);
     p = fma(p, r[k], c1);
     p = fma(p, r[k], 1.0);
-    e[k] = ldexp(p * tv[k], J[k] >> 6);
+    e[k] = ldexp(p * tv[k], J[k] >> kExp2Bits);
   }
 }
 
@@ -2943,9 +2943,9 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
   if (!request_range(a, b, d0, d1)) return;
   const int g = d1 - d0;
   const int64_t t0 = static_cast<int64_t>(d0) + b;
-  if (threadIdx.x < kExp2Tab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) / 64.0);
+  exp2_table_init(tab);
   const int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &slot);  // (its barriers also publish tab)
-  const Exp2Consts C = exp2_consts_load(nullptr);
+  const Exp2Consts C = exp2_consts_load();
   const int64_t trow = t0 + n;
   const bool draft = n < g;
   const double4 st = a.rstat[trow];
@@ -2991,8 +2991,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
   const int64_t t0 = static_cast<int64_t>(d0) + b;
   const double s = a.s64;
   const double u_smp = static_cast<double>(a.u[t0 + g]);  // the request's sample uniform
-  if (tid < kExp2Tab) tab[tid] = exp2(static_cast<double>(tid) / 64.0);
-  const Exp2Consts C = exp2_consts_load(nullptr);
+  exp2_table_init(tab);
+  const Exp2Consts C = exp2_consts_load();
 
   int start = 0;
   bool from_pass = true;  // the first open row's tile sums come from the pass kernel
