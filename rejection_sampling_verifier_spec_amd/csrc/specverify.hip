@@ -2787,6 +2787,7 @@ __device__ __forceinline__ void load8qf(const float* __restrict__ q, const float
 __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j == nt - 1 && j * kTile + kTile > V; }
 
 struct ReqShared {
+  double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see request_finish_kernel)
   int first;    // first row not yet accepted
   int nund;     // tiles with undecided elements
   int cross, lastpos;
@@ -2913,6 +2914,7 @@ constexpr int kPassWaves = kPassNT / 64;
 constexpr int kPassSlices = 3;     // blocks per request in the pass kernel
 constexpr int kFinishNT = 256;     // threads per block of the finish kernel
 constexpr int kFinishWaves = kFinishNT / 64;
+static_assert(kFinishWaves == 4, "the finish kernel's in-tile search maps 16 scan lanes to each of four waves");
 
 // One-hot drafts (no q rows): the draft token of draft row d when it lies in
 // the vocabulary, else -1; -1 for a bonus row or when q rows are given.
@@ -3090,9 +3092,9 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       __syncthreads();
     }
     auto tile_val = [&](int j) -> double { return mode == 1 ? W[j] : E[j] * iz; };
-    // ---- the rest is sequential work on one row: wave 0 alone, with wave-level
-    // scans (lanes in token order) and no block barriers
-    if (wave != 0) return;
+    // ---- tile-level search: every wave computes it (the same LDS values in
+    // the same order give identical results in each), with wave-level scans
+    // (lanes in token order) and no block barriers
     // tile-level CDF: lane l owns tiles [l tp, (l + 1) tp)
     const int tp = (nt + 63) / 64;
     const int jlo = min(nt, lane * tp), jhi = min(nt, jlo + tp);
@@ -3145,64 +3147,52 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
         if (j < jt) pl += tile_val(j);
       pb = wave_sum_d(pl);
     }
-    // in-tile search: lane l owns the 32 consecutive elements jt*kTile + 32 l + (0..31),
-    // loaded once (all loads in flight together); the weights are computed
-    // twice from registers (lane sums, then the crossing lane's prefix)
-    const int k0 = jt * kTile + 32 * lane;
-    float lall[4][8], qall[4][8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      load8f<LT, VEC>(lrow, V, k0 + 8 * h, lall[h]);
-      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, k0 + 8 * h, qall[h]);
+    // in-tile search: scan lane l (of wave 0) owns the 32 consecutive elements
+    // jt*kTile + 32 l + (0..31). The four waves compute the tile's weights
+    // once, lane (w, l') the 8 elements of scan lane 16 w + l' / 4 from
+    // 8 (l' % 4), into LDS (weight i of scan lane l at wbuf[i 64 + l]); wave 0
+    // then sums and scans them in token order.
+    {
+      const int L = 16 * wave + (lane >> 2), h = lane & 3;
+      const int kc = jt * kTile + 32 * L + 8 * h;
+      float lv[8], qv[8];
+      load8f<LT, VEC>(lrow, V, kc, lv);
+      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, kc, qv);
       if (mode == 1 && onehot) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qall[h][k] = k0 + 8 * h + k == hot ? 1.f : 0.f;
+        for (int k = 0; k < 8; ++k) qv[k] = kc + k == hot ? 1.f : 0.f;
       }
-      if constexpr (FILTER) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) lall[h][k] = masked(lall[h][k]);
-      }
-    }
-    auto weights8 = [&](int h, double (&w8)[8]) __attribute__((always_inline)) {
-      const float (&lv)[8] = lall[h];
-      const float (&qv)[8] = qall[h];
 #pragma unroll
       for (int g4 = 0; g4 < 8; g4 += kExpW) {
         double ar[kExpW], e[kExpW];
 #pragma unroll
-        for (int k = 0; k < kExpW; ++k) ar[k] = fma(static_cast<double>(lv[g4 + k]), s, nms);
+        for (int k = 0; k < kExpW; ++k) ar[k] = fma(static_cast<double>(masked(lv[g4 + k])), s, nms);
         exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
         for (int k = 0; k < kExpW; ++k) {
           const double p = e[k] * iz;
-          w8[g4 + k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[g4 + k])) : p;
+          rs.wbuf[(8 * h + g4 + k) * 64 + L] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[g4 + k])) : p;
         }
       }
-    };
-    double ls = 0.0;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      double w8[8];
-      weights8(h, w8);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ls += w8[k];
     }
+    __syncthreads();
+    if (wave != 0) return;
+    const int k0 = jt * kTile + 32 * lane;
+    double ls = 0.0;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) ls += rs.wbuf[i * 64 + lane];
     const double lincl = wave_scan_incl_d(ls);
     const double tl = tau - pb;
     int tok = -1, lastpos = -1;
     {
       double c = lincl - ls;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        double w8[8];
-        weights8(h, w8);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          c += w8[k];
-          if (w8[k] > 0.0) {
-            lastpos = k0 + 8 * h + k;
-            if (tok < 0 && c >= tl) tok = k0 + 8 * h + k;
-          }
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const double w = rs.wbuf[i * 64 + lane];
+        c += w;
+        if (w > 0.0) {
+          lastpos = k0 + i;
+          if (tok < 0 && c >= tl) tok = k0 + i;
         }
       }
     }
