@@ -2411,10 +2411,10 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
 // Algorithm 1 stops at the first rejection ([READING] and [VISUAL],
 // Algorithm 1): a row after a position already known to be a certain
 // rejection is not needed and is not read (it is recorded as unread). The
-// host launches positions 0 and 1 first; the second launch then sees every
-// mark those rows set and reads only the rows of requests that survived
-// them (rows whose earlier positions are still undecided are read
-// speculatively).
+// host launches the first positions (as many as fill the chip once: two at
+// 256 requests) first; the second launch then sees every mark those rows
+// set and reads only the rows of requests that survived them (rows whose
+// earlier positions are still undecided are read speculatively).
 // The requests still undecided after positions [0, p1) (no certain rejection
 // there) with a position >= p1, in request order: written by the last block
 // of the first launch to finish, for the second launch. The rows at
@@ -3367,7 +3367,31 @@ size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * size
 // stream logits and q per row and prefer larger blocks (shorter per-row time).
 constexpr int kRowsNTLazy = 512;
 constexpr int kRaggedPositionMajor = 4;  // ragged batches: positions launched position-major
-constexpr int kLazyFirstPositions = 2;   // lazy mode: positions of the first launch
+constexpr int kLazyBlocksPerCU = 2;      // lazy per-row kernel: 512-thread blocks resident per CU
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Positions of the lazy mode's first launch: as many as fill the blocks the
+// chip holds at once (at least one, at most every position launched
+// position-major). A launch of one round gains nothing from stopping early;
+// beyond one round, rows of later positions mostly start before the row that
+// would make them unneeded has finished, and are read for nothing.
+int lazy_first_positions(int B, int pm) {
+  const int resident = kLazyBlocksPerCU * device_cus();
+  const int p = B > 0 ? resident / B : pm;
+  return max(1, min(p, pm));
+}
 constexpr int kRowsNTEager = 512;
 
 template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
@@ -3375,8 +3399,8 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
   if constexpr (EAGER) {
     hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st, a);
   } else {
-    // positions [0, 2), then the rest (with the flat order for ragged batches)
-    const int split = min(kLazyFirstPositions, a.pm);
+    // positions [0, split), then the rest (with the flat order for ragged batches)
+    const int split = lazy_first_positions(a.B, a.pm);
     hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
                        lds, st, a, 0, split, 0);
     const int64_t rest = static_cast<int64_t>(a.B) * (a.pm - split) + (a.cu ? rows : 0);

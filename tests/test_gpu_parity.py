@@ -178,6 +178,25 @@ def test_modes_give_identical_outputs_and_are_deterministic(name, B):
         assert len(unread) == 0 or unread.min() > int(lazy[1][b])
 
 
+@pytest.mark.parametrize("B", [200, 300])
+def test_both_lazy_launches_all_requests(B):
+    """Batches large enough that the default mode splits the rows over its two
+    per-row launches (the first launch holds as many positions as fill the
+    chip once: 2 at B=200, 1 at B=300 on 256 compute units), compared with
+    the oracle on every request: q rows, one-hot drafts, the ragged layout,
+    and top-k / top-p."""
+    gh = _gh()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert max(1, 2 * cus // B) < 6, "the batch must not fit in one launch"
+    w = make_dense_custom(20 + B, B=B, gamma=5, V=1500, dtype="bf16", temperature=0.9)
+    gh.compare(w, gh.run_gpu(w), label=f"B={B} q rows")
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label=f"B={B} one-hot")
+    wr = dense_as_ragged(w)
+    gh.compare(wr, gh.run_gpu(wr), label=f"B={B} ragged")
+    gh.compare(w, gh.run_gpu_filtered(w, 20, 0.9), label=f"B={B} filtered", filt=(20, 0.9))
+
+
 def test_ragged_equals_dense():
     gh = _gh()
     w = make_workload("peaked_bf16", 3, B=10, V=9000)
