@@ -76,7 +76,9 @@ enum sv_status {
  *    a certain rejection is not read (rows whose earlier positions are still
  *    undecided are read speculatively); the residual max(0, p - q) is then
  *    drawn only at each request's first rejection (the logits and q of that
- *    one row are read again).
+ *    one row are read again; with one-hot drafts only its logits: the
+ *    residual is then p without the draft token). Row statistics imply
+ *    SV_FLAG_ALL_RESIDUALS.
  *  SV_FLAG_EAGER: every draft row whose own accept test fails draws its
  *    replacement in the same launch (speculatively; most are unused).
  *  SV_FLAG_ALL_RESIDUALS: every draft row draws its replacement. */
