@@ -311,6 +311,11 @@ __device__ __forceinline__ float lane_f(float v, int l) {
 // by 4 and 8 within the row; every lane ends with its row's total. The four
 // row totals are then combined in a fixed order, so every lane of the wave
 // holds the same, deterministic result.
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
@@ -1394,6 +1399,10 @@ constexpr float kHeadH1 = 12.f;
 constexpr int kHeadFix = 50;  // fraction bits of the head masses: kHeadCap terms <= 1 stay below 2^63
 constexpr int kRungs = 4;
 __constant__ float kRungBelow[kRungs] = {48.f, 32.f, 16.f, 8.f};
+// pass 1 also counts, per wave, the elements at or above c2 = c1 - kCount2 / s:
+// with top-k on and pass 1's head too small, a second head at c2 that fits
+// and holds k elements is gathered in one sweep (no count sweep)
+constexpr float kCount2 = 8.f;
 __constant__ float kRungAbove[kRungs] = {0.25f, 0.5f, 0.75f, 1.f};
 
 struct FilterShared {
@@ -1408,7 +1417,9 @@ struct FilterShared {
   uint32_t head[kHeadCap];              // keys of the head elements
   unsigned long long hfix[kHeadCap];    // their masses 2^((l - m) s64) as fixed point (kHeadFix bits)
   int wcnt[16];                         // per-wave counts
+  int wcnt2[16];                        // pass 1: per-wave counts of the elements >= cut2
   float cut1;                           // pass 1's head cutoff
+  float cut2;                           // pass 1's counted cutoff (cut1 - kCount2 / s)
   int ik, ip;                           // head indices: end of tau_k's tie group, top-p crossing
   int amb;                              // top-p: first tie-group end within the bound of the target
   double zk;                            // exact Z_K (head sum) when top-k is on
@@ -1681,6 +1692,39 @@ __device__ __forceinline__ void head_append_wave(const RawTile<LT, VEC>& r, int 
   }
 }
 
+// head_append_wave for pass 1, which also counts in `cnt2` (per lane) the
+// in-row elements at or above c2 < c; groups of 8 slots without an element
+// at or above c2 are skipped, and the appends run only in groups that hold
+// one at or above c.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void head_append_count_wave(const RawTile<LT, VEC>& r, int base, int V, int lane, float c,
+                                                       float c2, uint32_t* dst, int slice, int& cnt, int& cnt2) {
+  using L = Lay<LT, VEC>;
+  const bool full = base + kTile <= V;
+#pragma unroll
+  for (int g = 0; g < kLaneElems; g += 8) {
+    float gm = r.get(g);
+#pragma unroll
+    for (int k = g + 1; k < g + 8; ++k) gm = fmaxf(gm, r.get(k));
+    if (!__any(gm >= c2)) continue;
+#pragma unroll
+    for (int k = g; k < g + 8; ++k)
+      cnt2 += ((full || L::index(base, lane, k) < V) && r.get(k) >= c2) ? 1 : 0;
+    if (!__any(gm >= c)) continue;
+#pragma unroll
+    for (int k = g; k < g + 8; ++k) {
+      const float v = r.get(k);
+      const bool in = (full || L::index(base, lane, k) < V) && v >= c;
+      const uint64_t mk = __ballot(in);
+      if (mk) {
+        const int at = cnt + static_cast<int>(__popcll(mk & ((1ull << lane) - 1)));
+        if (in && at < slice) dst[at] = order_key(v);
+        cnt += static_cast<int>(__popcll(mk));
+      }
+    }
+  }
+}
+
 // The per-wave slices of the head buffer (counts in fs.wcnt) made
 // contiguous through head2; returns the head size, or kHeadCap + 1 when some
 // slice overflowed (its count above the slice). Called by every thread.
@@ -1709,6 +1753,9 @@ __device__ int compact_slices(FilterShared& fs) {
   __syncthreads();
   return n;
 }
+
+template <typename LT, bool VEC, int NT>
+__device__ int gather_at(const LT* __restrict__ lrow, int V, float cut, FilterShared& fs);
 
 // A head gathered by its own two sweeps, after pass 1 (m known): the first
 // counts, per wave, the elements at or above each of kRungs increasing
@@ -1771,8 +1818,19 @@ __device__ int gather_head(const LT* __restrict__ lrow, int V, const float (&cut
   for (int w = 0; w < kW; ++w) li = max(li, fs.wcnt[w]);
   __syncthreads();
   if (li >= kRungs) return -1;
-  const float cut = cuts[li];
-  // ---- gather into the per-wave slices
+  return gather_at<LT, VEC, NT>(lrow, V, cuts[li], fs);
+}
+
+// The gathering sweep: every element at or above `cut` into the per-wave
+// slices, then made contiguous; returns the head size (kHeadCap + 1 if a
+// slice overflowed).
+template <typename LT, bool VEC, int NT>
+__device__ int gather_at(const LT* __restrict__ lrow, int V, float cut, FilterShared& fs) {
+  constexpr int kW = NT / 64;
+  constexpr int kSlice = kHeadCap / kW;
+  using Raw = RawTile<LT, VEC>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nt = (V + kTile - 1) / kTile;
   int hc = 0;
   {
     Raw ra, rb;
@@ -1982,6 +2040,23 @@ __device__ int head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
                                double& dZt) {
   const int n1 = compact_slices<NT>(fs);  // pass 1's slices (> kHeadCap: one overflowed)
   if (n1 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n1, fs, sc, tau, Zt, dZt)) return 1;
+  // top-k on and pass 1's head too small: the head at pass 1's counted cutoff
+  // when it fits every wave's slice and holds k elements (the top-k set, and
+  // so the top-p crossing within it, lie at or above that cutoff)
+  if (n1 <= kHeadCap && a.top_k > 0 && a.top_k < a.V) {
+    constexpr int kSlice = kHeadCap / (NT / 64);
+    int tot = 0;
+    bool fits = true;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      fits = fits && fs.wcnt2[w] <= kSlice;
+      tot += fs.wcnt2[w];
+    }
+    if (fits && tot >= a.top_k) {
+      const int n2 = gather_at<LT, VEC, NT>(lrow, a.V, fs.cut2, fs);
+      if (n2 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt)) return 2;
+    }
+  }
   // a head of its own: below pass 1's cutoff when that head was too small
   // (the crossing or the k-th element lay below it), above it when it overflowed
   const float cut1 = fs.cut1;
@@ -2211,6 +2286,8 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   float ref = -INFINITY;
   float cut1 = -INFINITY;  // top-k / top-p: pass 1 gathers the head {l >= cut1}
   int hcnt = 0;            // (into per-wave slices, hcnt elements offered by this wave)
+  float cut2 = -INFINITY;  // and counts per lane the elements >= cut2 (hcnt2)
+  int hcnt2 = 0;
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
     const float c = -(ref * s);
@@ -2227,9 +2304,9 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
       a4[k & 3] = fmaf(e, arg, a4[k & 3]);
     }
     if constexpr (FILTER) {
-      if (__any(lm >= cut1))
-        head_append_wave<LT, VEC>(r, base, V, lane, cut1, fsp->head + wave * (kHeadCap / kWaves), kHeadCap / kWaves,
-                                  hcnt);
+      if (__any(lm >= cut2))
+        head_append_count_wave<LT, VEC>(r, base, V, lane, cut1, cut2, fsp->head + wave * (kHeadCap / kWaves),
+                                        kHeadCap / kWaves, hcnt, hcnt2);
     }
     float es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
     float ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
@@ -2266,7 +2343,10 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ref = fmaxf(ref, sh.wmax[w]);
-    if constexpr (FILTER) cut1 = ref - kHeadH1 / s;
+    if constexpr (FILTER) {
+      cut1 = ref - kHeadH1 / s;
+      cut2 = cut1 - kCount2 / s;
+    }
     if (j < nt) {
       while (true) {
         rb.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
@@ -2280,8 +2360,15 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
       }
     }
     if constexpr (FILTER) {
-      if (lane == 0) fsp->wcnt[wave] = hcnt;
-      if (tid == 0) fsp->cut1 = cut1;
+      hcnt2 = wave_sum_i(hcnt2);
+      if (lane == 0) {
+        fsp->wcnt[wave] = hcnt;
+        fsp->wcnt2[wave] = hcnt2;
+      }
+      if (tid == 0) {
+        fsp->cut1 = cut1;
+        fsp->cut2 = cut2;
+      }
     }
   }
   __syncthreads();
