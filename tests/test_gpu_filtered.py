@@ -222,6 +222,31 @@ def test_filtered_full_size_sampled(top_k, top_p):
         assert 0 <= out[b, n] < w["V"] and np.all(out[b, n + 1:] == -1)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_second_head_by_its_count_sweep(dtype):
+    """Rows whose top holds 40 tied maxima, then 30 values 15 below them and
+    100 values 18 below (T = 1, the rest ~N(0, 1)): pass 1's head (within
+    12/s of the max) and its count at 20/s both hold 40 < k = 50 elements, so
+    the second tier runs its count sweep and gathers the lowest cutoff that
+    fits (the one 28/s below the max, 170 elements); no row needs the
+    select over the whole row."""
+    gh = _gh()
+    w = make_dense_custom(23, B=8, gamma=3, V=8192, dtype=dtype, temperature=1.0, logit_sigma=1.0)
+    rng = np.random.default_rng(23)
+    l = w["logits"].reshape(-1, w["V"])
+    for r in range(l.shape[0]):
+        ids = rng.choice(w["V"], 170, replace=False)
+        l[r, ids[:40]], l[r, ids[40:70]], l[r, ids[70:]] = 25.0, 10.0, 7.0
+    if dtype == "bf16":
+        w["logits_bits"] = f32_to_bf16_bits(w["logits"])
+        w["logits"] = bf16_bits_to_f32(w["logits_bits"])
+    for top_k, top_p in ((50, 1.0), (50, 0.9)):
+        gpu = gh.run_gpu_filtered(w, top_k, top_p)
+        gh.compare(w, gpu, filt=(top_k, top_p), label=f"second head {dtype} k{top_k} p{top_p}")
+        t = tier_counts(gpu)
+        assert t["head2"] > 0 and t["row_select"] == 0, t
+
+
 def test_filtered_f32_four_level_select():
     """fp32 logits take the four-level select; 32000 ids, several tiles."""
     gh = _gh()
