@@ -69,44 +69,56 @@ def measured_traffic():
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=256 γ=7 V=128k"
 
 
-def _oracle_chunk(args):
-    import numpy as np
+_CPU_W = None  # the workload the oracle workers read (inherited through fork, not pickled)
 
+
+def _oracle_chunk(job):
+    """Requests [lo, hi) of the workload through the oracle, `reps` times
+    over (the same work each time); returns the last pass's results."""
     import oracle
 
-    logits, q, x, u, T = args
-    n = 0
-    out = []
-    for b in range(len(x)):
-        p_rows = [oracle.target_probs(logits[b, i], T) for i in range(logits.shape[1])]
-        toks, nb = oracle.verify_request(p_rows, [q[b, i] for i in range(q.shape[1])], x[b], u[b])
-        out.append((toks, nb))
-        n += 1
+    lo, hi, reps = job
+    w = _CPU_W
+    logits, q, x, u, T = w["logits"], w["draft_probs"], w["draft_tokens"], w["uniforms"], w["temperature"]
+    for _ in range(reps):
+        out = []
+        for b in range(lo, hi):
+            p_rows = [oracle.target_probs(logits[b, i], T) for i in range(logits.shape[1])]
+            toks, nb = oracle.verify_request(p_rows, [q[b, i] for i in range(q.shape[1])], x[b], u[b])
+            out.append((toks, nb))
     return out
 
 
-def cpu_baseline(w, max_requests: int):
-    """Time the oracle over the first `max_requests` requests with one worker
-    per host core; returns (dict, oracle results)."""
+def cpu_baseline(w, max_requests: int, reps: int):
+    """Time the oracle over the first `max_requests` requests, `reps` passes
+    over them, with one worker per host core (the workers inherit the inputs
+    through fork; each gets a range of requests); returns (dict, oracle
+    results)."""
+    global _CPU_W
     import multiprocessing as mp
 
     import numpy as np
 
+    _CPU_W = w
     nb = min(max_requests, w["B"])
     cores = len(os.sched_getaffinity(0))
     workers = max(1, min(cores, nb))
-    chunks = np.array_split(np.arange(nb), workers)
-    jobs = [(w["logits"][c], w["draft_probs"][c], w["draft_tokens"][c], w["uniforms"][c], w["temperature"])
-            for c in chunks if len(c)]
+    jobs = [(int(c[0]), int(c[-1]) + 1, reps) for c in np.array_split(np.arange(nb), workers) if len(c)]
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(_oracle_chunk, jobs)
     dt = time.perf_counter() - t0
     flat = [r for part in res for r in part]
-    positions = nb * w["gamma"]
+    positions = nb * w["gamma"] * reps
+    # one core: the first few requests in this process
+    n1 = min(8, nb)
+    t1 = time.perf_counter()
+    _oracle_chunk((0, n1, 1))
+    single = n1 * w["gamma"] / (time.perf_counter() - t1)
     return dict(value=positions / dt, unit="positions/s", cores=len(jobs), kind="oracle",
-                sample=f"first {nb} of {w['B']} requests of the same inputs, float64 numpy, "
-                       f"{len(jobs)} worker processes, {dt:.2f} s wall"), flat
+                sample=f"first {nb} of {w['B']} requests of the same inputs, {reps} passes, float64 numpy, "
+                       f"{len(jobs)} worker processes (pool start included), {dt:.2f} s wall",
+                single_core_value=single, single_core_sample=f"first {n1} requests in one process"), flat
 
 
 def measure_loop(steps: int, dev):
@@ -318,7 +330,9 @@ def main():
     ap.add_argument("--flags", type=int, default=0,
                     help="SV_FLAG_* bits passed to the library (0: lazy residuals, 4: eager, 2: all residuals)")
     ap.add_argument("--cpu-requests", type=int, default=256, help="requests in the oracle baseline sample (0: skip)")
-    ap.add_argument("--config-steps", type=int, default=20,
+    ap.add_argument("--cpu-passes", type=int, default=20,
+                    help="passes of the oracle over its sample (about 10 s of CPU work on 16 cores at the default)")
+    ap.add_argument("--config-steps", type=int, default=100,
                     help="calls timed for each of the other workloads after the timed region (0: skip)")
     ap.add_argument("--filtered-steps", type=int, default=30,
                     help="calls of the top-k / top-p entry point timed after the timed region (0: skip)")
@@ -463,7 +477,7 @@ def main():
     if args.loop_steps > 0:
         result["loop"] = measure_loop(args.loop_steps, dev)
     if args.cpu_requests > 0 and q is not None:
-        base, ref = cpu_baseline(w, args.cpu_requests)
+        base, ref = cpu_baseline(w, args.cpu_requests, args.cpu_passes)
         o = out.cpu().numpy()
         na = nacc.cpu().numpy()
         mism = sum(1 for b, (toks, n) in enumerate(ref) if n != na[b] or list(o[b, :n + 1]) != toks)
