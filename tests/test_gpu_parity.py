@@ -6,8 +6,8 @@ import pytest
 import torch
 
 from rejection_sampling_verifier_spec_amd import api
-from rejection_sampling_verifier_spec_amd.workloads import (RECIPES, dense_as_ragged, lattice_uniforms,
-                                                            make_dense_custom, make_workload)
+from rejection_sampling_verifier_spec_amd.workloads import (dense_as_ragged, lattice_uniforms, make_dense_custom,
+                                                            make_workload)
 
 pytestmark = pytest.mark.gpu
 
