@@ -118,8 +118,8 @@ enum sv_status {
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of
- * `vocab_size` tokens: 100 bytes per row for the records, list, counters and
- * lazy-mode statistics, marks and lists, plus 28 * ceil(vocab_size / 2048) bytes
+ * `vocab_size` tokens: 104 bytes per row for the records, list, counters and
+ * lazy-mode statistics, marks and task list, plus 28 * ceil(vocab_size / 2048) bytes
  * per row for fp64 tile sums, each part rounded up to 256 bytes. The greedy
  * entry point needs only the records (8 bytes per row, rounded up to 256).
  * Returns 0 for a negative row count or a vocab_size outside [1, SV_MAX_VOCAB]. */

@@ -462,31 +462,25 @@ struct Task {
 __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__ cu, int B, int gamma,
                                             int ndraft);
 
-// Lazy mode, one launch over positions [p0, p1): blocks 0 .. B (p1 - p0) - 1
-// take position p0 + blk / B of request b = blk % B (all first drafts, then
-// all second drafts, ...); with `flat` (ragged batches, last launch) the rest
-// take the rows at positions >= pm in the flat order.
+// Lazy mode. First launch (tasks == nullptr): block blk takes position
+// blk / B of request b = blk % B (all first drafts, then all second drafts,
+// ...). Second launch: block blk takes task blk of the list the first launch
+// wrote ({request, position}, request by request), if there is one.
 __device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restrict__ cu, int B, int gamma,
-                                                 int ndraft, int p0, int p1, int pm, bool flat,
-                                                 const int* __restrict__ surv, int nsurv) {
+                                                 int ndraft, const int2* __restrict__ tasks, int ntasks) {
   Task t;
-  if (blk >= B * (p1 - p0)) {
-    t = decode_task(blk - B * (p1 - p0), cu, B, gamma, ndraft);
-    if (!flat || t.i < pm) t.valid = false;  // launched position-major
-    return t;
-  }
   t.valid = true;
-  if (surv) {  // second launch: the listed requests' positions, request by request
-    const int k = blk / (p1 - p0);
-    if (k >= nsurv) {
+  if (tasks) {
+    if (blk >= ntasks) {
       t.valid = false;
       return t;
     }
-    t.b = surv[k];
-    t.i = p0 + blk % (p1 - p0);
+    const int2 tk = tasks[blk];
+    t.b = tk.x;
+    t.i = tk.y;
   } else {
     t.b = blk % B;
-    t.i = p0 + blk / B;
+    t.i = blk / B;
   }
   int d0, d1;
   if (cu) {
@@ -581,9 +575,9 @@ struct ProbsArgs {
   ExactEntry* xlist;
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
   int* mark;      // lazy mode, per request: kMarkBase - (first position known to be a certain rejection), or 0
-  int pm;         // lazy mode: positions 0 .. pm - 1 are launched position-major
-  int* surv;      // lazy mode: requests still undecided after the first launch (count at surv_n)
-  int* surv_n;    // lazy mode: [0] the count, [16] the first launch's finished-block counter
+  int pm;         // lazy mode: most positions of the first launch (all of a dense batch)
+  int2* tasks;    // lazy mode: {request, position} of the rows the second launch takes (count at surv_n)
+  int* surv_n;    // lazy mode: [0] the task count, [16] the first launch's finished-block counter
   int top_k;      // filtered lazy mode: keep the top_k largest logits (with ties); off unless 0 < top_k < V
   double top_p;   // filtered lazy mode: keep the smallest top set of mass >= top_p; off when >= 1
 };
@@ -2502,10 +2496,12 @@ __global__ __launch_bounds__(NT) void probs_rows_kernel(ProbsArgs a) {
 // 256 requests) first; the second launch then sees every mark those rows
 // set and reads only the rows of requests that survived them (rows whose
 // earlier positions are still undecided are read speculatively).
-// The requests still undecided after positions [0, p1) (no certain rejection
-// there) with a position >= p1, in request order: written by the last block
-// of the first launch to finish, for the second launch. The rows at
-// positions [p1, pm) of every other request are recorded as unread.
+// The second launch's tasks, written by the last block of the first launch
+// to finish: every row at a position >= p1 of each request still undecided
+// after positions [0, p1) (no certain rejection there), request by request
+// in request order, so that the rows that can matter are dispatched first
+// and no block is launched for a request already decided. The rows at
+// positions >= p1 of every other request are recorded as unread.
 template <int NT>
 __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -2513,7 +2509,7 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
   int base = 0;
   for (int b0 = 0; b0 < a.B; b0 += NT) {
     const int b = b0 + static_cast<int>(threadIdx.x);
-    bool keep = false;
+    int cnt = 0;  // this request's tasks
     if (b < a.B) {
       int d0, d1;
       if (a.cu) {
@@ -2524,18 +2520,28 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
         d1 = d0 + a.gamma;
       }
       const bool ok = !a.cu || (d0 >= 0 && d1 >= d0 && d1 <= a.ndraft);
-      keep = ok && d1 - d0 >= p1 &&
-             __hip_atomic_load(a.mark + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= kMarkBase - p1;
-      if (ok && !keep)
-        for (int i = p1; i <= min(d1 - d0, a.pm - 1); ++i)
+      const int g = d1 - d0;
+      const bool keep = ok && g >= p1 &&
+                        __hip_atomic_load(a.mark + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= kMarkBase - p1;
+      if (keep) {
+        cnt = g + 1 - p1;
+      } else if (ok) {
+        for (int i = p1; i <= g; ++i)
           a.ws[static_cast<int64_t>(d0) + b + i] = make_int2(-1, static_cast<int>(kRowUnread));
+      }
     }
-    const uint64_t m = __ballot(keep);
-    if (lane == 0) sh.wcount[wave] = __popcll(m);
+    // offsets: exclusive scan of the counts over the block (lanes, then waves)
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) sh.wcount[wave] = incl;
     __syncthreads();
-    int off = base;
+    int off = base + incl - cnt;
     for (int w = 0; w < wave; ++w) off += sh.wcount[w];
-    if (keep) a.surv[off + __popcll(m & ((1ull << lane) - 1))] = b;
+    for (int k = 0; k < cnt; ++k) a.tasks[off + k] = make_int2(b, p1 + k);
     for (int w = 0; w < kW; ++w) base += sh.wcount[w];
     __syncthreads();
   }
@@ -2545,14 +2551,16 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
 // (FILTER: at least four waves per SIMD, two blocks per CU as without it;
 // the rare radix-select path of the threshold may then spill)
 template <typename LT, bool VEC, int NT, bool FILTER>
-__global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p0, int p1, int flat) {
+__global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
+  // phase 0: first launch, alone; 1: first launch, a second follows (its last
+  // block lists the tasks); 2: second launch
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
   __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
-  const bool second = p0 > 0;
-  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, p0, p1, a.pm, flat != 0,
-                                  second ? a.surv : nullptr, second ? a.surv_n[0] : 0);
+  const bool second = phase == 2;
+  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, second ? a.tasks : nullptr,
+                                  second ? a.surv_n[0] : 0);
   bool read = t.valid;
   if (t.valid && t.i > 0) {
     if (threadIdx.x == 0)
@@ -2564,8 +2572,8 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
     }
   }
   if (read) probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
-  if (second || a.pm <= p1) return;
-  // first launch: the last block to finish lists the requests the second launch
+  if (phase != 1) return;
+  // first launch: the last block to finish lists the tasks of the second launch
   // reads. Marks and the count are device-scope atomics, each block's mark
   // completed before its count (see probs_row), and the list reads the marks
   // with atomic loads: no cache-wide fence is needed.
@@ -3444,7 +3452,7 @@ WsLayout ws_layout(int64_t rows, int V) {
   l.rstat = l.amb + align256(r * nt * sizeof(int));
   l.mark = l.rstat + align256(r * 4 * sizeof(double));
   l.surv = l.mark + align256(r * sizeof(int));
-  l.total = l.surv + align256(r * sizeof(int));
+  l.total = l.surv + align256(r * sizeof(int2));
   return l;
 }
 size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
@@ -3453,7 +3461,7 @@ size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * size
 // flight with small blocks; the eager modes and the per-request second pass
 // stream logits and q per row and prefer larger blocks (shorter per-row time).
 constexpr int kRowsNTLazy = 512;
-constexpr int kRaggedPositionMajor = 4;  // ragged batches: positions launched position-major
+constexpr int kRaggedFirstMax = 4;  // ragged batches: most positions in the first lazy launch
 constexpr int kLazyBlocksPerCU = 2;      // lazy per-row kernel: 512-thread blocks resident per CU
 
 // Compute units of the current device (cached per device; 256 if the query fails).
@@ -3486,14 +3494,15 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
   if constexpr (EAGER) {
     hipLaunchKernelGGL((probs_rows_kernel<LT, VEC, NT>), dim3(static_cast<unsigned>(rows)), dim3(NT), lds, st, a);
   } else {
-    // positions [0, split), then the rest (with the flat order for ragged batches)
+    // positions [0, split) position-major, then the listed tasks: at most
+    // every later row (every draft row of a ragged batch but one per request)
     const int split = lazy_first_positions(a.B, a.pm);
+    const int64_t rest = a.cu ? static_cast<int64_t>(a.ndraft) : static_cast<int64_t>(a.B) * (a.pm - split);
     hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
-                       lds, st, a, 0, split, 0);
-    const int64_t rest = static_cast<int64_t>(a.B) * (a.pm - split) + (a.cu ? rows : 0);
+                       lds, st, a, split, rest > 0 ? 1 : 0);
     if (rest > 0)
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st,
-                         a, split, a.pm, 1);
+                         a, split, 2);
   }
 }
 
@@ -3519,7 +3528,7 @@ Profiler g_prof;
 
 void prof_record(int id, int which, hipStream_t st) {
   if (!(g_prof.mask & (1u << id)) || g_prof.used[id] >= g_prof.capacity) return;
-  hipEventRecord(g_prof.ev[id][2 * g_prof.used[id] + which], st);
+  (void)hipEventRecord(g_prof.ev[id][2 * g_prof.used[id] + which], st);
   if (which == 1) ++g_prof.used[id];
 }
 
@@ -3594,8 +3603,8 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     return SV_ERR_INVALID_ARGUMENT;
   if (stats && !(T > 0.0)) return SV_ERR_INVALID_ARGUMENT;
   const int64_t rows = static_cast<int64_t>(ndraft) + B;
-  // (the lazy grid of a ragged batch adds kRaggedPositionMajor blocks per request)
-  if (rows + static_cast<int64_t>(kRaggedPositionMajor) * B > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+  // (the first lazy launch of a ragged batch has up to kRaggedFirstMax blocks per request)
+  if (rows + static_cast<int64_t>(kRaggedFirstMax) * B > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
   if (B == 0) return SV_OK;
   if (!logits || !out || !nacc) return SV_ERR_INVALID_ARGUMENT;
   if (ndraft > 0 && !x) return SV_ERR_INVALID_ARGUMENT;
@@ -3640,10 +3649,10 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.top_p = filter ? fa.top_p : 1.0;
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.mark = reinterpret_cast<int*>(wsb + wl.mark);
-    p.surv = reinterpret_cast<int*>(wsb + wl.surv);
+    p.tasks = reinterpret_cast<int2*>(wsb + wl.surv);
     p.surv_n = reinterpret_cast<int*>(wsb + wl.count + 128);
 
-    p.pm = cu ? kRaggedPositionMajor : gamma + 1;
+    p.pm = cu ? kRaggedFirstMax : gamma + 1;
     p.xcount = xcount;
     p.xlist = reinterpret_cast<ExactEntry*>(wsb + wl.list);
     ExactArgs e;
@@ -3705,7 +3714,7 @@ int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity) {
       // timing only: no system-scope fence (cache writeback and invalidate) at
       // each record, which would otherwise slow the work around the events
       if (hipEventCreateWithFlags(&g_prof.ev[id][i], hipEventDisableSystemFence) != hipSuccess) {
-        for (int k = 0; k < i; ++k) hipEventDestroy(g_prof.ev[id][k]);
+        for (int k = 0; k < i; ++k) (void)hipEventDestroy(g_prof.ev[id][k]);
         delete[] g_prof.ev[id];
         g_prof.ev[id] = nullptr;
         spec_verify_profile_stop(t, n);
@@ -3733,7 +3742,7 @@ int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
           rc = SV_ERR_LAUNCH;
         sum += ms;
       }
-      for (int i = 0; i < 2 * g_prof.capacity; ++i) hipEventDestroy(g_prof.ev[id][i]);
+      for (int i = 0; i < 2 * g_prof.capacity; ++i) (void)hipEventDestroy(g_prof.ev[id][i]);
       delete[] g_prof.ev[id];
       g_prof.ev[id] = nullptr;
     }

@@ -52,11 +52,12 @@ def test_status_strings(lib):
 
 def test_workspace_size(lib):
     # records + counters + 48-byte list entries + per-row tile counters + three fp64 and one int
-    # per-tile arrays (nt = ceil(V / 2048)) + per-row {m, Z, bound, shift} + per-request marks;
-    # each part 256-aligned
+    # per-tile arrays (nt = ceil(V / 2048)) + per-row {m, Z, bound, shift} + per-request marks
+    # + the second lazy launch's {request, position} tasks; each part 256-aligned
     assert api.workspace_size(1, 100) == 256 * 11
     assert api.workspace_size(2048, 128256) == (2048 * 8 + 256 + 2048 * 48 + 2048 * 4
-                                                + 3 * 2048 * 63 * 8 + 2048 * 63 * 4 + 2048 * 32 + 2 * 2048 * 4)
+                                                + 3 * 2048 * 63 * 8 + 2048 * 63 * 4 + 2048 * 32 + 2048 * 4
+                                                + 2048 * 8)
     assert lib.spec_verify_workspace_size(-1, 100) == 0
     assert lib.spec_verify_workspace_size(5, 0) == 0
     assert lib.spec_verify_workspace_size(5, (1 << 21) + 1) == 0
