@@ -2882,6 +2882,7 @@ __device__ __forceinline__ void load8qf(const float* __restrict__ q, const float
 __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j == nt - 1 && j * kTile + kTile > V; }
 
 struct ReqShared {
+  double part[4];  // per-wave partial sums (an undecided tile)
   double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see request_finish_kernel)
   int first;    // first row not yet accepted
   int nund;     // tiles with undecided elements
@@ -3163,28 +3164,28 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
         else W[j] = fmax(0.0, P[j] * iz - Q[j]);
       }
       __syncthreads();
-      // tiles with undecided elements, one per wave, summed again with Z
-      for (int k = wave; k < rs.nund; k += kFinishWaves) {
+      // tiles with undecided elements (usually none or one), summed again
+      // with Z by the whole block: wave w takes chunk w of each lane's part
+      for (int k = 0; k < rs.nund; ++k) {
         const int j = ulist[k];
-        const int base = j * kTile;
+        float lv[8], qv[8];
+        load_chunk<LT, VEC, true>(lrow, qrow, V, j * kTile, lane, wave, lv, qv);
         double ws = 0.0;
-        for (int c = 0; c < 4; ++c) {
-          float lv[8], qv[8];
-          load_chunk<LT, VEC, true>(lrow, qrow, V, base, lane, c, lv, qv);
 #pragma unroll
-          for (int g4 = 0; g4 < 8; g4 += kExpW) {
-            double ar[kExpW], e[kExpW];
+        for (int g4 = 0; g4 < 8; g4 += kExpW) {
+          double ar[kExpW], e[kExpW];
 #pragma unroll
-            for (int kk = 0; kk < kExpW; ++kk) ar[kk] = fma(static_cast<double>(masked(lv[g4 + kk])), s, nms);
-            exp2_negN<kExpW>(ar, tab, C, e);
+          for (int kk = 0; kk < kExpW; ++kk) ar[kk] = fma(static_cast<double>(masked(lv[g4 + kk])), s, nms);
+          exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
-            for (int kk = 0; kk < kExpW; ++kk) ws += fmax(0.0, e[kk] * iz - static_cast<double>(qv[g4 + kk]));
-          }
+          for (int kk = 0; kk < kExpW; ++kk) ws += fmax(0.0, e[kk] * iz - static_cast<double>(qv[g4 + kk]));
         }
         ws = wave_sum_d(ws);
-        if (lane == 0) W[j] = ws;
+        if (lane == 0) rs.part[wave] = ws;
+        __syncthreads();
+        if (tid == 0) W[j] = (rs.part[0] + rs.part[1]) + (rs.part[2] + rs.part[3]);
+        __syncthreads();
       }
-      __syncthreads();
     }
     auto tile_val = [&](int j) -> double { return mode == 1 ? W[j] : E[j] * iz; };
     // ---- tile-level search: every wave computes it (the same LDS values in
