@@ -194,15 +194,20 @@ def draft_views(logits, q, x, cu, B, g, V):
 
 
 def copy_ceiling(dev, mib=2048, reps=10):
-    """Practical HBM ceilings as context: a read-only reduction (torch amax
-    over fp32) and a device-to-device copy (bytes read + written)."""
+    """Practical HBM ceilings as context: the library's read-only stream
+    (spec_verify_stream_read: 16-byte loads, every byte once), torch's fp32
+    `amax` (read only) and a device-to-device copy (bytes read + written)."""
     import torch
+
+    from rejection_sampling_verifier_spec_amd import api
 
     n = (mib << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
+    word_sum = torch.empty(1, dtype=torch.int64, device=dev)
     out = {}
-    for name, fn, nbytes in (("read_amax", lambda: a.amax(), 4 * n), ("copy", lambda: b.copy_(a), 8 * n)):
+    for name, fn, nbytes in (("stream_read", lambda: api.stream_read(a, out=word_sum), 4 * n),
+                             ("read_amax", lambda: a.amax(), 4 * n), ("copy", lambda: b.copy_(a), 8 * n)):
         fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()

@@ -140,6 +140,16 @@ int spec_verify_version(void);
 int spec_verify_selftest_exp2(double* max_rel_err, void* stream);
 double spec_verify_exp2_error_bound(void);
 
+/* Benchmark context: a read-only stream of known size. Reads `bytes` of
+ * device memory at `src` once, with 16-byte loads, and writes the sum of its
+ * 32-bit words (as unsigned, modulo 2^64) to *word_sum (device pointer to
+ * one 64-bit integer); its rate is the practical HBM read ceiling the
+ * verifier's streaming kernels are measured against. Requires `src` 16-byte
+ * aligned, `bytes` a multiple of 16 (0 allowed), `word_sum` not NULL;
+ * otherwise SV_ERR_INVALID_ARGUMENT, and nothing is launched. Asynchronous on
+ * `stream`; allocates nothing. */
+int spec_verify_stream_read(const void* src, size_t bytes, unsigned long long* word_sum, void* stream);
+
 /* Benchmark diagnostics: time kernels of the probabilistic entry points with
  * HIP events that the library records on the launch stream right before and
  * right after each launch of a selected kernel.

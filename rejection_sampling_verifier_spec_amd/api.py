@@ -38,7 +38,7 @@ SV_PROFILE_REQUEST = 1
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
            "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
            "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop",
-           "spec_verify_probs_filtered", "spec_verify_ragged_filtered")
+           "spec_verify_probs_filtered", "spec_verify_ragged_filtered", "spec_verify_stream_read")
 
 _lib = None
 
@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_version.restype = ctypes.c_int
     lib.spec_verify_selftest_exp2.argtypes = [vp, vp]
     lib.spec_verify_selftest_exp2.restype = ctypes.c_int
+    lib.spec_verify_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.spec_verify_stream_read.restype = ctypes.c_int
     lib.spec_verify_exp2_error_bound.argtypes = []
     lib.spec_verify_exp2_error_bound.restype = ctypes.c_double
     lib.spec_verify_profile_start.argtypes = [u32, i32]
@@ -294,6 +296,22 @@ def selftest_exp2(device=None, stream=None):
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_selftest_exp2")
     return float(out.item()), float(lib.spec_verify_exp2_error_bound())
+
+
+def stream_read(buf, out=None, stream=None):
+    """Read the device buffer `buf` (contiguous, 16-byte aligned, a multiple of
+    16 bytes) once; returns a one-element int64 tensor holding the sum of its
+    32-bit words as unsigned integers modulo 2^64 (bit pattern)."""
+    lib = load()
+    dev = buf.device
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    out = torch.empty(1, dtype=torch.int64, device=dev) if out is None else out
+    rc = lib.spec_verify_stream_read(_ptr(buf), nbytes, _ptr(out), _stream(dev, stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_stream_read")
+    return out
 
 
 def profile_start(kernels=(SV_PROFILE_ROWS, SV_PROFILE_REQUEST), capacity=1024):

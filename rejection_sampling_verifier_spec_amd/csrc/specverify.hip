@@ -3396,6 +3396,45 @@ __global__ __launch_bounds__(kGreedyNT) void greedy_rows_kernel(GreedyArgs a) {
 // self-check of the exp2 accuracy the fast path's error bound assumes
 
 __global__ void zero_double_kernel(double* p) { *p = 0.0; }
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+
+// Read-only stream (benchmark context): each step a block reads four
+// consecutive 4 KB pieces (16-byte loads, four in flight per thread), then
+// moves on by the grid's span; the 32-bit words are summed per thread, per
+// wave, per block, then one atomic add per block. Two blocks per CU with
+// block-contiguous steps measured 6.4 TB/s on 2 GiB; grid-stride single
+// loads at 4-32 blocks per CU, 5.1-5.3 TB/s.
+constexpr int kStreamNT = 256;
+constexpr int kStreamBlocksPerCU = 2;
+__global__ __launch_bounds__(kStreamNT) void stream_read_kernel(const uint4* __restrict__ src, size_t n,
+                                                                unsigned long long* word_sum) {
+  __shared__ unsigned long long part[kStreamNT / 64];
+  unsigned long long acc = 0;
+  auto add = [&](const uint4& v) {
+    acc += static_cast<unsigned long long>(v.x) + v.y + static_cast<unsigned long long>(v.z) + v.w;
+  };
+  const size_t step = static_cast<size_t>(gridDim.x) * kStreamNT * 4;
+  size_t j = static_cast<size_t>(blockIdx.x) * kStreamNT * 4 + threadIdx.x;
+  for (; j + 3 * kStreamNT < n; j += step) {
+    const uint4 a = src[j], b = src[j + kStreamNT], c = src[j + 2 * kStreamNT], d = src[j + 3 * kStreamNT];
+    add(a);
+    add(b);
+    add(c);
+    add(d);
+  }
+  for (int k = 0; k < 4; ++k)
+    if (j + k * kStreamNT < n) add(src[j + k * kStreamNT]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+#pragma unroll
+    for (int w = 0; w < kStreamNT / 64; ++w) t += part[w];
+    atomicAdd(word_sum, t);
+  }
+}
 
 // Relative error of the hardware exp2 for every fp32 input in [-126, 0]
 // (bit patterns 0x80000000 .. 0xC2FC0000), against fp64 exp2; the maximum is
@@ -3762,6 +3801,23 @@ int spec_verify_selftest_exp2(double* max_rel_err, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(zero_double_kernel, dim3(1), dim3(1), 0, st, max_rel_err);
   hipLaunchKernelGGL(exp2_error_kernel, dim3(2048), dim3(kNT), 0, st, max_rel_err);
+  return finish_launch();
+}
+
+int spec_verify_stream_read(const void* src, size_t bytes, unsigned long long* word_sum, void* stream) {
+  if (!word_sum || (bytes % 16) != 0 || (bytes > 0 && (!src || !aligned16(src)))) return SV_ERR_INVALID_ARGUMENT;
+  (void)hipGetLastError();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, st, word_sum);
+  const size_t n = bytes / 16;
+  if (n > 0) {
+    const size_t want = (n + 4 * kStreamNT - 1) / (4 * kStreamNT);
+    const size_t grid = want < static_cast<size_t>(kStreamBlocksPerCU) * device_cus()
+                            ? want
+                            : static_cast<size_t>(kStreamBlocksPerCU) * device_cus();
+    hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(kStreamNT), 0, st,
+                       static_cast<const uint4*>(src), n, word_sum);
+  }
   return finish_launch();
 }
 

@@ -150,6 +150,16 @@ def test_ragged_filtered_validation(lib):
     assert r(FAKE, 1, FAKE, FAKE, FAKE, FAKE, 0, 0, 100, 1.0, 5, 0.9, FAKE, FAKE, FAKE, 0, None) == 0
 
 
+def test_stream_read_validation(lib):
+    """Rejected on the host before anything is launched: no result pointer, a
+    size that is not a multiple of 16, a source that is not 16-byte aligned."""
+    f = lib.spec_verify_stream_read
+    assert f(FAKE, 16, None, None) == -1
+    assert f(FAKE, 15, FAKE, None) == -1
+    assert f(ctypes.c_void_p(0x1004), 16, FAKE, None) == -1
+    assert f(None, 16, FAKE, None) == -1
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(api, "_lib", None)
     monkeypatch.setattr(api, "LIB_PATH", "/nonexistent/libspecverify.so")

@@ -366,6 +366,18 @@ def test_largest_vocabulary(dtype):
     gh.compare(w, gh.run_gpu_filtered(w, 50, 0.9), label=f"V=2^21 {dtype} filtered", filt=(50, 0.9))
 
 
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 48, (64 << 20) + 16 * 1001])
+def test_stream_read_sums_every_word(nbytes):
+    """The read-only stream behind the bench's HBM ceiling reads every byte
+    once: its word sum equals numpy's (uint32 words, modulo 2^64)."""
+    rng = np.random.default_rng(nbytes % 9973)
+    host = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda:0")
+    got = int(api.stream_read(buf).cpu().numpy().view(np.uint64)[0])
+    want = int(host.astype(np.uint64).sum(dtype=np.uint64))
+    assert got == want
+
+
 def test_hardware_exp2_within_the_assumed_bound():
     """The certified fast path assumes the fp32 exp2 instruction is accurate to
     a stated relative error; measure it exhaustively on [-126, 0]."""
