@@ -3030,11 +3030,16 @@ struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the 
 // slice of the deciding row's tiles.
 // Lazy mode, per-request pass: kPassSlices blocks per request, each over a
 // slice of the deciding row's tiles.
-template <typename LT, bool VEC, bool FILTER>
-__global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, PassArrays pa) {
+// HASQ = false (one-hot drafts, no q rows): every deciding row needs only its
+// tile sums of e, and the kernel is built without the residual's per-element
+// work (fewer registers, more waves per SIMD).
+constexpr int kPassSlicesE = 3;  // blocks per request of the e-only pass (HASQ = false)
+template <typename LT, bool VEC, bool FILTER, bool HASQ = true>
+__global__ __launch_bounds__(kPassNT, HASQ ? 1 : 4) void request_pass_kernel(ProbsArgs a, PassArrays pa) {
+  constexpr int kSl = HASQ ? kPassSlices : kPassSlicesE;
   __shared__ double tab[kExp2Tab];
   __shared__ int slot;
-  const int b = blockIdx.x / kPassSlices, sl = blockIdx.x % kPassSlices;
+  const int b = blockIdx.x / kSl, sl = blockIdx.x % kSl;
   const int V = a.V, nt = (V + kTile - 1) / kTile;
   const int wave = threadIdx.x >> 6;
   int d0, d1;
@@ -3050,13 +3055,17 @@ __global__ __launch_bounds__(kPassNT) void request_pass_kernel(ProbsArgs a, Pass
   const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
   const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
-  const int per = (nt + kPassSlices - 1) / kPassSlices;
+  const int per = (nt + kSl - 1) / kSl;
   const int j0 = sl * per, j1 = min(nt, j0 + per);
   const int64_t o = static_cast<int64_t>(b) * nt;
   // a one-hot draft row needs only the tile sums of e (its residual is p
   // without x's element, taken out of its tile by the finish kernel)
-  fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1, kPassWaves,
-                                 tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
+  if constexpr (HASQ)
+    fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
+                                   kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
+  else
+    fp64_row_pass<LT, VEC, FILTER>(lrow, nullptr, V, nt, st.x, a.s64, zhi, zlo, false, j0 + wave, j1, kPassWaves,
+                                   tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
 }
 
 // Lazy mode, per-request finish: one block per request. Z from the pass's
@@ -3550,8 +3559,12 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
 // per request), then one block per request decides it and writes the outputs.
 template <typename LT, bool VEC, bool FILTER>
 void launch_request(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2, hipStream_t st) {
-  hipLaunchKernelGGL((request_pass_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
-                     dim3(kPassNT), 0, st, a, pa);
+  if (!FILTER && a.q == nullptr)
+    hipLaunchKernelGGL((request_pass_kernel<LT, VEC, false, false>), dim3(static_cast<unsigned>(a.B) * kPassSlicesE),
+                       dim3(kPassNT), 0, st, a, pa);
+  else
+    hipLaunchKernelGGL((request_pass_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
+                       dim3(kPassNT), 0, st, a, pa);
   hipLaunchKernelGGL((request_finish_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
                      st, a, sel, pa);
 }
