@@ -321,6 +321,20 @@ def test_extreme_uniforms_and_ties():
     gh.compare(wg, gh.run_gpu(wg), label="greedy ties")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [0.02, 0.1, 5.0, 50.0])
+def test_extreme_temperatures(dtype, T):
+    """Very low temperatures (p nearly one-hot: residual masses near the 1e-8
+    fallback, exp arguments far below 0) and very high ones (p nearly flat),
+    with q rows, one-hot drafts, and top-k / top-p."""
+    gh = _gh()
+    w = make_dense_custom(int(1000 * T) % 97 + 30, B=24, gamma=3, V=5000, dtype=dtype, temperature=T)
+    gh.compare(w, gh.run_gpu(w), label=f"T={T} {dtype}")
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label=f"T={T} {dtype} one-hot")
+    gh.compare(w, gh.run_gpu_filtered(w, 20, 0.9), label=f"T={T} {dtype} filtered", filt=(20, 0.9))
+
+
 def test_out_of_range_draft_token_is_rejected():
     gh = _gh()
     w = make_dense_custom(10, B=4, gamma=2, V=1000, dtype="f32", temperature=1.0)
