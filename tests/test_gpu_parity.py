@@ -197,6 +197,33 @@ def test_both_lazy_launches_all_requests(B):
     gh.compare(w, gh.run_gpu_filtered(w, 20, 0.9), label=f"B={B} filtered", filt=(20, 0.9))
 
 
+def test_ragged_long_requests_over_both_launches():
+    """A ragged batch of 300 requests with 0 to 24 drafts each and drafts
+    close to the target (most accepted), so that the second per-row launch
+    takes long task lists reaching deep positions; every request compared."""
+    gh = _gh()
+    rng = np.random.default_rng(52)
+    B, G, V = 300, 24, 1500
+    d = make_dense_custom(52, B=B, gamma=G, V=V, dtype="bf16", temperature=1.0, q_sigma=0.05)
+    gb = rng.integers(0, G + 1, B)
+    cu = np.concatenate([[0], np.cumsum(gb)]).astype(np.int32)
+    T = int(cu[-1])
+    rows = [np.r_[np.arange(g), G] for g in gb]  # a request's draft rows, then a target row as its bonus row
+    l = np.concatenate([d["logits"][b, r] for b, r in enumerate(rows)])
+    bits = np.concatenate([d["logits_bits"][b, r] for b, r in enumerate(rows)])
+    q = np.concatenate([d["draft_probs"][b, :g] for b, g in enumerate(gb)])
+    x = np.concatenate([d["draft_tokens"][b, :g] for b, g in enumerate(gb)])
+    u = np.concatenate([d["uniforms"][b, r] for b, r in enumerate(rows)])
+    w = dict(kind="ragged", B=B, V=V, dtype="bf16", temperature=1.0, logits=l, logits_bits=bits,
+             draft_probs=q, draft_tokens=x, uniforms=u, cu=cu, max_gamma=G)
+    assert T + B == len(l)
+    out, nacc, _, _ = gpu = gh.run_gpu(w)
+    gh.compare(w, gpu, label="ragged long")
+    assert nacc.max() >= 10  # deep positions were reached
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label="ragged long one-hot")
+
+
 def test_ragged_equals_dense():
     gh = _gh()
     w = make_workload("peaked_bf16", 3, B=10, V=9000)
