@@ -87,9 +87,12 @@ enum sv_status {
 #define SV_FLAG_EAGER 0x4u         /* draw the replacement of every locally rejected draft row */
 
 /* Workspace: device memory of spec_verify_workspace_size() bytes, 256-byte
- * aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call leaves it ready for
- * the next one. One workspace per call in flight (calls that share one on
- * different streams race). It starts with one 8-byte record per target row,
+ * aligned, ZERO-FILLED BEFORE ITS FIRST USE AND AGAIN WHENEVER A CALL USES
+ * IT WITH ANOTHER NUMBER OF TARGET ROWS OR VOCABULARY SIZE than the call
+ * before (where each part lies depends on both; a greedy call writes only the
+ * records, but zero-fill after one as well); every call leaves it ready for
+ * the next one with the same rows and vocabulary size. One workspace per call
+ * in flight (calls that share one on different streams race). It starts with one 8-byte record per target row,
  * {int32 token, uint32 row_flags} (documented for diagnostics), followed by
  * the list, counters and fp64 tile sums of the rows recomputed in fp64 (the
  * counters return to zero at the end of every call that completes; a call

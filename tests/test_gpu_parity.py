@@ -224,6 +224,42 @@ def test_ragged_long_requests_over_both_launches():
     gh.compare(wo, gh.run_gpu(wo), label="ragged long one-hot")
 
 
+def test_one_workspace_across_calls_of_every_kind():
+    """One workspace through a sequence of calls of different kinds and
+    shapes, each twice: every result equals that of a fresh workspace. The
+    library leaves the workspace ready for the next call with the same rows
+    and vocabulary size; the binding zero-fills it when those change (a call
+    with another layout can leave data where this one keeps its marks)."""
+    gh = _gh()
+    big = make_workload("peaked_bf16", 5, B=300, V=3000)  # two per-row launches (p1 = 1)
+    small = make_workload("peaked_bf16", 6, B=8, V=9000)   # one launch
+    rag = make_workload("ragged_bf16", 7, B=40, V=5000)
+    oh = dict(make_workload("peaked_bf16", 8, B=64, V=4000), draft_probs=None)
+    rows = max(big["B"] * (big["gamma"] + 1), len(rag["logits"]))
+    ws = torch.zeros(api.workspace_size(rows, 9000), dtype=torch.uint8, device="cuda:0")
+
+    def call(w, fresh, kind):
+        t = gh.dev_inputs(w)
+        k = {} if fresh else {"workspace": ws}
+        if kind == "filtered":
+            o, n, _ = api.verify_probs_filtered(t["logits"], t["q"], t["x"], t["u"], w["temperature"], 20, 0.9, **k)
+        elif kind == "greedy":
+            o, n, _ = api.verify_greedy(t["logits"], t["x"], **k)
+        elif w["kind"] == "ragged":
+            o, n, _, _ = api.verify_ragged(t["logits"], t["q"], t["x"], t["cu"], t["u"], w["temperature"], **k)
+        else:
+            o, n, _, _ = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"], **k)
+        torch.cuda.synchronize()
+        return o.cpu().numpy(), n.cpu().numpy()
+
+    seq = [(big, "probs"), (small, "probs"), (rag, "probs"), (big, "filtered"), (oh, "probs"), (big, "greedy"),
+           (small, "filtered"), (big, "probs")]
+    for w, kind in seq + seq:
+        o1, n1 = call(w, False, kind)
+        o2, n2 = call(w, True, kind)
+        assert np.array_equal(o1, o2) and np.array_equal(n1, n2), kind
+
+
 def test_ragged_equals_dense():
     gh = _gh()
     w = make_workload("peaked_bf16", 3, B=10, V=9000)
