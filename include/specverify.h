@@ -87,17 +87,16 @@ enum sv_status {
 #define SV_FLAG_EAGER 0x4u         /* draw the replacement of every locally rejected draft row */
 
 /* Workspace: device memory of spec_verify_workspace_size() bytes, 256-byte
- * aligned, ZERO-FILLED BEFORE ITS FIRST USE AND AGAIN WHENEVER A CALL USES
- * IT WITH ANOTHER NUMBER OF TARGET ROWS OR VOCABULARY SIZE than the call
- * before (where each part lies depends on both; a greedy call writes only the
- * records, but zero-fill after one as well); every call leaves it ready for
- * the next one with the same rows and vocabulary size. One workspace per call
- * in flight (calls that share one on different streams race). It starts with one 8-byte record per target row,
- * {int32 token, uint32 row_flags} (documented for diagnostics), followed by
- * the list, counters and fp64 tile sums of the rows recomputed in fp64 (the
- * counters return to zero at the end of every call that completes; a call
- * that was never run to completion leaves the workspace to be zero-filled
- * again). row_flags bits: */
+ * aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call that completes
+ * leaves it ready for the next one, of any kind, row count or vocabulary
+ * size (the counters sit at a fixed offset and return to zero; per-request
+ * state is cleared by the call that uses it). One workspace per call in
+ * flight (calls that share one on different streams race); a call that was
+ * never run to completion leaves the workspace to be zero-filled again. It
+ * starts with a 256-byte block of counters, then one 8-byte record per target
+ * row, {int32 token, uint32 row_flags} (documented for diagnostics), then the
+ * list and fp64 tile sums of the rows recomputed in fp64 and the lazy mode's
+ * state. row_flags bits: */
 #define SV_ROW_ACCEPTED 0x1u  /* the row's own accept test passed */
 #define SV_ROW_EXACT 0x2u     /* the row was recomputed on the fp64 path */
 #define SV_ROW_RESIDUAL 0x4u  /* the row's replacement token was drawn (q read in full) */
@@ -124,7 +123,8 @@ enum sv_status {
  * `vocab_size` tokens: 104 bytes per row for the records, list, counters and
  * lazy-mode statistics, marks and task list, plus 28 * ceil(vocab_size / 2048) bytes
  * per row for fp64 tile sums, each part rounded up to 256 bytes. The greedy
- * entry point needs only the records (8 bytes per row, rounded up to 256).
+ * entry point needs only the counters and the records (256 bytes, then 8
+ * bytes per row rounded up to 256).
  * Returns 0 for a negative row count or a vocab_size outside [1, SV_MAX_VOCAB]. */
 size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size);
 

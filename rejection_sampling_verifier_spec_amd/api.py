@@ -131,26 +131,15 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-_WS_LAYOUT = {}  # workspace address -> the layout it was last used with (host-side bookkeeping only)
-
-
-def _workspace(rows, vocab, device, workspace, stream=None, layout=None):
-    """The library needs a zero-filled workspace on first use and leaves it
-    ready for the next call with the same layout (target rows and vocabulary
-    size; greedy calls use the records alone). A fresh workspace is allocated
-    zeroed; a given one is zeroed here, on the launch stream, when its layout
-    changes."""
+def _workspace(rows, vocab, device, workspace):
+    """The library needs a zero-filled workspace on first use (it leaves it
+    ready for the next call, of any kind and shape); a fresh one is allocated
+    zeroed."""
     need = workspace_size(rows, vocab)
-    key = (int(rows), int(vocab)) if layout is None else layout
     if workspace is None:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+        workspace = torch.zeros(max(need, 512), dtype=torch.uint8, device=device)
     elif workspace.numel() < need:
         raise ValueError(f"workspace of {workspace.numel()} bytes, {need} needed")
-    elif _WS_LAYOUT.get(workspace.data_ptr()) not in (None, key):
-        zs = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.current_stream(device)
-        with torch.cuda.stream(zs):
-            workspace.zero_()
-    _WS_LAYOUT[workspace.data_ptr()] = key
     return workspace, need
 
 
@@ -176,7 +165,7 @@ def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, flags
     out = torch.empty((B, g1), dtype=torch.int64, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(B * g1, V, dev, workspace, stream)
+    workspace, need = _workspace(B * g1, V, dev, workspace)
     rc = lib.spec_verify_probs(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(out), _ptr(nacc),
                                _ptr(stats), _ptr(workspace), workspace.numel(), _stream(dev, stream))
@@ -197,7 +186,7 @@ def verify_greedy(logits, draft_tokens, workspace=None, stream=None):
         raise ValueError("draft_tokens must be [B, gamma]")
     out = torch.empty((B, g1), dtype=torch.int64, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(B * g1, V, dev, workspace, stream, layout=("records", B * g1))
+    workspace, need = _workspace(B * g1, V, dev, workspace)
     rc = lib.spec_verify_greedy(_ptr(logits), _dtype_code(logits), _ptr(draft_tokens), B, g, V, _ptr(out),
                                 _ptr(nacc), _ptr(workspace), workspace.numel(), _stream(dev, stream))
     if rc != 0:
@@ -227,7 +216,7 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
     out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
     nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
     stats = torch.empty((T + nb, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(T + nb, V, dev, workspace, stream)
+    workspace, need = _workspace(T + nb, V, dev, workspace)
     rc = lib.spec_verify_ragged(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                 _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature), int(flags),
                                 _ptr(out), _ptr(nacc), _ptr(stats), _ptr(workspace), workspace.numel(),
@@ -258,7 +247,7 @@ def verify_probs_filtered(logits, draft_probs, draft_tokens, uniforms, temperatu
         raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
     out = torch.empty((B, g1), dtype=torch.int64, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(B * g1, V, dev, workspace, stream)
+    workspace, need = _workspace(B * g1, V, dev, workspace)
     rc = lib.spec_verify_probs_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                         _ptr(uniforms), B, g, V, float(temperature), int(top_k), float(top_p),
                                         _ptr(out), _ptr(nacc), _ptr(workspace), workspace.numel(),
@@ -288,7 +277,7 @@ def verify_ragged_filtered(logits, draft_probs, draft_tokens, cu_num_draft_token
         raise ValueError("draft_probs must be [T, V]")
     out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
     nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(T + nb, V, dev, workspace, stream)
+    workspace, need = _workspace(T + nb, V, dev, workspace)
     rc = lib.spec_verify_ragged_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
                                          _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature),
                                          int(top_k), float(top_p), _ptr(out), _ptr(nacc), _ptr(workspace),
@@ -346,7 +335,11 @@ def profile_stop():
     return {SV_PROFILE_ROWS: (float(total[0]), int(count[0])), SV_PROFILE_REQUEST: (float(total[1]), int(count[1]))}
 
 
+RECORDS_OFFSET = 256  # the records follow a 256-byte block of counters
+
+
 def row_records(workspace, num_target_rows):
     """Diagnostics: the per-row {token, row_flags} records the last call left
     in `workspace` (int32 [rows, 2])."""
-    return workspace[: num_target_rows * 8].view(torch.int32).view(num_target_rows, 2)
+    rec = workspace[RECORDS_OFFSET: RECORDS_OFFSET + num_target_rows * 8]
+    return rec.view(torch.int32).view(num_target_rows, 2)

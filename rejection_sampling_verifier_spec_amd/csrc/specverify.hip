@@ -573,6 +573,7 @@ struct ProbsArgs {
   uint32_t flags;
   int* xcount;    // list of rows for the fp64 path (see ExactArgs)
   ExactEntry* xlist;
+  int* xdone;     // the list's per-row finished-tile counters (zeroed when a row is listed)
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
   int* mark;      // lazy mode, per request: kMarkBase - (first position known to be a certain rejection), or 0
   int pm;         // lazy mode: most positions of the first launch (all of a dense batch)
@@ -1151,6 +1152,7 @@ __device__ __forceinline__ void flag_exact(const ProbsArgs& a, const Task& t, ui
     en.m = m;
     en.pad0 = en.pad1 = 0;
     a.xlist[pos] = en;
+    a.xdone[pos] = 0;  // (the fp64 kernel, a later launch, counts from zero)
   }
 }
 
@@ -2562,7 +2564,15 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
   const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, second ? a.tasks : nullptr,
                                   second ? a.surv_n[0] : 0);
   bool read = t.valid;
-  if (t.valid && t.i > 0) {
+  // The request's mark starts at zero in every call: its position-0 block (in
+  // the first launch) clears it before anything else. Blocks of the first
+  // launch therefore never read marks (its rows start in one round anyway);
+  // a mark raised there before the clear is lost, which only leaves a row to
+  // be read that could have been skipped. The second launch and the task
+  // list read marks after the first launch has completed.
+  if (!second && t.valid && t.i == 0 && threadIdx.x == 0)
+    __hip_atomic_store(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (second && t.valid && t.i > 0) {
     if (threadIdx.x == 0)
       sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
     __syncthreads();
@@ -3088,7 +3098,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
   int* ulist = reinterpret_cast<int*>(rbuf + 4 * nt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
-  if (tid == 0) a.mark[b] = 0;  // the per-row kernel has finished: ready for the next call
+
   int d0, d1;
   if (!request_range(a, b, d0, d1)) {
     if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
@@ -3490,9 +3500,12 @@ WsLayout ws_layout(int64_t rows, int V) {
   WsLayout l;
   const size_t nt = static_cast<size_t>((V + kTile - 1) / kTile);
   const size_t r = static_cast<size_t>(rows);
-  l.rec = 0;
-  l.count = align256(r * sizeof(int2));  // list count at +0, finished rows at +64, survivors at +128
-  l.list = l.count + 256;
+  // the counters first, at the same offset for every row count and
+  // vocabulary size, so that whatever a call of another shape left elsewhere
+  // never lands on them; then the records
+  l.count = 0;  // list count at +0, finished rows at +64, task count at +128, first-launch count at +192
+  l.rec = 256;
+  l.list = l.rec + align256(r * sizeof(int2));
   l.done = l.list + align256(r * sizeof(ExactEntry));
   l.etile = l.done + align256(r * sizeof(int));
   l.ptile = l.etile + align256(r * nt * sizeof(double));
@@ -3504,7 +3517,7 @@ WsLayout ws_layout(int64_t rows, int V) {
   l.total = l.surv + align256(r * sizeof(int2));
   return l;
 }
-size_t ws_bytes(int64_t rows) { return align256(static_cast<size_t>(rows) * sizeof(int2)); }
+size_t ws_bytes(int64_t rows) { return 256 + align256(static_cast<size_t>(rows) * sizeof(int2)); }
 
 // Block sizes: the lazy first pass reads logits only and keeps more rows in
 // flight with small blocks; the eager modes and the per-request second pass
@@ -3669,7 +3682,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     return SV_ERR_WORKSPACE;
   (void)hipGetLastError();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int2* wsp = static_cast<int2*>(ws);
+  int2* wsp = reinterpret_cast<int2*>(static_cast<char*>(ws) + wl.rec);
 
   char* wsb = static_cast<char*>(ws);
   int* xcount = greedy ? nullptr : reinterpret_cast<int*>(wsb + wl.count);
@@ -3708,6 +3721,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.pm = cu ? kRaggedFirstMax : gamma + 1;
     p.xcount = xcount;
     p.xlist = reinterpret_cast<ExactEntry*>(wsb + wl.list);
+    p.xdone = reinterpret_cast<int*>(wsb + wl.done);
     ExactArgs e;
     e.count = xcount;
     e.finished = reinterpret_cast<int*>(wsb + wl.count + 64);
