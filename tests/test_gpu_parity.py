@@ -260,6 +260,38 @@ def test_one_workspace_across_calls_of_every_kind():
         assert np.array_equal(o1, o2) and np.array_equal(n1, n2), kind
 
 
+def test_concurrent_streams_with_their_own_workspaces():
+    """Calls in flight together on two streams, each with its own workspace
+    (the library keeps no other device state): results equal those of the
+    same calls made one at a time."""
+    gh = _gh()
+    wa = make_workload("peaked_bf16", 9, B=300, V=3000)
+    wb = dict(make_workload("onehot_bf16", 9, B=200, V=5000))
+    ta, tb = gh.dev_inputs(wa), gh.dev_inputs(wb)
+
+    def run(t, w, ws, stream):
+        return api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"], workspace=ws, stream=stream)
+
+    ref_a = run(ta, wa, None, None)
+    ref_b = run(tb, wb, None, None)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    wsa = torch.zeros(api.workspace_size(wa["B"] * (wa["gamma"] + 1), wa["V"]), dtype=torch.uint8, device="cuda:0")
+    wsb = torch.zeros(api.workspace_size(wb["B"] * (wb["gamma"] + 1), wb["V"]), dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(sa):
+            ra = run(ta, wa, wsa, sa)
+        with torch.cuda.stream(sb):
+            rb = run(tb, wb, wsb, sb)
+        outs.append((ra, rb))
+    torch.cuda.synchronize()
+    for ra, rb in outs:
+        assert torch.equal(ra[0], ref_a[0]) and torch.equal(ra[1], ref_a[1])
+        assert torch.equal(rb[0], ref_b[0]) and torch.equal(rb[1], ref_b[1])
+
+
 def test_ragged_equals_dense():
     gh = _gh()
     w = make_workload("peaked_bf16", 3, B=10, V=9000)
