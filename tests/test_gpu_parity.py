@@ -292,6 +292,46 @@ def test_concurrent_streams_with_their_own_workspaces():
         assert torch.equal(rb[0], ref_b[0]) and torch.equal(rb[1], ref_b[1])
 
 
+@pytest.mark.parametrize("kind", ["probs", "filtered", "greedy"])
+def test_captured_in_a_hip_graph(kind):
+    """A call captured in a HIP graph (the library launches kernels only: no
+    allocation, synchronisation or memset) and replayed several times, with
+    eager calls of another batch on the same workspace in between: every
+    replay equals the eager result."""
+    gh = _gh()
+    w = make_workload("peaked_bf16", 10, B=300, V=3000)
+    other = make_workload("peaked_bf16", 11, B=40, V=7000)
+    t, to = gh.dev_inputs(w), gh.dev_inputs(other)
+    rows = max(w["B"] * (w["gamma"] + 1), other["B"] * (other["gamma"] + 1))
+    ws = torch.zeros(api.workspace_size(rows, 7000), dtype=torch.uint8, device="cuda:0")
+
+    def call(tt, ww):
+        if kind == "filtered":
+            return api.verify_probs_filtered(tt["logits"], tt["q"], tt["x"], tt["u"], ww["temperature"], 30, 0.9,
+                                             workspace=ws)[:2]
+        if kind == "greedy":
+            return api.verify_greedy(tt["logits"], tt["x"], workspace=ws)[:2]
+        return api.verify_probs(tt["logits"], tt["q"], tt["x"], tt["u"], ww["temperature"], workspace=ws)[:2]
+
+    ref = [r.clone() for r in call(t, w)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        call(t, w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = call(t, w)
+    for _ in range(3):
+        call(to, other)  # eager work of another shape on the same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1])
+
+
 def test_ragged_equals_dense():
     gh = _gh()
     w = make_workload("peaked_bf16", 3, B=10, V=9000)
