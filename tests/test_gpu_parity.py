@@ -224,12 +224,50 @@ def test_ragged_long_requests_over_both_launches():
     gh.compare(wo, gh.run_gpu(wo), label="ragged long one-hot")
 
 
+def test_empty_batch_through_every_entry_point():
+    """A batch of no requests is a valid call that launches nothing, through
+    each of the five verifying entry points and both logits types; between
+    two calls of a real batch on one workspace it changes neither result."""
+    gh = _gh()
+    dev = "cuda:0"
+    V, g = 1000, 3
+    w = make_workload("peaked_bf16", 9, B=12, V=V)
+    t = gh.dev_inputs(w)
+    first = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"])
+    ws = first[3]
+    for dt in (torch.float32, torch.bfloat16):
+        l = torch.zeros((0, g + 1, V), dtype=dt, device=dev)
+        q = torch.zeros((0, g, V), dtype=torch.float32, device=dev)
+        x = torch.zeros((0, g), dtype=torch.int64, device=dev)
+        u = torch.zeros((0, g + 1), dtype=torch.float32, device=dev)
+        lr = torch.zeros((0, V), dtype=dt, device=dev)
+        qr = torch.zeros((0, V), dtype=torch.float32, device=dev)
+        xr = torch.zeros((0,), dtype=torch.int64, device=dev)
+        ur = torch.zeros((0,), dtype=torch.float32, device=dev)
+        cu = torch.zeros((1,), dtype=torch.int32, device=dev)
+        results = [
+            api.verify_probs(l, q, x, u, 0.7, workspace=ws),
+            api.verify_probs(l, None, x, u, 0.7, row_stats=True, workspace=ws),
+            api.verify_greedy(l, x, workspace=ws),
+            api.verify_probs_filtered(l, q, x, u, 0.7, top_k=5, top_p=0.9, workspace=ws),
+            api.verify_ragged(lr, qr, xr, cu, ur, 1.0, workspace=ws),
+            api.verify_ragged_filtered(lr, qr, xr, cu, ur, 1.0, top_k=5, top_p=0.9, workspace=ws),
+        ]
+        for i, r in enumerate(results):
+            assert r[0].numel() == 0 and r[1].numel() == 0, i
+            assert r[-1] is ws, i
+    again = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    gh.compare(w, (again[0].cpu().numpy(), again[1].cpu().numpy(), None, None), label="after empty batches")
+
+
 def test_one_workspace_across_calls_of_every_kind():
     """One workspace through a sequence of calls of different kinds and
-    shapes, each twice: every result equals that of a fresh workspace. The
-    library leaves the workspace ready for the next call with the same rows
-    and vocabulary size; the binding zero-fills it when those change (a call
-    with another layout can leave data where this one keeps its marks)."""
+    shapes, each twice: every result equals that of a fresh workspace. After
+    one zero-fill the library leaves the workspace ready for the next call of
+    any kind, row count or vocabulary size; the binding does nothing to it
+    between calls."""
     gh = _gh()
     big = make_workload("peaked_bf16", 5, B=300, V=3000)  # two per-row launches (p1 = 1)
     small = make_workload("peaked_bf16", 6, B=8, V=9000)   # one launch
