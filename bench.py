@@ -5,25 +5,26 @@ requests, gamma=7 drafts each, V=128256, bf16 target logits (N(0, 4^2) with
 1% of each row boosted by 8), fp32 draft probabilities, T=0.7 — the whole hot
 path (temperature softmax, accept test, residual and bonus sampling, first
 rejection select). Inputs are synthetic and seeded, already resident in HBM
-when the timed region starts.
+when the timed region starts: four input sets (the batch with its request
+order rotated), cycled through every timed loop so that no cache holds a
+call's inputs from the call before.
 
 Prints one JSON line. `value` is verified draft positions per second
-(B * gamma per call). The roofline object prices the dominant stage (the
-per-row pass, two launches per call: positions 0-1, then the rest) against
-HBM: its algorithmic bytes per call are the logits of every row it reads (a
-row after a position already known to be a certain rejection is not read),
-plus per draft row read the token, its q(x), the accept uniform and l(x), plus
-the row records and the statistics it hands to the per-request pass; its
-duration is the mean of HIP events the library records on the launch stream
-around the two launches over the timed region. The per-request stage (two
-kernels) is timed the same way in a loop after the timed region and reported
-beside it (algorithmic bytes: the logit row and, for a replacement
-draw, the q row of each request's deciding row). `traffic` is the HBM traffic
-per launch of the dominant kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE
-counters scaled by a copy-kernel calibration, read from the committed summary
-under profiles/ only when that summary was taken on the current kernel source
-(else null). The oracle (float64 numpy) is timed on the host cores on the
-same inputs as the CPU baseline.
+(B * gamma per call). Bytes count every input element a call reads once
+(`unique`); the deciding rows' logits, which the per-request stage reads a
+second time, are reported apart (`reread`). The roofline object prices the
+dominant stage (the per-row pass, two launches per call) against HBM: its
+algorithmic bytes are the logit rows it reads (a row after a position already
+known to be a certain rejection is not read), 16 B of token, q(x) and uniform
+per draft row read, and the records and statistics it writes; its duration is
+the mean of HIP events the library records on the launch stream around the
+two launches over the timed region. The per-request stage is timed the same
+way in a loop after the timed region and reported beside it. `traffic` is the
+HBM traffic per call of the dominant stage from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters scaled by a copy-kernel calibration, read from the
+committed summary under profiles/ only when that summary was taken on the
+current kernel source (else null). The oracle (float64 numpy) is timed on
+the host cores on the same inputs as the CPU baseline.
 """
 
 from __future__ import annotations
@@ -66,6 +67,8 @@ def measured_traffic():
         return float(vals["rows_kernel_hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak), B=256 γ=7 V=128k"
 
 
@@ -223,15 +226,107 @@ def copy_ceiling(dev, mib=2048, reps=10):
 
 OTHER_CONFIGS = ("dense_f32", "ragged_bf16", "greedy_bf16", "onehot_bf16")
 
+NSETS = 4  # input sets resident in HBM, cycled through every timed loop
+
+
+def device_tensors(w, dev):
+    """(logits, q or None, x, u, cu or None) of workload w on the device."""
+    import numpy as np
+    import torch
+
+    if w["dtype"] == "bf16":
+        logits = torch.from_numpy(w["logits_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        logits = torch.from_numpy(w["logits"]).to(dev)
+    q = None if w["draft_probs"] is None else torch.from_numpy(w["draft_probs"]).to(dev)
+    x = torch.from_numpy(w["draft_tokens"]).to(dev)
+    u = torch.from_numpy(w["uniforms"]).to(dev)
+    cu = torch.from_numpy(w["cu"].astype(np.int32)).to(dev) if w["kind"] == "ragged" else None
+    return logits, q, x, u, cu
+
+
+def input_sets(t, w):
+    """NSETS copies of the batch on the device, set k with the request order
+    rotated by k * B / NSETS: the same values at other addresses, so that no
+    cache (the 256 MB Infinity Cache included) still holds a call's inputs
+    from the call before; set 0 is the batch itself."""
+    import numpy as np
+    import torch
+
+    logits, q, x, u, cu = t
+    B = w["B"]
+    sets = [t]
+    for k in range(1, NSETS):
+        perm = np.roll(np.arange(B), -(k * B // NSETS))
+        if cu is None:
+            idx = torch.from_numpy(perm).to(logits.device)
+            sets.append((logits[idx].contiguous(), None if q is None else q[idx].contiguous(), x[idx].contiguous(),
+                         u[idx].contiguous(), None))
+            continue
+        cu_h = w["cu"].astype(np.int64)
+        lens = np.diff(cu_h)
+        t_idx = np.concatenate([np.arange(cu_h[b] + b, cu_h[b + 1] + b + 1) for b in perm])
+        d_idx = np.concatenate([np.arange(cu_h[b], cu_h[b + 1]) for b in perm])
+        ncu = np.concatenate([[0], np.cumsum(lens[perm])]).astype(np.int32)
+        ti = torch.from_numpy(t_idx).to(logits.device)
+        di = torch.from_numpy(d_idx).to(logits.device)
+        sets.append((logits[ti].contiguous(), None if q is None else q[di].contiguous(), x[di].contiguous(),
+                     u[ti].contiguous(), torch.from_numpy(ncu).to(logits.device)))
+    return sets
+
+
+def time_calls(call, sets, steps):
+    """Wall time per call of `steps` calls cycling through the input sets
+    (synchronize on both sides)."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def call_bytes(rec, nacc, V, esz, has_q, gamma=None, cu=None):
+    """Bytes one call reads, from its row records: `unique` counts every
+    input element once (the logit rows the per-row pass read, the q rows of
+    the replacement draws, 16 B of token, q(x) and uniform per draft row
+    read); `reread` the logit rows the per-request stage reads again (the
+    deciding rows). Returns a dict with the row counts."""
+    import numpy as np
+
+    flags = rec[:, 1].astype(np.int64)
+    rows = len(flags)
+    B = len(nacc)
+    if cu is None:
+        draft = (np.arange(rows) % (gamma + 1)) < gamma
+    else:
+        draft = np.ones(rows, dtype=bool)
+        draft[cu[1:].astype(np.int64) + np.arange(B)] = False
+    read = (flags & 0x1000) == 0  # not SV_ROW_UNREAD
+    resid = int(np.count_nonzero(flags & 0x4))  # SV_ROW_RESIDUAL
+    bonus = int(np.count_nonzero(nacc == (np.full(B, gamma) if cu is None else np.diff(cu))))
+    rows_read = int(np.count_nonzero(read))
+    drafts_read = int(np.count_nonzero(read & draft))
+    unique = rows_read * V * esz + drafts_read * 16 + (resid * V * 4 if has_q else 0)
+    reread = (resid + bonus) * V * esz
+    needed = int(np.sum(nacc + 1)) * V * esz + (resid * V * 4 if has_q else 0)
+    return dict(unique=unique, reread=reread, rows_read=rows_read, drafts_read=drafts_read, residual=resid,
+                bonus=bonus, rows=rows, needed=needed)
+
+
+def mean_bytes(items):
+    keys = items[0].keys()
+    return {k: sum(d[k] for d in items) / len(items) for k in keys}
+
 
 def measure_config(name: str, steps: int, dev):
     """One of the other workloads (fp32 batch, ragged batch, greedy argmax,
-    one-hot drafts), `steps` calls after 3 warm-up calls: wall time per call,
-    verified positions per second and the bytes the call reads against HBM
-    peak. Bytes, as for the headline workload: the logit rows the per-row pass
-    reads (rows recorded as not read are left out) and the draft tokens, then
-    in sampling modes the deciding rows read again (a replacement draw: logits
-    and q, or logits only with one-hot drafts; a bonus draw: logits)."""
+    one-hot drafts): `steps` calls cycling through NSETS input sets after 3
+    warm-up calls: wall time per call, verified positions per second, and
+    the bytes a call reads (every input element once; the deciding rows read
+    again reported apart) against HBM peak."""
     import numpy as np
     import torch
 
@@ -241,89 +336,100 @@ def measure_config(name: str, steps: int, dev):
     w = make_workload(name, 0)
     V, T, B = w["V"], w["temperature"], w["B"]
     esz = 2 if w["dtype"] == "bf16" else 4
-    if w["dtype"] == "bf16":
-        logits = torch.from_numpy(w["logits_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-    else:
-        logits = torch.from_numpy(w["logits"]).to(dev)
-    q = None if w["draft_probs"] is None else torch.from_numpy(w["draft_probs"]).to(dev)
-    x = torch.from_numpy(w["draft_tokens"]).to(dev)
-    u = torch.from_numpy(w["uniforms"]).to(dev)
+    sets = input_sets(device_tensors(w, dev), w)
     ragged = w["kind"] == "ragged"
-    cu = torch.from_numpy(w["cu"].astype(np.int32)).to(dev) if ragged else None
-    rows = logits.shape[0] if ragged else B * (w["gamma"] + 1)
-    positions = int(x.numel())
+    rows = sets[0][0].shape[0] if ragged else B * (w["gamma"] + 1)
+    positions = int(sets[0][2].numel())
     ws = torch.zeros(api.workspace_size(rows, V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def call():
+    def call(st):
+        logits, q, x, u, cu = st
         if ragged:
             return api.verify_ragged(logits, q, x, cu, u, T, workspace=ws, stream=stream)[:2]
         if T == 0.0:
             return api.verify_greedy(logits, x, workspace=ws, stream=stream)[:2]
         return api.verify_probs(logits, q, x, u, T, workspace=ws, stream=stream)[:2]
 
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        out, nacc = call()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-    pct = call_percentiles(call, steps, stream)
-    rec = api.row_records(ws, rows).cpu().numpy().astype(np.int64)
-    flags = rec[:, 1]
-    read = int(np.count_nonzero((flags & api.SV_ROW_UNREAD) == 0))
-    if ragged:
-        cu_h = w["cu"].astype(np.int64)
-        last = cu_h[1:] + np.arange(B)
-    else:
-        last = np.arange(B) * (w["gamma"] + 1) + w["gamma"]
-    # the rows the per-row pass read, then (sampling modes) the deciding rows read
-    # again: a replacement draw reads logits and q (one-hot drafts: logits only), a
-    # bonus draw the last row's logits
-    nbytes = read * V * esz + positions * 8
-    if T > 0:
-        resid = int(np.count_nonzero(flags & api.SV_ROW_RESIDUAL))
-        bonus = int(np.count_nonzero(rec[last, 0] >= 0))
-        nbytes += resid * V * (esz + (4 if q is not None else 0)) + bonus * V * esz
-    mode = "greedy argmax" if T == 0.0 else ("one-hot drafts" if q is None else "lazy")
+    for i in range(3):
+        call(sets[i % NSETS])
+    dt = time_calls(call, sets, steps)
+    k = [0]
+
+    def one():
+        call(sets[k[0] % NSETS])
+        k[0] += 1
+
+    pct = call_percentiles(one, steps, stream)
+    per_set = []
+    for st in sets:
+        out, nacc = call(st)
+        rec = api.row_records(ws, rows).cpu().numpy().astype(np.int64)
+        cu_h = st[4].cpu().numpy().astype(np.int64) if ragged else None
+        if T == 0.0:  # greedy: every logit row once, and the tokens
+            per_set.append(dict(unique=rows * V * esz + positions * 8, reread=0, rows_read=rows, needed=rows * V * esz))
+        else:
+            per_set.append(call_bytes(rec, nacc.cpu().numpy(), V, esz, st[1] is not None, w["gamma"], cu_h))
+    b = mean_bytes(per_set)
+    mode = "greedy argmax" if T == 0.0 else ("one-hot drafts" if sets[0][1] is None else "lazy")
+    logits, q, x, _, cu = sets[0]
     return {"workload": f"{name}: B={B} V={V} T={T} {w['dtype']} logits, {mode}", "steps": steps,
-            "ms_per_call": dt * 1e3, "positions_per_s": positions / dt, "rows_read": read, "target_rows": rows,
-            "bytes_per_call": nbytes, "achieved_GBps": nbytes / dt / 1e9, "frac_of_hbm_peak": nbytes / dt / 1e9 / HBM_PEAK_GBS,
+            "input_sets": NSETS, "ms_per_call": dt * 1e3, "positions_per_s": positions / dt,
+            "rows_read": b["rows_read"], "target_rows": rows,
+            "unique_bytes_per_call": b["unique"], "reread_bytes_per_call": b["reread"],
+            "achieved_GBps": b["unique"] / dt / 1e9, "frac_of_hbm_peak": b["unique"] / dt / 1e9 / HBM_PEAK_GBS,
             "mean_accepted": float(nacc.float().mean().item()), "call_ms": pct,
             "beta_mean": (measured_beta(*draft_views(logits, q, x, cu, B, w["gamma"], V), T) if T > 0 else None)}
 
 
-def measure_filtered(steps, logits, q, x, u, T, ws, stream, top_k=50, top_p=0.9):
+def measure_filtered(steps, sets, T, ws, stream, top_k=50, top_p=0.9):
     """The same batch through spec_verify_probs_filtered (top-k then top-p on
-    the target): wall time per call and the per-row pass's event time."""
+    the target), cycling through the input sets: wall time per call and the
+    per-row pass's event time."""
     import torch
 
     from rejection_sampling_verifier_spec_amd import api
 
-    def call():
+    def call(st):
+        logits, q, x, u, _ = st
         return api.verify_probs_filtered(logits, q, x, u, T, top_k, top_p, workspace=ws, stream=stream)
 
-    for _ in range(3):
-        call()
+    for i in range(3):
+        call(sets[i % NSETS])
     torch.cuda.synchronize()
     api.profile_start((api.SV_PROFILE_ROWS,), capacity=steps)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        out, nacc, _ = call()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
+    wall = time_calls(call, sets, steps)
     rows_ms, rows_n = api.profile_stop()[api.SV_PROFILE_ROWS]
-    B, g = x.shape
+    out, nacc, _ = call(sets[0])
+    B, g = sets[0][2].shape
     flags = api.row_records(ws, B * (g + 1))[:, 1].cpu().numpy()
     read = (flags & api.SV_ROW_UNREAD) == 0
     tiers = {"rows_read": int(read.sum()),
              "second_tier": int(((flags & api.SV_ROW_HEAD2) != 0).sum()),
              "row_select": int(((flags & api.SV_ROW_ROW_SELECT) != 0).sum())}
-    return {"top_k": top_k, "top_p": top_p, "steps": steps, "ms_per_call": wall * 1e3,
+    return {"top_k": top_k, "top_p": top_p, "steps": steps, "input_sets": NSETS, "ms_per_call": wall * 1e3,
             "positions_per_s": B * g / wall, "per_row_pass_ms_mean": rows_ms / max(rows_n, 1),
             "mean_accepted": float(nacc.float().mean().item()), "threshold_tiers": tiers}
+
+
+def measure_speculative(steps, sets, T, ws, stream, esz, V):
+    """SV_FLAG_ALL_RESIDUALS, the design that draws every draft row's
+    replacement speculatively (every logit row and every q row read once,
+    then a per-request select), on the same input sets."""
+    from rejection_sampling_verifier_spec_amd import api
+
+    def call(st):
+        logits, q, x, u, _ = st
+        return api.verify_probs(logits, q, x, u, T, flags=api.SV_FLAG_ALL_RESIDUALS, workspace=ws, stream=stream)
+
+    for i in range(3):
+        call(sets[i % NSETS])
+    wall = time_calls(call, sets, steps)
+    B, g = sets[0][2].shape
+    nbytes = B * (g + 1) * V * esz + B * g * (V * 4 + 16)
+    return {"flags": api.SV_FLAG_ALL_RESIDUALS, "steps": steps, "input_sets": NSETS, "ms_per_call": wall * 1e3,
+            "positions_per_s": B * g / wall, "unique_bytes_per_call": nbytes, "achieved_GBps": nbytes / wall / 1e9,
+            "frac_of_hbm_peak": nbytes / wall / 1e9 / HBM_PEAK_GBS}
 
 
 def main():
@@ -341,6 +447,8 @@ def main():
                     help="calls timed for each of the other workloads after the timed region (0: skip)")
     ap.add_argument("--filtered-steps", type=int, default=30,
                     help="calls of the top-k / top-p entry point timed after the timed region (0: skip)")
+    ap.add_argument("--speculative-steps", type=int, default=30,
+                    help="calls of the all-residuals mode timed after the timed region (0: skip)")
     ap.add_argument("--loop-steps", type=int, default=30,
                     help="steps of the synthetic end-to-end loop measured after the timed region (0: skip)")
     ap.add_argument("--only-config", choices=OTHER_CONFIGS, default=None,
@@ -366,81 +474,79 @@ def main():
         return
     w = make_workload(args.workload, 0)
     B, g, V, T = w["B"], w["gamma"], w["V"], w["temperature"]
-    if w["dtype"] == "bf16":
-        logits = torch.from_numpy(w["logits_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
-    else:
-        logits = torch.from_numpy(w["logits"]).to(dev)
-    q = None if w["draft_probs"] is None else torch.from_numpy(w["draft_probs"]).to(dev)
-    x = torch.from_numpy(w["draft_tokens"]).to(dev)
-    u = torch.from_numpy(w["uniforms"]).to(dev)
+    sets = input_sets(device_tensors(w, dev), w)
     rows = B * (g + 1)
     ws = torch.zeros(api.workspace_size(rows, V), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    esz = 2 if w["dtype"] == "bf16" else 4
+    has_q = sets[0][1] is not None
 
-    def step():
+    def step(st):
+        logits, q, x, u, _ = st
         return api.verify_probs(logits, q, x, u, T, flags=args.flags, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(sets[i % NSETS])
     torch.cuda.synchronize()
-    # timed region: the library records timing-only events (no system fence) on
-    # the launch stream around the dominant kernel; the whole call is timed by
-    # the wall clock. A second event pair between the two stages would add a
-    # few microseconds of queue gap per call, so the per-request stage is timed
-    # in a loop of its own after the timed region.
+    # timed region: exactly --steps calls, cycling through the input sets; the
+    # library records timing-only events (no system fence) on the launch
+    # stream around the dominant kernel; the whole call is timed by the wall
+    # clock. A second event pair between the two stages would add a few
+    # microseconds of queue gap per call, so the per-request stage is timed in
+    # a loop of its own after the timed region.
     api.profile_start((api.SV_PROFILE_ROWS,), capacity=args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        out, nacc, _, _ = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = time_calls(step, sets, args.steps)
     prof = api.profile_stop()
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = wall * 1e3
     api.profile_start((api.SV_PROFILE_REQUEST,), capacity=args.steps)
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
+    time_calls(step, sets, args.steps)
     prof[api.SV_PROFILE_REQUEST] = api.profile_stop()[api.SV_PROFILE_REQUEST]
-    pct = call_percentiles(step, args.steps, stream)
+    k = [0]
+
+    def one():
+        step(sets[k[0] % NSETS])
+        k[0] += 1
+
+    pct = call_percentiles(one, args.steps, stream)
     positions = B * g
 
-    rec = api.row_records(ws, rows).cpu().numpy().reshape(B, g + 1, 2)
-    flags = rec[..., 1]
-    esz = 2 if w["dtype"] == "bf16" else 4
-    residual_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_RESIDUAL))
-    accepted_rows = int(np.count_nonzero(flags[:, :g] & api.SV_ROW_ACCEPTED))
-    exact_rows = int(np.count_nonzero(flags & api.SV_ROW_EXACT))
-    exact_why = {name: int(np.count_nonzero(flags & bit)) for bit, name in api.SV_ROW_WHY.items()}
-    bonus_drawn = int(np.count_nonzero(rec[:, g, 0] >= 0))
-    nacc_h = nacc.cpu().numpy()
-    # rows the per-row pass read: all but those recorded as not read (after a known rejection);
-    # the method needs rows 0 .. n of each request (n accepted drafts, then the deciding row)
-    read = (flags & api.SV_ROW_UNREAD) == 0
-    rows_read = int(np.count_nonzero(read))
-    drafts_read = int(np.count_nonzero(read[:, :g]))
-    rows_needed = int(np.sum(nacc_h + 1))
-    # per-row pass: the logits of every row read; per draft row read x (8 B), q(x) (4), u (4),
-    # l(x); records (8 per row) and the {m, Z, bound} statistics (32 B) of every row read that
-    # it leaves to the per-request pass
-    handed = int(np.count_nonzero(read & ((flags & api.SV_ROW_ACCEPTED) == 0))) if q is not None else 0
-    rows_bytes = rows_read * V * esz + drafts_read * (8 + 4 + 4 + esz) + rows * 8 + handed * 32
-    # per-request pass: the deciding row's logits and, for a replacement draw, its q row
-    req_bytes = residual_rows * V * (esz + 4) + bonus_drawn * V * esz
-    alg_bytes = rows_bytes + req_bytes
-    full_bytes = rows * V * esz + (0 if q is None else positions * V * 4)
-    needed_bytes = rows_needed * V * esz + req_bytes - (residual_rows + bonus_drawn) * V * esz
-    call_s = wall / args.steps
+    # bytes per call from each input set's row records (which rows the
+    # per-row pass read and which were drawn from depends on the batch and,
+    # for rows read speculatively, on timing)
+    per_set, rows_info = [], []
+    for st in sets:
+        out, nacc, _, _ = step(st)
+        rec = api.row_records(ws, rows).cpu().numpy().astype(np.int64)
+        na = nacc.cpu().numpy()
+        cb = call_bytes(rec, na, V, esz, has_q, g)
+        flags = rec[:, 1]
+        handed = int(np.count_nonzero(((flags & api.SV_ROW_UNREAD) == 0) & ((flags & api.SV_ROW_ACCEPTED) == 0)))
+        # per-row pass: logits of the rows read, 16 B per draft row read (token,
+        # q(x), uniform), and what it writes: an 8-byte record per row and the
+        # 32-byte statistics of the rows it hands to the per-request stage
+        cb["rows_kernel"] = cb["rows_read"] * V * esz + cb["drafts_read"] * 16 + rows * 8 + handed * 32
+        # per-request stage: the deciding rows' logits (read again) and q rows
+        cb["request_stage"] = cb["reread"] + (cb["residual"] * V * 4 if has_q else 0)
+        per_set.append(cb)
+        fl = flags.reshape(B, g + 1)
+        rows_info.append(dict(accepted=int(np.count_nonzero(fl[:, :g] & api.SV_ROW_ACCEPTED)),
+                              exact=int(np.count_nonzero(fl & api.SV_ROW_EXACT)),
+                              mean_accepted=float(na.mean())))
+    b = mean_bytes(per_set)
+    out0, nacc0, _, _ = step(sets[0])  # set 0 = the batch in its own order (the oracle's)
+    torch.cuda.synchronize()
+    full_bytes = rows * V * esz + (0 if not has_q else positions * (V * 4 + 16))
     rows_ms, rows_n = prof[api.SV_PROFILE_ROWS]
     req_ms, req_n = prof[api.SV_PROFILE_REQUEST]
     rows_s = rows_ms / max(rows_n, 1) * 1e-3
     req_s = req_ms / max(req_n, 1) * 1e-3
-    achieved = rows_bytes / rows_s / 1e9 if rows_n else None
+    achieved = b["rows_kernel"] / rows_s / 1e9 if rows_n else None
     traffic = measured_traffic()
+    logits0, q0, x0, _, _ = sets[0]
 
     result = {
         "metric": METRIC,
-        "value": positions / (wall / args.steps),
+        "value": positions / wall,
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -450,52 +556,63 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 logits, fp32 q, fp32 arithmetic with fp64 accumulation" if esz == 2 else "fp32",
-        "data": "synthetic, seeded (numpy PCG64), same recipe as the parity tests",
+        "data": f"synthetic, seeded (numpy PCG64), same recipe as the parity tests; {NSETS} input sets resident in "
+                f"HBM (request order rotated), cycled through every timed loop",
         "config": {"workload": f"{args.workload}: B={B} gamma={g} V={V} T={T} {w['dtype']} logits",
                    "global_batch": B, "gamma": g, "vocab": V, "flags": args.flags},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": None if achieved is None else achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "lazy_rows_kernel (per-row pass, two launches per call)",
-                     "bytes_per_launch": rows_bytes,
+                     "bytes_per_launch": b["rows_kernel"],
                      "launch_ms_mean": rows_s * 1e3, "launches_timed": rows_n,
                      "note": "HIP events recorded by the library on the launch stream around the per-row "
-                             "pass (both launches); bytes: the rows it read"},
-        "request_pass": {"kernel": "request_pass_kernel + request_finish_kernel (per-request fp64 stage)", "bytes_per_launch": req_bytes,
-                         "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
-                         "achieved_GBps": req_bytes / req_s / 1e9 if req_n else None},
-        "whole_call": {"bytes": alg_bytes, "ms_mean": call_s * 1e3, "achieved_GBps": alg_bytes / call_s / 1e9,
+                             "pass (both launches) in the timed region; bytes: the logit rows it read, 16 B per "
+                             "draft row read, its records and statistics (mean over the input sets)"},
+        "request_stage": {"kernel": "request_pass_kernel + request_finish_kernel (per-request fp64 stage)",
+                          "bytes_per_launch": b["request_stage"],
+                          "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
+                          "achieved_GBps": b["request_stage"] / req_s / 1e9 if req_n else None},
+        "whole_call": {"unique_bytes": b["unique"], "reread_bytes": b["reread"], "ms_mean": ms_per_step,
+                       "achieved_GBps": b["unique"] / wall / 1e9,
+                       "frac_of_hbm_peak": b["unique"] / wall / 1e9 / HBM_PEAK_GBS,
                        "ms_event_percentiles": pct,
-                       "note": "ms_mean: wall clock over the timed steps (synchronize on both sides); percentiles: "
-                               "further calls, one event pair each on the launch stream"},
-        "rows": {"draft": positions, "target_rows": rows, "read_by_per_row_pass": rows_read,
-                 "needed_by_the_method": rows_needed, "accepted_own_test": accepted_rows,
-                 "residual_drawn": residual_rows, "bonus_drawn": bonus_drawn,
-                 "fp64_recomputed": exact_rows, "fp64_reasons": exact_why, "mean_accepted": float(nacc.float().mean().item()),
-                 "beta_mean": measured_beta(*draft_views(logits, q, x, None, B, g, V), T) if T > 0 else None},
+                       "note": "unique_bytes: every input element the call reads, once (logit rows read, q rows "
+                               "of the replacement draws, tokens, q(x), uniforms); reread_bytes: the deciding "
+                               "rows' logits read again by the per-request stage (not counted in achieved); "
+                               "ms_mean: wall clock over the timed steps; percentiles: further calls, one event "
+                               "pair each"},
+        "rows": {"draft": positions, "target_rows": rows, "read_by_per_row_pass": b["rows_read"],
+                 "needed_by_the_method": int(round(sum(r["mean_accepted"] for r in rows_info) / NSETS * B + B)),
+                 "accepted_own_test": sum(r["accepted"] for r in rows_info) / NSETS,
+                 "residual_drawn": b["residual"], "bonus_drawn": b["bonus"],
+                 "fp64_recomputed": sum(r["exact"] for r in rows_info) / NSETS,
+                 "mean_accepted": sum(r["mean_accepted"] for r in rows_info) / NSETS,
+                 "beta_mean": measured_beta(*draft_views(logits0, q0, x0, None, B, g, V), T) if T > 0 else None},
         "speculative_full_bytes_per_call": full_bytes,
-        "method_minimum_bytes_per_call": needed_bytes,
-        "method_minimum_GBps_equiv": needed_bytes / call_s / 1e9,
-        "speculative_full_GBps_equiv": full_bytes / call_s / 1e9,
+        "method_minimum_bytes_per_call": b["needed"],
     }
-    if args.filtered_steps > 0 and q is not None and T > 0:
-        result["filtered"] = measure_filtered(args.filtered_steps, logits, q, x, u, T, ws, stream)
+    if args.speculative_steps > 0 and has_q and T > 0:
+        result["speculative"] = measure_speculative(args.speculative_steps, sets, T, ws, stream, esz, V)
+    if args.filtered_steps > 0 and has_q and T > 0:
+        result["filtered"] = measure_filtered(args.filtered_steps, sets, T, ws, stream)
     if args.loop_steps > 0:
         result["loop"] = measure_loop(args.loop_steps, dev)
-    if args.cpu_requests > 0 and q is not None:
+    if args.cpu_requests > 0 and has_q:
         base, ref = cpu_baseline(w, args.cpu_requests, args.cpu_passes)
-        o = out.cpu().numpy()
-        na = nacc.cpu().numpy()
-        mism = sum(1 for b, (toks, n) in enumerate(ref) if n != na[b] or list(o[b, :n + 1]) != toks)
+        o = out0.cpu().numpy()
+        na = nacc0.cpu().numpy()
+        mism = sum(1 for bi, (toks, n) in enumerate(ref) if n != na[bi] or list(o[bi, :n + 1]) != toks)
         base["parity_mismatches_in_sample"] = mism
         result["cpu_baseline"] = base
     if args.config_steps > 0:
-        del logits, q, x, u, ws, w
+        del sets, ws, w, logits0, q0, x0, out0, nacc0
         torch.cuda.empty_cache()
         result["hbm_ceiling_context"] = copy_ceiling(dev)
         result["other_configs"] = []
         for n in OTHER_CONFIGS:
             print(f"bench: {n}", file=sys.stderr, flush=True)
             result["other_configs"].append(measure_config(n, args.config_steps, dev))
+            torch.cuda.empty_cache()
     print(json.dumps(result))
 
 

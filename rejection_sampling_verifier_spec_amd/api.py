@@ -126,15 +126,22 @@ def _check(t, name, dtype=None, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream(device, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(device)
+def _launch_stream(device, stream):
+    """The stream the library's kernels are enqueued on: `stream`, else torch's
+    current stream of `device`."""
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _handle(s):
     return ctypes.c_void_p(s.cuda_stream)
 
 
 def _workspace(rows, vocab, device, workspace):
     """The library needs a zero-filled workspace on first use (it leaves it
     ready for the next call, of any kind and shape); a fresh one is allocated
-    zeroed."""
+    zeroed. Called with the launch stream current (see the verify functions),
+    so that the zero-fill is ordered before the library's kernels and the
+    allocator ties the memory to the stream that uses it."""
     need = workspace_size(rows, vocab)
     if workspace is None:
         workspace = torch.zeros(max(need, 512), dtype=torch.uint8, device=device)
@@ -162,13 +169,15 @@ def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, flags
         raise ValueError("draft_probs must be [B, gamma, V]")
     if tuple(draft_tokens.shape) != (B, g) or tuple(uniforms.shape) != (B, g1):
         raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
-    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
-    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(B * g1, V, dev, workspace)
-    rc = lib.spec_verify_probs(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
-                               _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(out), _ptr(nacc),
-                               _ptr(stats), _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):  # outputs and a fresh workspace belong to the launch stream
+        out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
+        workspace, need = _workspace(B * g1, V, dev, workspace)
+        rc = lib.spec_verify_probs(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                   _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(out), _ptr(nacc),
+                                   _ptr(stats), _ptr(workspace), workspace.numel(), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_probs")
     return out, nacc, stats, workspace
@@ -184,11 +193,13 @@ def verify_greedy(logits, draft_tokens, workspace=None, stream=None):
     _check(draft_tokens, "draft_tokens", torch.int64, dev)
     if tuple(draft_tokens.shape) != (B, g):
         raise ValueError("draft_tokens must be [B, gamma]")
-    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
-    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(B * g1, V, dev, workspace)
-    rc = lib.spec_verify_greedy(_ptr(logits), _dtype_code(logits), _ptr(draft_tokens), B, g, V, _ptr(out),
-                                _ptr(nacc), _ptr(workspace), workspace.numel(), _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        workspace, need = _workspace(B * g1, V, dev, workspace)
+        rc = lib.spec_verify_greedy(_ptr(logits), _dtype_code(logits), _ptr(draft_tokens), B, g, V, _ptr(out),
+                                    _ptr(nacc), _ptr(workspace), workspace.numel(), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_greedy")
     return out, nacc, workspace
@@ -213,14 +224,16 @@ def verify_ragged(logits, draft_probs, draft_tokens, cu_num_draft_tokens, unifor
         raise ValueError("logits must be [T+B, V] and uniforms [T+B]")
     if draft_probs is not None and tuple(draft_probs.shape) != (T, V):
         raise ValueError("draft_probs must be [T, V]")
-    out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
-    nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
-    stats = torch.empty((T + nb, 4), dtype=torch.float32, device=dev) if row_stats else None
-    workspace, need = _workspace(T + nb, V, dev, workspace)
-    rc = lib.spec_verify_ragged(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
-                                _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature), int(flags),
-                                _ptr(out), _ptr(nacc), _ptr(stats), _ptr(workspace), workspace.numel(),
-                                _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
+        nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
+        stats = torch.empty((T + nb, 4), dtype=torch.float32, device=dev) if row_stats else None
+        workspace, need = _workspace(T + nb, V, dev, workspace)
+        rc = lib.spec_verify_ragged(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                    _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature),
+                                    int(flags), _ptr(out), _ptr(nacc), _ptr(stats), _ptr(workspace),
+                                    workspace.numel(), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_ragged")
     return out, nacc, stats, workspace
@@ -245,13 +258,15 @@ def verify_probs_filtered(logits, draft_probs, draft_tokens, uniforms, temperatu
         raise ValueError("draft_probs must be [B, gamma, V]")
     if tuple(draft_tokens.shape) != (B, g) or tuple(uniforms.shape) != (B, g1):
         raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
-    out = torch.empty((B, g1), dtype=torch.int64, device=dev)
-    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(B * g1, V, dev, workspace)
-    rc = lib.spec_verify_probs_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
-                                        _ptr(uniforms), B, g, V, float(temperature), int(top_k), float(top_p),
-                                        _ptr(out), _ptr(nacc), _ptr(workspace), workspace.numel(),
-                                        _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty((B, g1), dtype=torch.int64, device=dev)
+        nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+        workspace, need = _workspace(B * g1, V, dev, workspace)
+        rc = lib.spec_verify_probs_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs),
+                                            _ptr(draft_tokens), _ptr(uniforms), B, g, V, float(temperature),
+                                            int(top_k), float(top_p), _ptr(out), _ptr(nacc), _ptr(workspace),
+                                            workspace.numel(), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_probs_filtered")
     return out, nacc, workspace
@@ -275,13 +290,15 @@ def verify_ragged_filtered(logits, draft_probs, draft_tokens, cu_num_draft_token
         raise ValueError("logits must be [T+B, V] and uniforms [T+B]")
     if draft_probs is None or tuple(draft_probs.shape) != (T, V):
         raise ValueError("draft_probs must be [T, V]")
-    out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
-    nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
-    workspace, need = _workspace(T + nb, V, dev, workspace)
-    rc = lib.spec_verify_ragged_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
-                                         _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V, float(temperature),
-                                         int(top_k), float(top_p), _ptr(out), _ptr(nacc), _ptr(workspace),
-                                         workspace.numel(), _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty((T + nb,), dtype=torch.int64, device=dev)
+        nacc = torch.empty((nb,), dtype=torch.int32, device=dev)
+        workspace, need = _workspace(T + nb, V, dev, workspace)
+        rc = lib.spec_verify_ragged_filtered(_ptr(logits), _dtype_code(logits), _ptr(draft_probs),
+                                             _ptr(draft_tokens), _ptr(cu_num_draft_tokens), _ptr(uniforms), nb, T, V,
+                                             float(temperature), int(top_k), float(top_p), _ptr(out), _ptr(nacc),
+                                             _ptr(workspace), workspace.numel(), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_ragged_filtered")
     return out, nacc, workspace
@@ -292,8 +309,10 @@ def selftest_exp2(device=None, stream=None):
     the bound the certified fast path assumes: (measured, assumed)."""
     lib = load()
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-    out = torch.empty(1, dtype=torch.float64, device=dev)
-    rc = lib.spec_verify_selftest_exp2(_ptr(out), _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty(1, dtype=torch.float64, device=dev)
+        rc = lib.spec_verify_selftest_exp2(_ptr(out), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_selftest_exp2")
     return float(out.item()), float(lib.spec_verify_exp2_error_bound())
@@ -308,8 +327,10 @@ def stream_read(buf, out=None, stream=None):
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
     nbytes = buf.numel() * buf.element_size()
-    out = torch.empty(1, dtype=torch.int64, device=dev) if out is None else out
-    rc = lib.spec_verify_stream_read(_ptr(buf), nbytes, _ptr(out), _stream(dev, stream))
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        out = torch.empty(1, dtype=torch.int64, device=dev) if out is None else out
+        rc = lib.spec_verify_stream_read(_ptr(buf), nbytes, _ptr(out), _handle(s))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_stream_read")
     return out

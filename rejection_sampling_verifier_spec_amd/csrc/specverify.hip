@@ -43,7 +43,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <float.h>
 #include <math.h>
+#include <atomic>
 #include <type_traits>
 #include <stdint.h>
 
@@ -478,6 +480,12 @@ __device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restr
     const int2 tk = tasks[blk];
     t.b = tk.x;
     t.i = tk.y;
+    // entries come from the first launch; any other value (a workspace that
+    // was not zero-filled, a list left by an interrupted call) is no task
+    if (static_cast<unsigned>(t.b) >= static_cast<unsigned>(B) || t.i < 0) {
+      t.valid = false;
+      return t;
+    }
   } else {
     t.b = blk % B;
     t.i = blk / B;
@@ -739,18 +747,19 @@ __device__ __forceinline__ void load8(const LT* __restrict__ row, int V, int k0,
 #pragma unroll
   for (int e = 0; e < kExactPer; ++e) l[e] = k0 + e < V ? static_cast<double>(to_float(raw[e])) : -INFINITY;
 }
-// q of the same elements. With q == nullptr it reads fallback[0] (any valid
-// address) instead, so that the loads need no branch around them, and
-// returns zeros.
-__device__ __forceinline__ void load8q(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
-                                       double (&v)[kExactPer]) {
-  const bool has = q != nullptr;
-  const float* src = has ? q : fallback;
+// q of the same elements; zeros when q == nullptr (uniform over the block: a
+// row without a q row), which reads nothing.
+__device__ __forceinline__ void load8q(const float* __restrict__ q, int V, int k0, double (&v)[kExactPer]) {
+  if (q == nullptr) {
+#pragma unroll
+    for (int e = 0; e < kExactPer; ++e) v[e] = 0.0;
+    return;
+  }
   float raw[kExactPer];
 #pragma unroll
-  for (int e = 0; e < kExactPer; ++e) raw[e] = src[has ? min(k0 + e, V - 1) : 0];
+  for (int e = 0; e < kExactPer; ++e) raw[e] = q[min(k0 + e, V - 1)];
 #pragma unroll
-  for (int e = 0; e < kExactPer; ++e) v[e] = (has && k0 + e < V) ? static_cast<double>(raw[e]) : 0.0;
+  for (int e = 0; e < kExactPer; ++e) v[e] = k0 + e < V ? static_cast<double>(raw[e]) : 0.0;
 }
 
 struct ExactRow {
@@ -829,7 +838,7 @@ __device__ void exact_item(const ProbsArgs& a, const ExactArgs& e, const ExactRo
   for (int u = 0; u < kItemTiles; ++u) {
     const int k0 = (j0 + u) * kTile + kExactPer * threadIdx.x;
     load8<LT>(lrow, a.V, k0, l[u]);
-    load8q(r.qrow, a.u, a.V, k0, qv[u]);
+    load8q(r.qrow, a.V, k0, qv[u]);
   }
   double v[3 * kItemTiles];
   int undecided = 0;
@@ -938,7 +947,7 @@ __device__ void exact_finish_row(const ProbsArgs& a, const ExactArgs& e, const E
       const int k0 = j * kTile + kExactPer * tid;
       double l[kExactPer], qv[kExactPer];
       load8<LT>(lrow, a.V, k0, l);
-      load8q(r.qrow, a.u, a.V, k0, qv);
+      load8q(r.qrow, a.V, k0, qv);
       double acc = 0.0;
 #pragma unroll
       for (int k = 0; k < kExactPer; ++k) acc += fmax(0.0, exp2((l[k] - r.m) * s) * iz - qv[k]);
@@ -1021,7 +1030,7 @@ __device__ void exact_finish_row(const ProbsArgs& a, const ExactArgs& e, const E
     const int k0 = jt * kTile + kExactPer * tid;
     double l[kExactPer], w[kExactPer], qv[kExactPer];
     load8<LT>(lrow, a.V, k0, l);
-    load8q(mode == 1 ? r.qrow : nullptr, a.u, a.V, k0, qv);
+    load8q(mode == 1 ? r.qrow : nullptr, a.V, k0, qv);
     double tsum = 0.0;
 #pragma unroll
     for (int k = 0; k < kExactPer; ++k) {
@@ -2570,8 +2579,10 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
   // a mark raised there before the clear is lost, which only leaves a row to
   // be read that could have been skipped. The second launch and the task
   // list read marks after the first launch has completed.
+  // (a returning exchange, its result stored: the clear has been performed
+  // before this thread goes on, hence before this block's count below)
   if (!second && t.valid && t.i == 0 && threadIdx.x == 0)
-    __hip_atomic_store(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.mark_old = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (second && t.valid && t.i > 0) {
     if (threadIdx.x == 0)
       sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
@@ -2584,15 +2595,19 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
   if (read) probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
   if (phase != 1) return;
   // first launch: the last block to finish lists the tasks of the second launch
-  // reads. Marks and the count are device-scope atomics, each block's mark
-  // completed before its count (see probs_row), and the list reads the marks
-  // with atomic loads: no cache-wide fence is needed.
+  // reads. Marks and the count are device-scope atomics; every mark update
+  // (the clear above, a raise in probs_row) is a returning atomic whose result
+  // the thread waits for, so it has been performed before that block's count
+  // is issued, and the last block reads the marks with device-scope atomic
+  // loads after its own count has returned, behind an acquire fence. No
+  // block needs a release fence (a cache write-back) of its own.
   __syncthreads();
   if (threadIdx.x == 0)
     sh.last = __hip_atomic_fetch_add(a.surv_n + 16, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               static_cast<int>(gridDim.x) - 1;
   __syncthreads();
   if (!sh.last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   list_survivors<NT>(a, p1, sh);
   if (threadIdx.x == 0) a.surv_n[16] = 0;  // ready for the next call
 }
@@ -2835,9 +2850,8 @@ struct RawChunk<LT, false> {
 };
 
 // 8 consecutive elements from k0 (a multiple of 8), as fp32 logits (-inf past
-// the end of the row) or q (0 past the end; q == nullptr: zeros, with
-// fallback[0] read instead so that the loads need no branch). Loads are
-// unconditional, with addresses clamped into the row.
+// the end of the row) or q (0 past the end; q == nullptr: zeros, nothing
+// read). Loads are unconditional, with addresses clamped into the row.
 template <typename LT, bool VEC>
 __device__ __forceinline__ void load8f(const LT* __restrict__ row, int V, int k0, float (&v)[8]) {
   if constexpr (VEC && sizeof(LT) == 2) {
@@ -2866,14 +2880,17 @@ __device__ __forceinline__ void load8f(const LT* __restrict__ row, int V, int k0
     if (k0 + k >= V) v[k] = -INFINITY;
 }
 template <bool VEC>
-__device__ __forceinline__ void load8qf(const float* __restrict__ q, const float* __restrict__ fallback, int V, int k0,
+__device__ __forceinline__ void load8qf(const float* __restrict__ q, int V, int k0,
                                         float (&v)[8]) {
-  const bool has = q != nullptr;
-  const float* src = has ? q : fallback;
+  if (q == nullptr) {  // uniform over the block: no q row, no load
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    return;
+  }
   if constexpr (VEC) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float4 w = *reinterpret_cast<const float4*>(src + (has ? min(k0 + 4 * h, V - 4) : 0));
+      const float4 w = *reinterpret_cast<const float4*>(q + min(k0 + 4 * h, V - 4));
       v[4 * h] = w.x;
       v[4 * h + 1] = w.y;
       v[4 * h + 2] = w.z;
@@ -2881,11 +2898,11 @@ __device__ __forceinline__ void load8qf(const float* __restrict__ q, const float
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[has ? min(k0 + k, V - 1) : 0];
+    for (int k = 0; k < 8; ++k) v[k] = q[min(k0 + k, V - 1)];
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    if (!has || k0 + k >= V) v[k] = 0.f;
+    if (k0 + k >= V) v[k] = 0.f;
 }
 
 // whether tile j of a row of V elements reaches past its end
@@ -3272,7 +3289,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       const int kc = jt * kTile + 32 * L + 8 * h;
       float lv[8], qv[8];
       load8f<LT, VEC>(lrow, V, kc, lv);
-      load8qf<VEC>(mode == 1 ? qrow : nullptr, a.u, V, kc, qv);
+      load8qf<VEC>(mode == 1 ? qrow : nullptr, V, kc, qv);
       if (mode == 1 && onehot) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) qv[k] = kc + k == hot ? 1.f : 0.f;
@@ -3526,17 +3543,19 @@ constexpr int kRowsNTLazy = 512;
 constexpr int kRaggedFirstMax = 4;  // ragged batches: most positions in the first lazy launch
 constexpr int kLazyBlocksPerCU = 2;      // lazy per-row kernel: 512-thread blocks resident per CU
 
-// Compute units of the current device (cached per device; 256 if the query fails).
+// Compute units of the current device (cached per device; 256 if the query
+// fails). Callers on several host threads may fill an entry at the same time:
+// they store the same value, through atomics.
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Positions of the lazy mode's first launch: as many as fill the blocks the
@@ -3664,6 +3683,9 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
   if (B < 0 || gamma < 0 || ndraft < 0 || V < 1) return SV_ERR_INVALID_ARGUMENT;
   if (V > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
   if (!(T >= 0.0) || !isfinite(T)) return SV_ERR_INVALID_ARGUMENT;
+  // the fp32 scale log2(e) / T must be finite: T > 0 below about 4.2e-39 is
+  // rejected (T = 0 is argmax decoding)
+  if (T > 0.0 && !(1.4426950408889634 / T < static_cast<double>(FLT_MAX))) return SV_ERR_INVALID_ARGUMENT;
   if (fa.filtered && (!(T > 0.0) || !(fa.top_p > 0.0 && fa.top_p <= 1.0))) return SV_ERR_INVALID_ARGUMENT;
   if (flags & ~static_cast<uint32_t>(SV_FLAG_EXACT | SV_FLAG_ALL_RESIDUALS | SV_FLAG_EAGER))
     return SV_ERR_INVALID_ARGUMENT;

@@ -16,6 +16,8 @@ statistics: max(l/T) within 1e-6 relative, ln Z within
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -141,10 +143,9 @@ def _flip_tolerated(w, b, gpu_toks, gpu_n, ref_toks, ref_n, filt=None):
     return (lo - 1e-6) < us <= c[gt] + 1e-6
 
 
-def compare(w, gpu, reqs=None, stats=False, label="", filt=None):
-    """Compare GPU results with the oracle on requests `reqs` (all if None)."""
+def _compare_range(w, gpu, reqs, stats, label, filt):
+    """(hard mismatches, tolerated flips, rows checked) over requests `reqs`."""
     out, nacc, gst, _ = gpu
-    reqs = range(w["B"]) if reqs is None else reqs
     hard, flips, rows = [], 0, 0
     for b in reqs:
         l, q, x, u, sl = request_view(w, b)
@@ -165,6 +166,51 @@ def compare(w, gpu, reqs=None, stats=False, label="", filt=None):
         if stats:
             gs = gst[sl] if w["kind"] == "ragged" else gst[b]
             check_stats(gs, rst, f"{label} request {b}")
+    return hard, flips, rows
+
+
+def compare(w, gpu, reqs=None, stats=False, label="", filt=None):
+    """Compare GPU results with the oracle on requests `reqs` (all if None)."""
+    reqs = range(w["B"]) if reqs is None else reqs
+    hard, flips, rows = _compare_range(w, gpu, reqs, stats, label, filt)
+    assert not hard, f"{label}: {len(hard)} hard mismatches, first: {hard[:3]}"
+    assert flips <= 1e-4 * rows, f"{label}: {flips} tolerated flips in {rows} rows"
+    return rows, flips
+
+
+_JOB = None  # (w, gpu, stats, label, filt) inherited by the forked workers
+
+
+def _compare_job(rng):
+    w, gpu, stats, label, filt = _JOB
+    return _compare_range(w, gpu, range(*rng), stats, label, filt)
+
+
+def compare_all(w, gpu, stats=False, label="", filt=None, workers=16):
+    """compare() on every request of the batch, the oracle run by forked worker
+    processes over contiguous ranges of requests (host CPU work only; the
+    workers inherit the inputs and the GPU results through fork and never
+    touch the GPU). Prints the rows checked and the tolerated flips."""
+    import multiprocessing as mp
+    global _JOB
+    nb = w["B"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = 4
+    nw = max(1, min(workers, cores, nb))
+    bounds = np.linspace(0, nb, nw + 1).round().astype(int)
+    jobs = [(int(bounds[i]), int(bounds[i + 1])) for i in range(nw) if bounds[i + 1] > bounds[i]]
+    _JOB = (w, gpu, stats, label, filt)
+    try:
+        with mp.get_context("fork").Pool(len(jobs)) as pool:
+            parts = pool.map(_compare_job, jobs)
+    finally:
+        _JOB = None
+    hard = [h for p in parts for h in p[0]]
+    flips = sum(p[1] for p in parts)
+    rows = sum(p[2] for p in parts)
+    print(f"{label}: {nb} requests, {rows} rows, {flips} tolerated flips, {len(hard)} hard mismatches", flush=True)
     assert not hard, f"{label}: {len(hard)} hard mismatches, first: {hard[:3]}"
     assert flips <= 1e-4 * rows, f"{label}: {flips} tolerated flips in {rows} rows"
     return rows, flips

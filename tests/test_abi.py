@@ -83,6 +83,9 @@ def probs(lib, **kw):
     (dict(T=-0.5), -1),
     (dict(T=float("nan")), -1),
     (dict(T=float("inf")), -1),
+    (dict(T=1e-39), -1),        # log2(e) / T beyond the fp32 range
+    (dict(T=4.2e-39), -1),
+    (dict(T=5e-39, B=0), 0),    # the smallest temperatures whose scale fits fp32 pass validation
     (dict(flags=0x10), -1),
     (dict(logits=None), -1),
     (dict(out=None), -1),
@@ -178,3 +181,4 @@ def test_profile_argument_validation(lib):
     count = (ctypes.c_int32 * 2)(7, 7)
     assert lib.spec_verify_profile_stop(ctypes.cast(total, ctypes.c_void_p), ctypes.cast(count, ctypes.c_void_p)) == 0
     assert list(total) == [0.0, 0.0] and list(count) == [0, 0]
+

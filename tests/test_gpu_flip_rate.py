@@ -10,6 +10,11 @@ accept flip tolerated only when |u - p/q| <= 1e-6, a sampled-token flip only
 when u lies within 1e-6 of a boundary of the oracle's normalised CDF); none may
 be hard, and the tolerated ones must stay below 1e-4 of the samples. The
 counts are printed (the certified kernels are expected to give zero).
+
+Shapes: small synthetic cases (bf16 V=32000, fp32 V=4096), and the recipes
+the verifier is measured on: the peaked bf16 batch (V=128256, gamma=7,
+T=0.7) with q rows, through top-k 50 / top-p 0.9, and with one-hot drafts;
+the ragged batch's rows (V=152064, 1 to 8 drafts per request, low-overlap q).
 """
 
 import numpy as np
@@ -18,7 +23,7 @@ import torch
 
 import oracle
 from rejection_sampling_verifier_spec_amd import api
-from rejection_sampling_verifier_spec_amd.workloads import lattice_uniforms, make_dense_custom
+from rejection_sampling_verifier_spec_amd.workloads import lattice_uniforms, make_dense_custom, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -32,28 +37,37 @@ def _device():
     api.load()
 
 
-def logits_tensor(w):
-    if w["dtype"] == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(w["logits_bits"]).view(np.int16)).to(DEV).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(w["logits"])).to(DEV)
+def logits_tensor(rows_f32, rows_bits):
+    if rows_bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(rows_bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(rows_f32)).to(DEV)
 
 
 class DistinctRequest:
     """The oracle's view of one distinct request: p(x_i), q(x_i) per draft,
     and for every possible number n of accepted drafts the weights of the
     emitted token (residual at n < g, bonus row at n = g) and their
-    normalised CDF."""
+    normalised CDF. q None: one-hot drafts; filt = (top_k, top_p): the
+    adjusted target."""
 
-    def __init__(self, l, q, x, T):
+    def __init__(self, l, q, x, T, filt=None):
         g = len(x)
         self.g = g
-        p_rows = [oracle.target_probs(l[i], T) for i in range(g + 1)]
+        if filt is None:
+            p_rows = [oracle.target_probs(l[i], T) for i in range(g + 1)]
+        else:
+            p_rows = [oracle.adjusted_target_probs(l[i], T, filt[0], filt[1]) for i in range(g + 1)]
         self.px = [float(p_rows[i][int(x[i])]) for i in range(g)]
-        self.qx = [float(q[i][int(x[i])]) for i in range(g)]
+        self.qx = [1.0 if q is None else float(q[i][int(x[i])]) for i in range(g)]
         self.w = []
         for n in range(g + 1):
             if n < g:
-                wn, _, _ = oracle.residual_weights(p_rows[n], np.asarray(q[n], dtype=np.float64))
+                if q is None:
+                    qn = np.zeros(len(p_rows[n]))
+                    qn[int(x[n])] = 1.0
+                else:
+                    qn = np.asarray(q[n], dtype=np.float64)
+                wn, _, _ = oracle.residual_weights(p_rows[n], qn)
             else:
                 wn = p_rows[g]
             self.w.append(wn)
@@ -66,56 +80,154 @@ class DistinctRequest:
         return n
 
 
-@pytest.mark.parametrize("dtype,V,T,D,K,calls", [
-    ("bf16", 32000, 0.7, 32, 256, 123),  # 1,007,616 samples
-    ("f32", 4096, 1.0, 64, 256, 62),     # 1,015,808 samples
-])
-def test_flip_rate_over_a_million_samples(dtype, V, T, D, K, calls):
-    g = 3
-    w = make_dense_custom(40 + V % 7, B=D, gamma=g, V=V, dtype=dtype, temperature=T)
-    reqs = [DistinctRequest(w["logits"][d], w["draft_probs"][d], w["draft_tokens"][d], T) for d in range(D)]
-    L = logits_tensor(w).repeat_interleave(K, dim=0).contiguous()
-    Q = torch.from_numpy(w["draft_probs"]).to(DEV).repeat_interleave(K, dim=0).contiguous()
+def classify(r, u, na, gpu_tok, x):
+    """(tolerated accept flips, tolerated token flips, first hard mismatch or
+    None) of K replicas of distinct request r: uniforms u [K, g+1], GPU accept
+    counts na [K] and emitted tokens gpu_tok [K]."""
+    g = r.g
+    K = len(na)
+    n_ref = np.array([r.accepted(u[k]) for k in range(K)])
+    tok_ref = np.empty(K, dtype=np.int64)
+    for n in np.unique(n_ref):
+        sel = n_ref == n
+        tok_ref[sel] = oracle.inverse_cdf_many(r.w[n], u[sel, g])
+    acc = tok = 0
+    hard = None
+    for k in np.nonzero((na != n_ref) | (gpu_tok != tok_ref))[0]:
+        if na[k] != n_ref[k]:
+            i = min(na[k], n_ref[k])
+            ok = r.qx[i] > 0 and abs(float(u[k, i]) - r.px[i] / r.qx[i]) <= 1e-6
+            acc += ok
+        else:
+            cdf, t = r.cdf[n_ref[k]], int(gpu_tok[k])
+            lo = cdf[t - 1] if t > 0 else 0.0
+            ok = 0 <= t < len(cdf) and (lo - 1e-6) < float(u[k, g]) <= cdf[t] + 1e-6
+            tok += ok
+        if not ok and hard is None:
+            hard = (k, int(na[k]), int(n_ref[k]), int(gpu_tok[k]), int(tok_ref[k]))
+    return acc, tok, hard
+
+
+def run_dense(label, w, K, calls, seed, filt=None):
+    """w: a dense workload of D distinct requests; each replicated K times."""
+    D, g, V, T = w["B"], w["gamma"], w["V"], w["temperature"]
+    q_np = w["draft_probs"]
+    reqs = [DistinctRequest(w["logits"][d], None if q_np is None else q_np[d], w["draft_tokens"][d], T, filt)
+            for d in range(D)]
+    bits = w.get("logits_bits")
+    L = logits_tensor(w["logits"], bits).repeat_interleave(K, dim=0).contiguous()
+    Q = None if q_np is None else torch.from_numpy(q_np).to(DEV).repeat_interleave(K, dim=0).contiguous()
     X = torch.from_numpy(w["draft_tokens"]).to(DEV).repeat_interleave(K, dim=0).contiguous()
     B = D * K
     ws = torch.zeros(api.workspace_size(B * (g + 1), V), dtype=torch.uint8, device=DEV)
-    rng = np.random.default_rng(4242 + V)
+    rng = np.random.default_rng(seed)
     samples = hard = acc_flips = tok_flips = 0
     first_hard = None
     for c in range(calls):
         U = lattice_uniforms(rng, (B, g + 1))
-        out, nacc, _, _ = api.verify_probs(L, Q, X, torch.from_numpy(U).to(DEV), T, workspace=ws)
+        Ut = torch.from_numpy(U).to(DEV)
+        if filt is None:
+            out, nacc, _, _ = api.verify_probs(L, Q, X, Ut, T, workspace=ws)
+        else:
+            out, nacc, _ = api.verify_probs_filtered(L, Q, X, Ut, T, filt[0], filt[1], workspace=ws)
         torch.cuda.synchronize()
         out = out.cpu().numpy()
         nacc = nacc.cpu().numpy()
         for d, r in enumerate(reqs):
             rows = slice(d * K, (d + 1) * K)
-            u = U[rows]
-            n_ref = np.array([r.accepted(u[k]) for k in range(K)])
-            tok_ref = np.empty(K, dtype=np.int64)
-            for n in np.unique(n_ref):
-                sel = n_ref == n
-                tok_ref[sel] = oracle.inverse_cdf_many(r.w[n], u[sel, g])
             o, na = out[rows], nacc[rows]
             x = w["draft_tokens"][d]
-            assert np.all(o[:, :g][np.arange(g)[None, :] < na[:, None]] == np.broadcast_to(x, (K, g))[
-                np.arange(g)[None, :] < na[:, None]])
-            gpu_tok = o[np.arange(K), na]
-            for k in np.nonzero((na != n_ref) | (gpu_tok != tok_ref))[0]:
-                if na[k] != n_ref[k]:
-                    i = min(na[k], n_ref[k])
-                    ok = r.qx[i] > 0 and abs(float(u[k, i]) - r.px[i] / r.qx[i]) <= 1e-6
-                    acc_flips += ok
-                else:
-                    cdf, t = r.cdf[n_ref[k]], int(gpu_tok[k])
-                    lo = cdf[t - 1] if t > 0 else 0.0
-                    ok = 0 <= t < len(cdf) and (lo - 1e-6) < float(u[k, g]) <= cdf[t] + 1e-6
-                    tok_flips += ok
-                if not ok:
-                    hard += 1
-                    first_hard = first_hard or (c, d, k, int(na[k]), int(n_ref[k]), int(gpu_tok[k]), int(tok_ref[k]))
+            mask = np.arange(g)[None, :] < na[:, None]
+            assert np.all(o[:, :g][mask] == np.broadcast_to(x, (K, g))[mask])
+            a, t, h = classify(r, U[rows], na, o[np.arange(K), na], x)
+            acc_flips += a
+            tok_flips += t
+            if h is not None:
+                hard += 1
+                first_hard = first_hard or (c, d) + h
         samples += B
-    print(f"{dtype} V={V}: {samples} samples, {acc_flips} tolerated accept flips, {tok_flips} tolerated token flips, "
-          f"{hard} hard mismatches")
+    report(label, samples, acc_flips, tok_flips, hard, first_hard)
+
+
+def report(label, samples, acc_flips, tok_flips, hard, first_hard):
+    print(f"{label}: {samples} samples, {acc_flips} tolerated accept flips, {tok_flips} tolerated token flips, "
+          f"{hard} hard mismatches", flush=True)
+    assert samples >= 1_000_000
     assert hard == 0, first_hard
     assert acc_flips + tok_flips <= 1e-4 * samples
+
+
+@pytest.mark.parametrize("dtype,V,T,D,K,calls", [
+    ("bf16", 32000, 0.7, 32, 256, 123),  # 1,007,616 samples
+    ("f32", 4096, 1.0, 64, 256, 62),     # 1,015,808 samples
+])
+def test_flip_rate_over_a_million_samples(dtype, V, T, D, K, calls):
+    w = make_dense_custom(40 + V % 7, B=D, gamma=3, V=V, dtype=dtype, temperature=T)
+    run_dense(f"{dtype} V={V}", w, K, calls, 4242 + V)
+
+
+@pytest.mark.parametrize("kind", ["q_rows", "one_hot", "top_k_top_p"])
+def test_flip_rate_headline_recipe(kind):
+    """16 distinct requests of the peaked bf16 recipe (V=128256, gamma=7,
+    T=0.7), 64 replicas each, 977 calls: 1,000,448 emitted samples, with the
+    recipe's q rows, with one-hot drafts, and through top-k 50 / top-p 0.9."""
+    w = make_workload("peaked_bf16", 3, B=16)
+    if kind == "one_hot":
+        w = dict(w, draft_probs=None)
+    run_dense(f"peaked {kind}", w, 64, 977, 777 + len(kind), filt=(50, 0.9) if kind == "top_k_top_p" else None)
+
+
+def test_flip_rate_ragged_recipe():
+    """16 distinct requests of the ragged recipe (V=152064, 1..8 drafts each,
+    independent q), 64 replicas each in the ragged layout, 977 calls:
+    1,000,448 emitted samples."""
+    w = make_workload("ragged_bf16", 4, B=16)
+    D, K, calls, V, T = w["B"], 64, 977, w["V"], w["temperature"]
+    cu = w["cu"].astype(np.int64)
+    reqs, trows, drows, gs = [], [], [], []
+    for d in range(D):
+        d0, d1 = int(cu[d]), int(cu[d + 1])
+        tr = np.arange(d0 + d, d1 + d + 1)
+        reqs.append(DistinctRequest(w["logits"][tr], w["draft_probs"][d0:d1], w["draft_tokens"][d0:d1], T))
+        trows.append(tr)
+        drows.append(np.arange(d0, d1))
+        gs.append(d1 - d0)
+    # replica r of request d sits at batch position d * K + r
+    t_idx = np.concatenate([np.tile(trows[d], K) for d in range(D)])
+    d_idx = np.concatenate([np.tile(drows[d], K) for d in range(D)])
+    glen = np.repeat(np.array(gs), K)
+    rcu = np.concatenate([[0], np.cumsum(glen)]).astype(np.int32)
+    L = logits_tensor(w["logits"], w["logits_bits"])[torch.from_numpy(t_idx).to(DEV)].contiguous()
+    Q = torch.from_numpy(w["draft_probs"]).to(DEV)[torch.from_numpy(d_idx).to(DEV)].contiguous()
+    X = torch.from_numpy(w["draft_tokens"]).to(DEV)[torch.from_numpy(d_idx).to(DEV)].contiguous()
+    CU = torch.from_numpy(rcu).to(DEV)
+    B, T_total = D * K, int(rcu[-1])
+    ws = torch.zeros(api.workspace_size(T_total + B, V), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(991)
+    samples = hard = acc_flips = tok_flips = 0
+    first_hard = None
+    starts = rcu[:-1].astype(np.int64) + np.arange(B)  # first target row of each batch request
+    for c in range(calls):
+        U = lattice_uniforms(rng, (T_total + B,))
+        out, nacc, _, _ = api.verify_ragged(L, Q, X, CU, torch.from_numpy(U).to(DEV), T, workspace=ws)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        nacc = nacc.cpu().numpy()
+        for d, r in enumerate(reqs):
+            g = r.g
+            bs = np.arange(d * K, (d + 1) * K)
+            rows = starts[bs][:, None] + np.arange(g + 1)[None, :]  # [K, g+1] target rows
+            u = U[rows]
+            o = out[rows]
+            na = nacc[bs]
+            x = w["draft_tokens"][int(cu[d]):int(cu[d + 1])]
+            mask = np.arange(g)[None, :] < na[:, None]
+            assert np.all(o[:, :g][mask] == np.broadcast_to(x, (K, g))[mask])
+            a, t, h = classify(r, u, na, o[np.arange(K), na], x)
+            acc_flips += a
+            tok_flips += t
+            if h is not None:
+                hard += 1
+                first_hard = first_hard or (c, d) + h
+        samples += B
+    report("ragged", samples, acc_flips, tok_flips, hard, first_hard)

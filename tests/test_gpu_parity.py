@@ -49,10 +49,11 @@ def test_dense_f32_small(seed):
     gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"dense_f32 B8 stats s{seed}")
 
 
-def test_dense_f32_full():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_dense_f32_full_every_request(seed):
     gh = _gh()
-    w = make_workload("dense_f32", 0)
-    gh.compare(w, gh.run_gpu(w), label="dense_f32 full")
+    w = make_workload("dense_f32", seed)
+    gh.compare_all(w, gh.run_gpu(w), label=f"dense_f32 full s{seed}")
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -63,11 +64,14 @@ def test_peaked_bf16_small(seed):
     gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"peaked B6 stats s{seed}")
 
 
-def test_peaked_bf16_full_sampled():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_peaked_bf16_full_every_request(seed):
+    """The headline batch (B=256, gamma=7, V=128256, bf16, T=0.7), every
+    request against the oracle, five seeds."""
     gh = _gh()
-    w = make_workload("peaked_bf16", 0)
+    w = make_workload("peaked_bf16", seed)
     gpu = gh.run_gpu(w)
-    gh.compare(w, gpu, reqs=sampled(w["B"], 24), label="peaked full")
+    gh.compare_all(w, gpu, label=f"peaked full s{seed}")
     # properties at full size: accepted prefix equals the drafts, padding, ranges
     out, nacc, _, _ = gpu
     g = w["gamma"]
@@ -86,11 +90,13 @@ def test_ragged_small(seed):
     gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"ragged B12 stats s{seed}")
 
 
-def test_ragged_full_sampled():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_ragged_full_every_request(seed):
+    """The ragged batch (B=512, g_b in 1..8, V=152064), every request, five seeds."""
     gh = _gh()
-    w = make_workload("ragged_bf16", 0)
+    w = make_workload("ragged_bf16", seed)
     gpu = gh.run_gpu(w)
-    gh.compare(w, gpu, reqs=sampled(w["B"], 24), label="ragged full")
+    gh.compare_all(w, gpu, label=f"ragged full s{seed}")
     out, nacc, _, _ = gpu
     cu = w["cu"]
     for b in range(w["B"]):
@@ -107,9 +113,10 @@ def test_greedy_small(seed):
     gh.compare(w, gh.run_gpu(w), label=f"greedy B16 s{seed}")
 
 
-def test_greedy_full_all_requests():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_greedy_full_all_requests(seed):
     gh = _gh()
-    w = make_workload("greedy_bf16", 0)
+    w = make_workload("greedy_bf16", seed)
     out, nacc, _, _ = gh.run_gpu(w)
     import oracle
     ro, rn = oracle.verify_greedy(w["logits"], w["draft_tokens"])
@@ -124,10 +131,13 @@ def test_onehot_small(seed):
     gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label=f"onehot B16 stats s{seed}")
 
 
-def test_onehot_full_sampled():
+@pytest.mark.parametrize("seed", SEEDS)
+def test_onehot_full_every_request(seed):
+    """One-hot drafts on the greedy recipe's batch (B=1024, gamma=4,
+    V=128256, T=1), every request, five seeds."""
     gh = _gh()
-    w = make_workload("onehot_bf16", 0)
-    gh.compare(w, gh.run_gpu(w), reqs=sampled(w["B"], 24), label="onehot full")
+    w = make_workload("onehot_bf16", seed)
+    gh.compare_all(w, gh.run_gpu(w), label=f"onehot full s{seed}")
 
 
 # ------------------------------------------------------------ modes and flags
@@ -276,26 +286,37 @@ def test_one_workspace_across_calls_of_every_kind():
     rows = max(big["B"] * (big["gamma"] + 1), len(rag["logits"]))
     ws = torch.zeros(api.workspace_size(rows, 9000), dtype=torch.uint8, device="cuda:0")
 
+    modes = {"eager": api.SV_FLAG_EAGER, "all": api.SV_FLAG_ALL_RESIDUALS, "exact": api.SV_FLAG_EXACT}
+
     def call(w, fresh, kind):
         t = gh.dev_inputs(w)
         k = {} if fresh else {"workspace": ws}
+        st = None
         if kind == "filtered":
             o, n, _ = api.verify_probs_filtered(t["logits"], t["q"], t["x"], t["u"], w["temperature"], 20, 0.9, **k)
         elif kind == "greedy":
             o, n, _ = api.verify_greedy(t["logits"], t["x"], **k)
         elif w["kind"] == "ragged":
-            o, n, _, _ = api.verify_ragged(t["logits"], t["q"], t["x"], t["cu"], t["u"], w["temperature"], **k)
+            o, n, st, _ = api.verify_ragged(t["logits"], t["q"], t["x"], t["cu"], t["u"], w["temperature"],
+                                            flags=modes.get(kind, 0), row_stats=kind == "stats", **k)
         else:
-            o, n, _, _ = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"], **k)
+            o, n, st, _ = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"],
+                                           flags=modes.get(kind, 0), row_stats=kind == "stats", **k)
         torch.cuda.synchronize()
-        return o.cpu().numpy(), n.cpu().numpy()
+        return o.cpu().numpy(), n.cpu().numpy(), None if st is None else st.cpu().numpy()
 
-    seq = [(big, "probs"), (small, "probs"), (rag, "probs"), (big, "filtered"), (oh, "probs"), (big, "greedy"),
-           (small, "filtered"), (big, "probs")]
+    # lazy, filtered and greedy calls interleaved with the eager, all-residuals,
+    # fp64 (exact) and row-statistics modes, whose fp64 list counters share the
+    # fixed counter block with the lazy mode's
+    seq = [(big, "probs"), (small, "eager"), (rag, "probs"), (big, "filtered"), (oh, "all"), (big, "greedy"),
+           (small, "filtered"), (rag, "exact"), (big, "stats"), (oh, "probs"), (small, "exact"), (rag, "stats"),
+           (big, "eager"), (big, "probs")]
     for w, kind in seq + seq:
-        o1, n1 = call(w, False, kind)
-        o2, n2 = call(w, True, kind)
+        o1, n1, s1 = call(w, False, kind)
+        o2, n2, s2 = call(w, True, kind)
         assert np.array_equal(o1, o2) and np.array_equal(n1, n2), kind
+        if s1 is not None:
+            assert np.array_equal(s1, s2, equal_nan=True), kind
 
 
 def test_concurrent_streams_with_their_own_workspaces():
@@ -330,7 +351,7 @@ def test_concurrent_streams_with_their_own_workspaces():
         assert torch.equal(rb[0], ref_b[0]) and torch.equal(rb[1], ref_b[1])
 
 
-@pytest.mark.parametrize("kind", ["probs", "filtered", "greedy"])
+@pytest.mark.parametrize("kind", ["probs", "filtered", "greedy", "ragged", "stats"])
 def test_captured_in_a_hip_graph(kind):
     """A call captured in a HIP graph (the library launches kernels only: no
     allocation, synchronisation or memset) and replayed several times, with
@@ -339,11 +360,19 @@ def test_captured_in_a_hip_graph(kind):
     gh = _gh()
     w = make_workload("peaked_bf16", 10, B=300, V=3000)
     other = make_workload("peaked_bf16", 11, B=40, V=7000)
+    if kind == "ragged":
+        w = make_workload("ragged_bf16", 10, B=300, V=3000)
     t, to = gh.dev_inputs(w), gh.dev_inputs(other)
-    rows = max(w["B"] * (w["gamma"] + 1), other["B"] * (other["gamma"] + 1))
+    rows = max(len(w["uniforms"].reshape(-1)), other["B"] * (other["gamma"] + 1))
     ws = torch.zeros(api.workspace_size(rows, 7000), dtype=torch.uint8, device="cuda:0")
 
     def call(tt, ww):
+        if kind == "ragged" and ww is w:
+            return api.verify_ragged(tt["logits"], tt["q"], tt["x"], tt["cu"], tt["u"], ww["temperature"],
+                                     workspace=ws)[:2]
+        if kind == "stats":
+            return api.verify_probs(tt["logits"], tt["q"], tt["x"], tt["u"], ww["temperature"], row_stats=True,
+                                    workspace=ws)[:3:2]
         if kind == "filtered":
             return api.verify_probs_filtered(tt["logits"], tt["q"], tt["x"], tt["u"], ww["temperature"], 30, 0.9,
                                              workspace=ws)[:2]
@@ -362,12 +391,16 @@ def test_captured_in_a_hip_graph(kind):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         out = call(t, w)
+
+    def same(a, b):  # (row statistics hold NaN for bonus rows)
+        return torch.equal(a.nan_to_num(nan=-1.0), b.nan_to_num(nan=-1.0)) if a.is_floating_point() else torch.equal(a, b)
+
     for _ in range(3):
         call(to, other)  # eager work of another shape on the same workspace
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1])
+        assert same(out[0], ref[0]) and same(out[1], ref[1])
 
 
 def test_ragged_equals_dense():
@@ -459,6 +492,49 @@ def test_draft_equals_target_distribution():
     gpu = gh.run_gpu(w)
     gh.compare(w, gpu, label="q = p")
     gh.compare(w, gh.run_gpu(w, stats=True), stats=True, label="q = p stats")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("flags", [0, api.SV_FLAG_EAGER, api.SV_FLAG_ALL_RESIDUALS])
+@pytest.mark.parametrize("log2_delta,fallback", [(-30, True), (-26, False)])
+def test_residual_fallback_forced(dtype, flags, log2_delta, fallback):
+    """The 1e-8 fallback ([GUIDE] Step 2) forced and asserted. Every target row
+    holds equal logits over V = 4096, so p = 2^-12 exactly. Position 0's q moves
+    delta = 2^log2_delta from token y to the draft token x (q(x) = p + delta,
+    q(y) = p - delta, q = p elsewhere; all exact in fp32); its accept uniform
+    is 1, so x is rejected and the residual max(0, p - q) is delta at y alone.
+    delta = 2^-30 (9.3e-10, not above 1e-8): the replacement is drawn from p
+    (token ceil(4096 u) - 1) and the row's record carries SV_ROW_FALLBACK;
+    delta = 2^-26 (1.5e-8): the replacement is y and the bit is clear. Default
+    (lazy), eager and all-residuals modes, each against the oracle."""
+    from rejection_sampling_verifier_spec_amd.workloads import f32_to_bf16_bits
+    gh = _gh()
+    rng = np.random.default_rng(70 + log2_delta)
+    B, g, V, T = 16, 2, 4096, 0.9
+    delta = 2.0 ** log2_delta
+    l = np.zeros((B, g + 1, V), dtype=np.float32)
+    q = np.full((B, g, V), 2.0 ** -12, dtype=np.float32)
+    x = np.zeros((B, g), dtype=np.int64)
+    ys = []
+    for b in range(B):
+        xb, yb = (37 * b + 5) % V, (4000 - 13 * b) % V
+        q[b, 0, xb] += np.float32(delta)
+        q[b, 0, yb] -= np.float32(delta)
+        x[b, 0] = xb
+        x[b, 1] = int(rng.integers(0, V))
+        ys.append(yb)
+    assert np.all(q.astype(np.float64)[:, 0].sum(-1) == 1.0)
+    u = lattice_uniforms(rng, (B, g + 1))
+    u[:, 0] = 1.0
+    w = dict(kind="dense", B=B, gamma=g, V=V, dtype=dtype, temperature=T, logits=l,
+             logits_bits=f32_to_bf16_bits(l) if dtype == "bf16" else None, draft_probs=q, draft_tokens=x, uniforms=u)
+    out, nacc, _, rec = gpu = gh.run_gpu(w, flags=flags)
+    gh.compare(w, gpu, label=f"fallback {dtype} flags={flags} delta=2^{log2_delta}")
+    assert np.all(nacc == 0)
+    expect = np.ceil(u[:, g].astype(np.float64) * V).astype(np.int64) - 1 if fallback else np.array(ys)
+    assert np.array_equal(out[:, 0], expect)
+    bits = rec.reshape(B, g + 1, 2)[:, 0, 1] & api.SV_ROW_FALLBACK
+    assert np.all(bits != 0) if fallback else np.all(bits == 0)
 
 
 def test_disjoint_support():
@@ -594,3 +670,105 @@ def test_hardware_exp2_within_the_assumed_bound():
     measured, assumed = api.selftest_exp2()
     print(f"exp2 max relative error {measured:.3e} (assumed bound {assumed:.3e})")
     assert 0.0 < measured <= assumed
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiny_temperature(dtype):
+    """T = 1e-6: the scale log2(e) / T = 1.4e6 keeps every fp32 product finite
+    and p is one-hot at the argmax up to terms below 2^-1000 (each draft is
+    accepted iff it is the argmax, unless tied); with q rows, one-hot drafts
+    and top-k / top-p."""
+    gh = _gh()
+    w = make_dense_custom(61, B=16, gamma=3, V=5000, dtype=dtype, temperature=1e-6)
+    x = w["draft_tokens"].copy()
+    x[::2, 0] = np.argmax(w["logits"][::2, 0], axis=-1)  # plant some argmax drafts
+    w["draft_tokens"] = x
+    gh.compare(w, gh.run_gpu(w), label=f"T=1e-6 {dtype}")
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label=f"T=1e-6 {dtype} one-hot")
+    gh.compare(w, gh.run_gpu_filtered(w, 20, 0.9), label=f"T=1e-6 {dtype} filtered", filt=(20, 0.9))
+
+
+def test_outputs_untouched_outside_their_extent():
+    """Guard bands: out_tokens and num_accepted handed to the C ABI as views
+    into larger buffers filled with a canary; after dense, ragged, filtered,
+    greedy and one-hot calls the canaries around each output are intact and
+    the outputs equal those of the binding's own buffers."""
+    import ctypes
+    gh = _gh()
+    lib = api.load()
+    pad = 4096
+    dev = torch.device("cuda:0")
+    p = lambda tt: None if tt is None else ctypes.c_void_p(tt.data_ptr())
+
+    def guarded(n, dtype):
+        full = torch.full((n + 2 * pad,), -12345, dtype=dtype, device=dev)
+        return full, full[pad:pad + n]
+
+    def check(full, n):
+        torch.cuda.synchronize()
+        assert torch.all(full[:pad] == -12345) and torch.all(full[pad + n:] == -12345)
+
+    ws = torch.zeros(api.workspace_size(4000, 6000), dtype=torch.uint8, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    w = make_workload("peaked_bf16", 14, B=40, V=6000)
+    t = gh.dev_inputs(w)
+    B, g1, V = w["B"], w["gamma"] + 1, w["V"]
+    for kind in ("probs", "onehot", "filtered", "greedy"):
+        fo, o = guarded(B * g1, torch.int64)
+        fn, n = guarded(B, torch.int32)
+        q = None if kind == "onehot" else t["q"]
+        if kind == "filtered":
+            rc = lib.spec_verify_probs_filtered(p(t["logits"]), api.SV_DTYPE_BF16, p(q), p(t["x"]), p(t["u"]), B,
+                                                g1 - 1, V, 0.7, 20, 0.9, p(o), p(n), p(ws), ws.numel(), st)
+            ref = api.verify_probs_filtered(t["logits"], q, t["x"], t["u"], 0.7, 20, 0.9)
+        elif kind == "greedy":
+            rc = lib.spec_verify_greedy(p(t["logits"]), api.SV_DTYPE_BF16, p(t["x"]), B, g1 - 1, V, p(o), p(n),
+                                        p(ws), ws.numel(), st)
+            ref = api.verify_greedy(t["logits"], t["x"])
+        else:
+            rc = lib.spec_verify_probs(p(t["logits"]), api.SV_DTYPE_BF16, p(q), p(t["x"]), p(t["u"]), B, g1 - 1, V,
+                                       0.7, 0, p(o), p(n), None, p(ws), ws.numel(), st)
+            ref = api.verify_probs(t["logits"], q, t["x"], t["u"], 0.7)
+        assert rc == 0, kind
+        check(fo, B * g1)
+        check(fn, B)
+        assert torch.equal(o.view(B, g1), ref[0]) and torch.equal(n, ref[1]), kind
+    wr = make_workload("ragged_bf16", 14, B=40, V=6000)
+    tr = gh.dev_inputs(wr)
+    rows = len(wr["uniforms"])
+    fo, o = guarded(rows, torch.int64)
+    fn, n = guarded(wr["B"], torch.int32)
+    rc = lib.spec_verify_ragged(p(tr["logits"]), api.SV_DTYPE_BF16, p(tr["q"]), p(tr["x"]), p(tr["cu"]), p(tr["u"]),
+                                wr["B"], len(wr["draft_tokens"]), wr["V"], 1.0, 0, p(o), p(n), None, p(ws),
+                                ws.numel(), st)
+    assert rc == 0
+    check(fo, rows)
+    check(fn, wr["B"])
+    ref = api.verify_ragged(tr["logits"], tr["q"], tr["x"], tr["cu"], tr["u"], 1.0)
+    assert torch.equal(o, ref[0]) and torch.equal(n, ref[1])
+
+
+def test_side_stream_with_a_fresh_workspace():
+    """stream= another stream than torch's current one, no workspace given:
+    the binding allocates the outputs and zero-fills the new workspace on that
+    stream, ahead of the library's kernels (the current stream is kept busy
+    meanwhile); results equal a call on the current stream."""
+    gh = _gh()
+    w = make_workload("peaked_bf16", 15, B=300, V=4000)
+    t = gh.dev_inputs(w)
+    ref = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    busy = torch.randn(4096, 4096, device="cuda:0")
+    for _ in range(5):
+        for _ in range(4):
+            busy = busy @ busy.T / 64.0  # work queued on the current stream
+        out, nacc, _, ws = api.verify_probs(t["logits"], t["q"], t["x"], t["u"], w["temperature"], stream=side)
+        side.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(nacc, ref[1])
+        o2, n2, _ = api.verify_probs_filtered(t["logits"], t["q"], t["x"], t["u"], w["temperature"], 20, 0.9,
+                                              stream=side)
+        side.synchronize()
+        assert torch.all((o2 >= -1) & (o2 < w["V"]))
+    torch.cuda.synchronize()

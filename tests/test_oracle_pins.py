@@ -188,6 +188,38 @@ def test_residual_fallback_constant():
     assert oracle.SAMPLE_FALLBACK_MASS == 1e-8
 
 
+@pytest.mark.parametrize("m,fallback", [
+    (0.5e-8, True), (0.99e-8, True), (1e-8, True),          # not above 1e-8: draw from p
+    (float(np.nextafter(1e-8, 1.0)), False), (1.01e-8, False), (2e-8, False),
+])
+def test_residual_fallback_at_the_threshold(m, fallback):
+    """[GUIDE] Step 2: the replacement is drawn from p when the residual mass
+    is not above 1e-8. Rows built so that the residual mass is exactly m in
+    float64: p = [m, 1 - m] against q = [0, 1] leaves max(0, p - q) = [m, 0]
+    (the second difference is negative). The threshold itself (the float64
+    nearest 1e-8) falls back, the next float above it does not."""
+    p = np.array([m, 1.0 - m])
+    w, mass, fb = residual_weights(p, np.array([0.0, 1.0]))
+    assert mass == m
+    assert fb is fallback
+    assert np.array_equal(w, p if fallback else np.array([m, 0.0]))
+
+
+@pytest.mark.parametrize("m,fallback", [(0.99e-8, True), (1e-8, True), (1.01e-8, False)])
+def test_residual_fallback_decides_the_emitted_token(m, fallback):
+    """The fallback seen through a whole request: one draft x = 2 with
+    q(x) = 1/2 > p(x) = 1/2 - m, rejected at u = 1; the residual
+    max(0, p - q) = [m, 0, 0] has mass m. Drawn from the residual, the sample
+    uniform 0.75 gives token 0 (the only positive weight); drawn from p
+    (C = [m, 1/2 + m, 1]) it gives token 2."""
+    p1 = np.array([m, 0.5, 0.5 - m])
+    q1 = np.array([0.0, 0.5, 0.5])
+    bonus = np.array([0.25, 0.25, 0.5])
+    toks, n = oracle.verify_request([p1, bonus], [q1], [2], [1.0, 0.75])
+    assert n == 0
+    assert toks == [2 if fallback else 0]
+
+
 def test_recovered_token_never_the_rejected_draft():
     """A rejection needs p(x) < q(x), so max(0, p - q) is zero at x: the
     recovered token differs from the rejected draft (outside the fallback)."""
