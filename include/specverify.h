@@ -21,9 +21,11 @@
  *
  * Conventions shared by every entry point:
  *  - All array arguments are DEVICE pointers owned by the caller. The library
- *    keeps no state, never allocates, never synchronises; work is enqueued on
- *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and the
- *    outputs are valid once that stream has completed the work.
+ *    never allocates and never synchronises, and keeps no state apart from the
+ *    fixed scratch of spec_verify_probs_noalloc (and the host-side benchmark
+ *    diagnostics); work is enqueued on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream) and the outputs are valid once that
+ *    stream has completed the work.
  *  - Target temperature: p = softmax(logits / T) for T > 0; T == 0 means
  *    argmax decoding (p one-hot at the argmax, lowest index on ties).
  *  - Accept test, in product form: x is kept iff p(x) > 0 and u * q(x) <= p(x).
@@ -131,7 +133,8 @@ size_t spec_verify_workspace_size(int64_t num_target_rows, int32_t vocab_size);
 /* Static, human-readable text for a status code. */
 const char* spec_verify_status_string(int status);
 
-/* Library ABI version (currently 2: the *_filtered entry points). */
+/* Library ABI version (currently 3: 2 added the *_filtered entry points, 3
+ * spec_verify_probs_noalloc). */
 int spec_verify_version(void);
 
 /* Self-check of the one hardware property the certified fast path relies on:
@@ -203,6 +206,30 @@ int spec_verify_probs(const void* target_logits, int logits_dtype, const float* 
                       int32_t gamma, int32_t vocab_size, double temperature, uint32_t flags,
                       int64_t* out_tokens, int32_t* num_accepted, float* row_stats,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_probs_noalloc - spec_verify_probs for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The same verification and arguments as
+ * spec_verify_probs, minus the workspace: the library's own fixed device
+ * array of SV_NOALLOC_SCRATCH_BYTES takes its place (one per device, held
+ * until the process ends).
+ *  - Allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *  - A batch that needs more (spec_verify_workspace_size(B * (gamma + 1), V)
+ *    above SV_NOALLOC_SCRATCH_BYTES) returns SV_ERR_WORKSPACE and launches
+ *    nothing.
+ *  - Every call on a device shares that device's array: calls that overlap
+ *    in time on one device (several streams or host threads) race and must
+ *    be ordered by the caller (one stream, or events).
+ *  - The first call on a device looks up the array's address and enqueues a
+ *    zero-fill of it on `stream`, ahead of its own kernels; every completed
+ *    call leaves the array ready for the next call of any shape.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_probs_noalloc(const void* target_logits, int logits_dtype, const float* draft_probs,
+                              const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
+                              int32_t gamma, int32_t vocab_size, double temperature, uint32_t flags,
+                              int64_t* out_tokens, int32_t* num_accepted, float* row_stats, void* stream);
 
 /*
  * spec_verify_greedy - dense batch, argmax verification (temperature 0; the

@@ -38,7 +38,9 @@ SV_PROFILE_REQUEST = 1
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
            "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
            "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop",
-           "spec_verify_probs_filtered", "spec_verify_ragged_filtered", "spec_verify_stream_read")
+           "spec_verify_probs_filtered", "spec_verify_ragged_filtered", "spec_verify_stream_read",
+           "spec_verify_probs_noalloc")
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -78,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_profile_stop.restype = ctypes.c_int
     lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_probs.restype = ctypes.c_int
+    lib.spec_verify_probs_noalloc.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp]
+    lib.spec_verify_probs_noalloc.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.restype = ctypes.c_int
     lib.spec_verify_ragged.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp,
@@ -181,6 +185,46 @@ def verify_probs(logits, draft_probs, draft_tokens, uniforms, temperature, flags
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_probs")
     return out, nacc, stats, workspace
+
+
+def verify_probs_noalloc(logits, draft_probs, draft_tokens, uniforms, temperature, flags=0, row_stats=False,
+                         out=None, stream=None):
+    """verify_probs through spec_verify_probs_noalloc: no workspace (the
+    library's fixed per-device scratch instead), and with `out` = (out_tokens,
+    num_accepted[, row_stats]) given, no allocation here either. Returns
+    (out_tokens, num_accepted, row_stats or None)."""
+    lib = load()
+    dev = logits.device
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, gamma+1, V]")
+    B, g1, V = logits.shape
+    g = g1 - 1
+    _check(logits, "logits", device=dev)
+    _check(draft_probs, "draft_probs", torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", torch.int64, dev)
+    _check(uniforms, "uniforms", torch.float32, dev)
+    if draft_probs is not None and tuple(draft_probs.shape) != (B, g, V):
+        raise ValueError("draft_probs must be [B, gamma, V]")
+    if tuple(draft_tokens.shape) != (B, g) or tuple(uniforms.shape) != (B, g1):
+        raise ValueError("draft_tokens must be [B, gamma] and uniforms [B, gamma+1]")
+    s = _launch_stream(dev, stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            o = torch.empty((B, g1), dtype=torch.int64, device=dev)
+            nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+            stats = torch.empty((B, g1, 4), dtype=torch.float32, device=dev) if row_stats else None
+        else:
+            o, nacc = out[0], out[1]
+            stats = out[2] if row_stats else None
+            _check(o, "out_tokens", torch.int64, dev)
+            _check(nacc, "num_accepted", torch.int32, dev)
+            _check(stats, "row_stats", torch.float32, dev)
+        rc = lib.spec_verify_probs_noalloc(_ptr(logits), _dtype_code(logits), _ptr(draft_probs), _ptr(draft_tokens),
+                                           _ptr(uniforms), B, g, V, float(temperature), int(flags), _ptr(o),
+                                           _ptr(nacc), _ptr(stats), _handle(s))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_probs_noalloc")
+    return o, nacc, stats
 
 
 def verify_greedy(logits, draft_tokens, workspace=None, stream=None):

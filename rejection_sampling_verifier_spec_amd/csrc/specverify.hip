@@ -46,6 +46,7 @@
 #include <float.h>
 #include <math.h>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 
@@ -54,6 +55,9 @@
 // The error bound of the fast path follows the rounding steps as written:
 // no multiply-add is fused unless the source says fmaf.
 #pragma clang fp contract(off)
+
+// Scratch of spec_verify_probs_noalloc (see scratch_for_device).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -3767,6 +3771,47 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
   return finish_launch();
 }
 
+// ----------------------------------------------------------------------------
+// fixed scratch of spec_verify_probs_noalloc (callers that cannot allocate)
+
+// One copy per device, held until the process ends; its address on a device
+// comes from hipGetSymbolAddress with that device current (the array's name
+// is a host-side stand-in in host code and is never passed to a kernel).
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte blocks");
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n) {
+  const size_t step = static_cast<size_t>(gridDim.x) * 256;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += step) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // per device: the scratch's device address, once set up
+
+// The scratch's device address on the current device. The first call on a
+// device looks it up and enqueues a zero-fill of the whole scratch on `st`
+// (the workspace contract: zero-filled before its first use; every completed
+// call leaves it ready for the next).
+int scratch_for_device(void** out, hipStream_t st);
+
+}  // namespace
+
+namespace {
+int scratch_for_device(void** out, hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SV_ERR_LAUNCH;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(256), dim3(256), 0, st, static_cast<uint4*>(ptr), kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return SV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -3787,7 +3832,7 @@ const char* spec_verify_status_string(int status) {
   }
 }
 
-int spec_verify_version(void) { return 2; }
+int spec_verify_version(void) { return 3; }
 
 double spec_verify_exp2_error_bound(void) { return kEpsExp; }
 
@@ -3881,6 +3926,25 @@ int spec_verify_probs(const void* target_logits, int logits_dtype, const float* 
   return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, nullptr, uniforms, num_requests,
                        gamma, static_cast<int32_t>(nd), vocab_size, temperature, flags, out_tokens, num_accepted,
                        row_stats, workspace, workspace_bytes, stream, false);
+}
+
+int spec_verify_probs_noalloc(const void* target_logits, int logits_dtype, const float* draft_probs,
+                              const int64_t* draft_tokens, const float* uniforms, int32_t num_requests,
+                              int32_t gamma, int32_t vocab_size, double temperature, uint32_t flags,
+                              int64_t* out_tokens, int32_t* num_accepted, float* row_stats, void* stream) {
+  if (num_requests < 0 || gamma < 0) return SV_ERR_INVALID_ARGUMENT;
+  const int64_t nd = static_cast<int64_t>(num_requests) * gamma;
+  if (nd > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+  if (vocab_size < 1 || vocab_size > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+  if (num_requests == 0) return SV_OK;
+  if (ws_layout(nd + num_requests, vocab_size).total > kScratchBytes) return SV_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int rc = scratch_for_device(&ws, st);
+  if (rc != SV_OK) return rc;
+  return verify_common(target_logits, logits_dtype, draft_probs, draft_tokens, nullptr, uniforms, num_requests,
+                       gamma, static_cast<int32_t>(nd), vocab_size, temperature, flags, out_tokens, num_accepted,
+                       row_stats, ws, kScratchBytes, stream, false);
 }
 
 int spec_verify_greedy(const void* target_logits, int logits_dtype, const int64_t* draft_tokens,

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert sorted(declared_functions()) == sorted(api.EXPORTS)
-    assert lib.spec_verify_version() == 2
+    assert lib.spec_verify_version() == 3
 
 
 def test_status_strings(lib):
@@ -182,3 +182,33 @@ def test_profile_argument_validation(lib):
     assert lib.spec_verify_profile_stop(ctypes.cast(total, ctypes.c_void_p), ctypes.cast(count, ctypes.c_void_p)) == 0
     assert list(total) == [0.0, 0.0] and list(count) == [0, 0]
 
+
+def noalloc(lib, **kw):
+    a = dict(logits=FAKE, dtype=1, q=FAKE, x=FAKE, u=FAKE, B=2, g=3, V=100, T=1.0, flags=0, out=FAKE, nacc=FAKE,
+             stats=None, stream=None)
+    a.update(kw)
+    return lib.spec_verify_probs_noalloc(a["logits"], a["dtype"], a["q"], a["x"], a["u"], a["B"], a["g"], a["V"],
+                                         a["T"], a["flags"], a["out"], a["nacc"], a["stats"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), -1),
+    (dict(g=-1), -1),
+    (dict(V=0), -2),
+    (dict(V=(1 << 21) + 1), -2),
+    (dict(B=1200, g=7, V=128256), -4),   # more workspace than the fixed scratch holds
+    (dict(B=1 << 16, g=7, V=1 << 21), -4),
+    (dict(B=0), 0),
+])
+def test_noalloc_argument_validation(lib, kw, status):
+    """Checked on the host before the scratch is set up or anything launched."""
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_limit_matches_the_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define SV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.SV_NOALLOC_SCRATCH_BYTES
+    # the largest workloads the bench measures fit (workspace of each)
+    for rows, V in ((256 * 8, 128256), (2819, 152064), (1024 * 5, 128256), (64 * 6, 32000)):
+        assert api.workspace_size(rows, V) <= api.SV_NOALLOC_SCRATCH_BYTES
