@@ -568,7 +568,7 @@ def main():
                      "note": "HIP events recorded by the library on the launch stream around the per-row "
                              "pass (both launches) in the timed region; bytes: the logit rows it read, 16 B per "
                              "draft row read, its records and statistics (mean over the input sets)"},
-        "request_stage": {"kernel": "request_pass_kernel + request_finish_kernel (per-request fp64 stage)",
+        "request_stage": {"kernel": "request_kernel (per-request fp64 pass and finish, one launch)",
                           "bytes_per_launch": b["request_stage"],
                           "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
                           "achieved_GBps": b["request_stage"] / req_s / 1e9 if req_n else None},

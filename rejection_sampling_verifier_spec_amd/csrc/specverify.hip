@@ -2299,29 +2299,36 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   int hcnt2 = 0;
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
-    const float c = -(ref * s);
+    // the tile's maximum first: a tile that raises the wave's reference is
+    // summed once, against the raised one
     float lm = -INFINITY;
-    float e4[4] = {0.f, 0.f, 0.f, 0.f};
-    float a4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kLaneElems; ++k) {
-      const float v = r.get(k);
-      lm = fmaxf(lm, v);
-      const float arg = fmaf(v, s, c);
-      const float e = fexp2(arg);
-      e4[k & 3] += e;
-      a4[k & 3] = fmaf(e, arg, a4[k & 3]);
-    }
+    for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, r.get(k));
+    if (__any(lm > ref)) ref = fmaxf(ref, wave_max(lm));
     if constexpr (FILTER) {
       if (__any(lm >= cut2))
         head_append_count_wave<LT, VEC>(r, base, V, lane, cut1, cut2, fsp->head + wave * (kHeadCap / kWaves),
                                         kHeadCap / kWaves, hcnt, hcnt2);
     }
-    float es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
-    float ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-    const bool redo = lm > ref || !(ea == ea) || base + kTile > V || (xmask >= base && xmask < base + kTile);
-    if (__any(redo)) {
-      ref = fmaxf(ref, wave_max(lm));
+    float es = 0.f, ea = 0.f;
+    const bool special = base + kTile > V || (xmask >= base && xmask < base + kTile);  // uniform
+    if (!special && ref != -INFINITY) {
+      const float c = -(ref * s);
+      float e4[4] = {0.f, 0.f, 0.f, 0.f};
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) {
+        const float arg = fmaf(r.get(k), s, c);
+        const float e = fexp2(arg);
+        e4[k & 3] += e;
+        a4[k & 3] = fmaf(e, arg, a4[k & 3]);
+      }
+      es = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+      ea = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    }
+    // the careful sum: the partial last tile, the one-hot token's tile, and a
+    // tile with a -inf or a NaN (e a = NaN)
+    if (__any(special || !(ea == ea))) {
       es = 0.f;
       ea = 0.f;
       if (ref != -INFINITY) tile_sum_careful(r, base, ref, es, ea);
@@ -2914,7 +2921,7 @@ __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j ==
 
 struct ReqShared {
   double part[4];  // per-wave partial sums (an undecided tile)
-  double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see request_finish_kernel)
+  double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see finish_row)
   int first;    // first row not yet accepted
   int nund;     // tiles with undecided elements
   int cross, lastpos;
@@ -3036,12 +3043,10 @@ __device__ __forceinline__ bool request_range(const ProbsArgs& a, int b, int& d0
   return true;
 }
 
-constexpr int kPassNT = 256;       // threads per block of the pass kernel
+constexpr int kPassNT = 256;       // threads per block of the per-request kernel
 constexpr int kPassWaves = kPassNT / 64;
-constexpr int kPassSlices = 3;     // blocks per request in the pass kernel
-constexpr int kFinishNT = 256;     // threads per block of the finish kernel
-constexpr int kFinishWaves = kFinishNT / 64;
-static_assert(kFinishWaves == 4, "the finish kernel's in-tile search maps 16 scan lanes to each of four waves");
+constexpr int kMaxSlices = 16;     // most blocks per request
+static_assert(kPassWaves == 4, "the finish's in-tile search maps 16 scan lanes to each of four waves");
 
 // One-hot drafts (no q rows): the draft token of draft row d when it lies in
 // the vocabulary, else -1; -1 for a bonus row or when q rows are given.
@@ -3057,59 +3062,19 @@ struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the 
   double* Q;
 };
 
-// Lazy mode, per-request pass: kPassSlices blocks per request, each over a
-// slice of the deciding row's tiles.
-// Lazy mode, per-request pass: kPassSlices blocks per request, each over a
-// slice of the deciding row's tiles.
-// HASQ = false (one-hot drafts, no q rows): every deciding row needs only its
-// tile sums of e, and the kernel is built without the residual's per-element
-// work (fewer registers, more waves per SIMD).
-constexpr int kPassSlicesE = 3;  // blocks per request of the e-only pass (HASQ = false)
-template <typename LT, bool VEC, bool FILTER, bool HASQ = true>
-__global__ __launch_bounds__(kPassNT, HASQ ? 1 : 4) void request_pass_kernel(ProbsArgs a, PassArrays pa) {
-  constexpr int kSl = HASQ ? kPassSlices : kPassSlicesE;
-  __shared__ double tab[kExp2Tab];
-  __shared__ int slot;
-  const int b = blockIdx.x / kSl, sl = blockIdx.x % kSl;
-  const int V = a.V, nt = (V + kTile - 1) / kTile;
-  const int wave = threadIdx.x >> 6;
-  int d0, d1;
-  if (!request_range(a, b, d0, d1)) return;
-  const int g = d1 - d0;
-  const int64_t t0 = static_cast<int64_t>(d0) + b;
-  exp2_table_init(tab);
-  const int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &slot);  // (its barriers also publish tab)
-  const Exp2Consts C = exp2_consts_load();
-  const int64_t trow = t0 + n;
-  const bool draft = n < g;
-  const double4 st = a.rstat[trow];
-  const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
-  const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
-  const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
-  const int per = (nt + kSl - 1) / kSl;
-  const int j0 = sl * per, j1 = min(nt, j0 + per);
-  const int64_t o = static_cast<int64_t>(b) * nt;
-  // a one-hot draft row needs only the tile sums of e (its residual is p
-  // without x's element, taken out of its tile by the finish kernel)
-  if constexpr (HASQ)
-    fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
-                                   kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
-  else
-    fp64_row_pass<LT, VEC, FILTER>(lrow, nullptr, V, nt, st.x, a.s64, zhi, zlo, false, j0 + wave, j1, kPassWaves,
-                                   tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
-}
-
-// Lazy mode, per-request finish: one block per request. Z from the pass's
-// tile sums; an undecided accept test settled exactly (if the row is accepted
-// after all, the next open row gets its fp64 pass here, in LDS); residual tile
-// sums W_j = P_j / Z - Q_j, tiles with undecided elements summed again with
-// Z; then wave 0 draws the token and writes the request's outputs.
+// The finish of one request at its open row n (the first row whose own
+// accept test did not pass), by one block of kPassNT threads, with the row's
+// tile sums E_j, P_j, Q_j already in LDS: Z = sum_j E_j; an undecided accept
+// test settled exactly - if the row is accepted after all, its record says so
+// and the function returns true (the caller takes the next open row);
+// otherwise residual tile sums W_j = P_j / Z - Q_j, tiles with undecided
+// elements summed again with Z, residual mass <= 1e-8 falls back to p, wave 0
+// draws the token (tile search, then in-tile search, in fp64) and writes the
+// request's outputs, and the function returns false.
 template <typename LT, bool VEC, bool FILTER>
-__global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa) {
-  extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
-  __shared__ BlockScratchT<kFinishNT> sc;
-  __shared__ ReqShared rs;
-  __shared__ double tab[kExp2Tab];
+__device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int d0, int d1, int n, double* rbuf,
+                           BlockScratchT<kPassNT>& sc, ReqShared& rs, const double* __restrict__ tab,
+                           const Exp2Consts& C) {
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
   double* E = rbuf;
@@ -3118,24 +3083,12 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
   double* W = rbuf + 3 * nt;
   int* ulist = reinterpret_cast<int*>(rbuf + 4 * nt);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x;
-
-  int d0, d1;
-  if (!request_range(a, b, d0, d1)) {
-    if (tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
-    return;
-  }
   const int g = d1 - d0;
   const int64_t t0 = static_cast<int64_t>(d0) + b;
   const double s = a.s64;
   const double u_smp = static_cast<double>(a.u[t0 + g]);  // the request's sample uniform
-  exp2_table_init(tab);
-  const Exp2Consts C = exp2_consts_load();
 
-  int start = 0;
-  bool from_pass = true;  // the first open row's tile sums come from the pass kernel
-  for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
-    const int n = first_open_row<kFinishNT>(a.ws, t0, start, g, &rs.first);
+  {
     const int64_t trow = t0 + n;
     const bool draft = n < g;
     const uint32_t f0 = static_cast<uint32_t>(a.ws[trow].y);
@@ -3149,23 +3102,10 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
     const float* __restrict__ qrow = (draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
     const int hot = onehot_index(a, draft, d0 + n);
     const bool onehot = draft && !a.q;
-    if (from_pass) {
-      const int64_t o = static_cast<int64_t>(b) * nt;
-      for (int j = tid; j < nt; j += kFinishNT) {
-        E[j] = pa.E[o + j];
-        P[j] = pa.P[o + j];
-        Q[j] = pa.Q[o + j];
-      }
-    } else {  // a later row (an undecided accept test turned out accepted): its pass here
-      const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
-      fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, m, s, zhi, zlo, qrow != nullptr, wave, nt, kFinishWaves, tab,
-                                     C, E, P, Q, keep_min);
-    }
-    __syncthreads();
-    for (int j = tid; j < nt; j += kFinishNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
+    for (int j = tid; j < nt; j += kPassNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
     double zl = 0.0;
-    for (int j = tid; j < nt; j += kFinishNT) zl += E[j];
-    const double Z = block_sum<kFinishNT>(zl, sc);
+    for (int j = tid; j < nt; j += kPassNT) zl += E[j];
+    const double Z = block_sum<kPassNT>(zl, sc);
     const double iz = 1.0 / Z;
 
     uint32_t rflags = undecided ? (kRowExact | kWhyAccept) : 0u;
@@ -3178,10 +3118,8 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
         if (tid == 0)
           a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags | (f0 & (kRowHead2 | kRowRowSelect))));
-        start = n + 1;
-        from_pass = false;
         __syncthreads();
-        continue;
+        return true;
       }
     }
 
@@ -3194,12 +3132,12 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       // nothing
       const int jx = hot >= 0 ? hot / kTile : -1;
       const double ex = hot >= 0 ? exp2_neg(fma(static_cast<double>(to_float(lrow[hot])), s, nms), tab) : 0.0;
-      for (int j = tid; j < nt; j += kFinishNT) W[j] = (j == jx ? fmax(0.0, E[j] - ex) : E[j]) * iz;
+      for (int j = tid; j < nt; j += kPassNT) W[j] = (j == jx ? fmax(0.0, E[j] - ex) : E[j]) * iz;
       __syncthreads();
     } else if (draft) {
       if (tid == 0) rs.nund = 0;
       __syncthreads();
-      for (int j = tid; j < nt; j += kFinishNT) {
+      for (int j = tid; j < nt; j += kPassNT) {
         if (W[j] < 0.0) ulist[atomicAdd(&rs.nund, 1)] = j;
         else W[j] = fmax(0.0, P[j] * iz - Q[j]);
       }
@@ -3312,7 +3250,7 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       }
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0) return false;
     const int k0 = jt * kTile + 32 * lane;
     double ls = 0.0;
 #pragma unroll 8
@@ -3352,7 +3290,92 @@ __global__ __launch_bounds__(kFinishNT) void request_finish_kernel(ProbsArgs a, 
       sel.nacc[b] = n;
       a.ws[trow] = make_int2(token, static_cast<int>(rflags | (f0 & (kRowHead2 | kRowRowSelect))));
     }
+    return false;
+  }
+}
+
+// Lazy mode, per-request stage: for each request, the fp64 pass over its
+// deciding row (its first open row) - per tile, the sum E_j of
+// e_k = 2^((l_k - m) log2(e) / T) and the part of the residual sum that the
+// certified Z interval [zlo, zhi] of the per-row pass already decides: P_j
+// and Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
+// every Z in the interval (P_j = -1: an element left undecided) - then
+// finish_row. One kernel template, three ways to launch it:
+//   kReqFused:  one block per request does the whole row into LDS and the
+//               finish (when the requests alone fill the chip's block slots);
+//   kReqPass:   `slices` blocks per request, each a slice of the row's tiles,
+//               the sums to device memory (plain stores: the finish is a
+//               launch of its own);
+//   kReqFinish: one block per request reads the sums into LDS and finishes.
+// A later open row (an undecided accept test that turned out accepted, rare)
+// gets its whole pass from the finishing block alone, in LDS.
+// HASQ = false (one-hot drafts, no q rows): every deciding row needs only its
+// tile sums of e, and the kernel is built without the residual's per-element
+// work (fewer registers, more waves per SIMD).
+enum RequestMode { kReqFused = 0, kReqPass = 1, kReqFinish = 2 };
+
+// Blocks of the per-request kernel resident per compute unit, the register
+// budget its pass builds are held to: three with bf16 logits and q rows (at
+// most 168 VGPRs), two with fp32 logits (their raw chunks take twice the
+// registers) or scalar loads, four without q rows (128 VGPRs).
+template <typename LT, bool VEC, bool HASQ>
+constexpr int request_blocks_per_cu() {
+  return !HASQ ? 4 : ((VEC && sizeof(LT) == 2) ? 3 : 2);
+}
+
+template <typename LT, bool VEC, bool FILTER, bool HASQ, int MODE>
+__global__ __launch_bounds__(kPassNT, (MODE == kReqFinish ? 1 : request_blocks_per_cu<LT, VEC, HASQ>())) void
+request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
+  extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
+  __shared__ BlockScratchT<kPassNT> sc;
+  __shared__ ReqShared rs;
+  __shared__ double tab[kExp2Tab];
+  const int b = MODE == kReqPass ? blockIdx.x / slices : blockIdx.x;
+  const int sl = MODE == kReqPass ? blockIdx.x % slices : 0;
+  const int V = a.V, nt = (V + kTile - 1) / kTile;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int d0, d1;
+  if (!request_range(a, b, d0, d1)) {
+    if (MODE != kReqPass && tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
     return;
+  }
+  const int g = d1 - d0;
+  const int64_t t0 = static_cast<int64_t>(d0) + b;
+  const int64_t o = static_cast<int64_t>(b) * nt;
+  exp2_table_init(tab);
+  int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &rs.first);  // (its barriers also publish tab)
+  const Exp2Consts C = exp2_consts_load();
+  for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
+    if (MODE == kReqFinish && guard == 0) {
+      for (int j = tid; j < nt; j += kPassNT) {
+        rbuf[j] = pa.E[o + j];
+        rbuf[nt + j] = pa.P[o + j];
+        rbuf[2 * nt + j] = pa.Q[o + j];
+      }
+    } else {
+      const int64_t trow = t0 + n;
+      const bool draft = n < g;
+      const double4 st = a.rstat[trow];
+      const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
+      const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
+      const float* __restrict__ qrow =
+          (HASQ && draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
+      if constexpr (MODE == kReqPass) {
+        const int per = (nt + slices - 1) / slices;
+        const int j0 = min(nt, sl * per), j1 = min(nt, j0 + per);
+        fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
+                                       kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
+        return;
+      } else {
+        fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, wave, nt,
+                                       kPassWaves, tab, C, rbuf, rbuf + nt, rbuf + 2 * nt, static_cast<float>(st.w));
+      }
+    }
+    if constexpr (MODE != kReqPass) {
+      __syncthreads();
+      if (!finish_row<LT, VEC, FILTER>(a, sel, b, d0, d1, n, rbuf, sc, rs, tab, C)) return;
+      n = first_open_row<kPassNT>(a.ws, t0, n + 1, g, &rs.first);
+    }
   }
 }
 
@@ -3591,18 +3614,48 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
   }
 }
 
-// The per-request stage of the lazy mode: the fp64 pass (kPassSlices blocks
-// per request), then one block per request decides it and writes the outputs.
+// The per-request stage of the lazy mode. Slices per request: the fewest
+// reaching the shortest estimated span (rounds of the chip's resident block
+// slots, request_blocks_per_cu per compute unit, times the tiles of one
+// block), at most one per two tiles. One slice: the fused kernel (pass and
+// finish in one block); more: the slice pass, then the finish.
+int request_slices(int B, int nt, int per_cu) {
+  const int64_t resident = static_cast<int64_t>(per_cu) * device_cus();
+  const int most = max(1, min(min(kMaxSlices, nt / 2), 0x7fffffff / max(B, 1)));
+  int best = 1;
+  double best_span = 0.0;
+  for (int sl = 1; sl <= most; ++sl) {
+    const int64_t rounds = (static_cast<int64_t>(B) * sl + resident - 1) / resident;
+    const double span = static_cast<double>(rounds) * static_cast<double>((nt + sl - 1) / sl);
+    if (sl == 1 || span < best_span * 0.999) {
+      best = sl;
+      best_span = span;
+    }
+  }
+  return best;
+}
+
+template <typename LT, bool VEC, bool FILTER, bool HASQ>
+void launch_request_modes(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2,
+                          hipStream_t st) {
+  const int nt = (a.V + kTile - 1) / kTile;
+  const int sl = request_slices(a.B, nt, request_blocks_per_cu<LT, VEC, HASQ>());
+  if (sl == 1) {
+    hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqFused>), dim3(static_cast<unsigned>(a.B)),
+                       dim3(kPassNT), lds2, st, a, sel, pa, 1);
+    return;
+  }
+  hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPass>),
+                     dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), 0, st, a, sel, pa,
+                     sl);
+  hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqFinish>), dim3(static_cast<unsigned>(a.B)),
+                     dim3(kPassNT), lds2, st, a, sel, pa, 1);
+}
+
 template <typename LT, bool VEC, bool FILTER>
 void launch_request(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2, hipStream_t st) {
-  if (!FILTER && a.q == nullptr)
-    hipLaunchKernelGGL((request_pass_kernel<LT, VEC, false, false>), dim3(static_cast<unsigned>(a.B) * kPassSlicesE),
-                       dim3(kPassNT), 0, st, a, pa);
-  else
-    hipLaunchKernelGGL((request_pass_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B) * kPassSlices),
-                       dim3(kPassNT), 0, st, a, pa);
-  hipLaunchKernelGGL((request_finish_kernel<LT, VEC, FILTER>), dim3(static_cast<unsigned>(a.B)), dim3(kFinishNT), lds2,
-                     st, a, sel, pa);
+  if (!FILTER && a.q == nullptr) launch_request_modes<LT, VEC, false, false>(a, sel, pa, lds2, st);
+  else launch_request_modes<LT, VEC, FILTER, true>(a, sel, pa, lds2, st);
 }
 
 // Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
