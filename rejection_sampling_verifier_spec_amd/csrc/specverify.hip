@@ -598,9 +598,10 @@ struct ProbsArgs {
 struct RowShared {
   int skip;        // lazy mode: an earlier position of the request is a certain rejection
   int last;        // lazy mode: this block is the last of the first launch to finish
-  int mark_old;    // lazy mode: the mark before this row's rejection raised it
+  int mark_old;    // lazy mode: the values this block's mark atomics returned (stored to wait for them)
   int wcount[16];  // lazy mode: per-wave counts of the survivor list
   float wmax[16];  // per-wave maxima (blocks of up to 1024 threads)
+  float wref[16];  // per-wave final references of pass 1 (the row max is their maximum)
   float m;
   double z;        // Z (e-units)
   double px;
@@ -2227,10 +2228,13 @@ __device__ void row_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
   dZt = dZ;
 }
 
+// Returns (thread 0 of a lazy-mode block) the value its mark raise returned,
+// or 0: the caller consumes it later, so that the atomic's round trip
+// overlaps the rest of the row's work.
 template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
-__device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
-                                          RowShared& sh,
-                                          std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr) {
+__device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
+                                         RowShared& sh,
+                                         std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr) {
   static_assert(!(EAGER && FILTER), "top-k / top-p run in the lazy mode only");
   constexpr int kWaves = NT / 64;
   using L = Lay<LT, VEC>;
@@ -2375,6 +2379,10 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
         if (j >= nt) break;
       }
     }
+    // the wave's final reference is the largest M_j of its tiles (every raise
+    // sets it to the raising tile's M_j); a wave without tiles holds the block
+    // maximum of the first tiles
+    if (lane == 0) sh.wref[wave] = ref;
     if constexpr (FILTER) {
       hcnt2 = wave_sum_i(hcnt2);
       if (lane == 0) {
@@ -2392,9 +2400,9 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   // Row max m, c_m = fl(-m s) and Z = sum_j S_j exp2(c_m - c_j) in e-units.
   // The c_j cancel exactly, so Z approximates 2^D sum_k 2^((l_k - m) s) with
   // D = c_m + m s (|D| <= u |m s|); D is carried into p(x) exactly.
-  float mloc = -INFINITY;
-  for (int j = tid; j < nt; j += NT) mloc = fmaxf(mloc, M[j]);
-  const float m = block_max(mloc, sc);
+  float m = -INFINITY;  // = max_j M_j
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sh.wref[w]);
   const float cm = -(m * s);
   double zl = 0.0, eal = 0.0;
   for (int j = tid; j < nt; j += NT) {
@@ -2462,17 +2470,18 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
   }
   __syncthreads();
   const bool accepted = sh.accepted != 0;
+  int mark_ret = 0;
   if constexpr (!EAGER) {
     // lazy mode: an accept test the bound cannot settle, every rejection and
     // every bonus row are left to the per-request pass, with the row max and
     // the certified Z interval in fp64 units (or {0, inf} when there is none)
     if (tid == 0) {
       const uint32_t f = sh.uncertain ? kRowUndecided : ((is_draft && accepted) ? kRowAccepted : kRowDeferred);
-      // a certain rejection raises the request's mark; the atomic returns (and the
-      // value is stored) before this thread goes on, so the mark is in place
-      // before anything this thread does later (the first launch's count)
+      // a certain rejection raises the request's mark; the returned value goes
+      // back to the caller, which stores it (waiting for the atomic) before
+      // the first launch's count
       if (is_draft && f == kRowDeferred)
-        sh.mark_old = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mark_ret = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (f != kRowAccepted) {
         double z = 0.0, dz = INFINITY;
         if (Z > 0.0 && Z < INFINITY && dZ < Z && m != -INFINITY) {
@@ -2484,19 +2493,20 @@ __device__ __forceinline__ void probs_row(const ProbsArgs& a, const Task& t, flo
       }
       a.ws[t.trow] = make_int2(-1, static_cast<int>(f | tier));
     }
-    return;
+    return mark_ret;
   }
   if (sh.uncertain) {
     if (tid == 0) flag_exact(a, t, static_cast<uint32_t>(sh.uncertain), m, false, Z, dZ);
-    return;
+    return 0;
   }
   const bool sample = !is_draft || !accepted || all_res;
   if (!sample) {
     if (tid == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowAccepted));
-    return;
+    return 0;
   }
 
   sample_row<LT, VEC, NT, EAGER>(a, t, lrow, qrow, xmask, accepted, m, Z, bt, relZ, sh.px, S, M, W, sc, sh);
+  return 0;
 }
 
 // Eager modes: one block per row (draft rows first, then bonus rows).
@@ -2590,10 +2600,12 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
   // a mark raised there before the clear is lost, which only leaves a row to
   // be read that could have been skipped. The second launch and the task
   // list read marks after the first launch has completed.
-  // (a returning exchange, its result stored: the clear has been performed
-  // before this thread goes on, hence before this block's count below)
+  // (a returning exchange whose result is stored before this block's count
+  // below: the clear has been performed before the count is issued; the
+  // result is consumed only then, so the round trip overlaps the row)
+  int mark_ret = 0;
   if (!second && t.valid && t.i == 0 && threadIdx.x == 0)
-    sh.mark_old = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mark_ret = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (second && t.valid && t.i > 0) {
     if (threadIdx.x == 0)
       sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
@@ -2603,12 +2615,13 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
       read = false;
     }
   }
-  if (read) probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
+  if (read) mark_ret ^= probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
   if (phase != 1) return;
+  if (threadIdx.x == 0) sh.mark_old = mark_ret;  // waits for this thread's mark atomics
   // first launch: the last block to finish lists the tasks of the second launch
   // reads. Marks and the count are device-scope atomics; every mark update
   // (the clear above, a raise in probs_row) is a returning atomic whose result
-  // the thread waits for, so it has been performed before that block's count
+  // thread 0 stores above (so it has been performed) before that block's count
   // is issued, and the last block reads the marks with device-scope atomic
   // loads after its own count has returned, behind an acquire fence. No
   // block needs a release fence (a cache write-back) of its own.
