@@ -227,6 +227,7 @@ def copy_ceiling(dev, mib=2048, reps=10):
 OTHER_CONFIGS = ("dense_f32", "ragged_bf16", "greedy_bf16", "onehot_bf16")
 
 NSETS = 4  # input sets resident in HBM, cycled through every timed loop
+PROFILE_EVERY = 4  # calls per call carrying the library's timing events
 
 
 def device_tensors(w, dev):
@@ -397,7 +398,7 @@ def measure_filtered(steps, sets, T, ws, stream, top_k=50, top_p=0.9):
     for i in range(3):
         call(sets[i % NSETS])
     torch.cuda.synchronize()
-    api.profile_start((api.SV_PROFILE_ROWS,), capacity=steps)
+    api.profile_start((api.SV_PROFILE_ROWS,), capacity=steps, every=PROFILE_EVERY)
     wall = time_calls(call, sets, steps)
     rows_ms, rows_n = api.profile_stop()[api.SV_PROFILE_ROWS]
     out, nacc, _ = call(sets[0])
@@ -490,17 +491,22 @@ def main():
     torch.cuda.synchronize()
     # timed region: exactly --steps calls, cycling through the input sets; the
     # library records timing-only events (no system fence) on the launch
-    # stream around the dominant kernel; the whole call is timed by the wall
-    # clock. A second event pair between the two stages would add a few
-    # microseconds of queue gap per call, so the per-request stage is timed in
-    # a loop of its own after the timed region.
-    api.profile_start((api.SV_PROFILE_ROWS,), capacity=args.steps)
+    # stream around the dominant stage (the per-row pass, both launches) on
+    # one call in PROFILE_EVERY: an event recorded between two kernels delays
+    # the next by a few microseconds, so recording every call would slow the
+    # region it measures. The whole call is timed by the wall clock. The first
+    # per-row launch alone and the per-request stage are timed the same way in
+    # a loop of their own after the timed region.
+    api.profile_start((api.SV_PROFILE_ROWS,), capacity=args.steps, every=PROFILE_EVERY)
     wall = time_calls(step, sets, args.steps)
     prof = api.profile_stop()
     ms_per_step = wall * 1e3
-    api.profile_start((api.SV_PROFILE_REQUEST,), capacity=args.steps)
+    api.profile_start((api.SV_PROFILE_REQUEST, api.SV_PROFILE_ROWS_FIRST), capacity=args.steps,
+                      every=PROFILE_EVERY)
     time_calls(step, sets, args.steps)
-    prof[api.SV_PROFILE_REQUEST] = api.profile_stop()[api.SV_PROFILE_REQUEST]
+    after = api.profile_stop()
+    prof[api.SV_PROFILE_REQUEST] = after[api.SV_PROFILE_REQUEST]
+    prof[api.SV_PROFILE_ROWS_FIRST] = after[api.SV_PROFILE_ROWS_FIRST]
     k = [0]
 
     def one():
@@ -513,6 +519,8 @@ def main():
     # bytes per call from each input set's row records (which rows the
     # per-row pass read and which were drawn from depends on the batch and,
     # for rows read speculatively, on timing)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    p1 = max(1, min(2 * cus // B, g + 1))
     per_set, rows_info = [], []
     for st in sets:
         out, nacc, _, _ = step(st)
@@ -525,6 +533,12 @@ def main():
         # q(x), uniform), and what it writes: an 8-byte record per row and the
         # 32-byte statistics of the rows it hands to the per-request stage
         cb["rows_kernel"] = cb["rows_read"] * V * esz + cb["drafts_read"] * 16 + rows * 8 + handed * 32
+        # the first per-row launch: every row at positions 0 .. p1 - 1 (p1 as the
+        # library takes it: as many positions as fill the chip's 2 blocks per CU once)
+        pos = np.arange(g + 1)[None, :].repeat(B, 0).reshape(-1)
+        first = pos < p1
+        cb["rows_first"] = int(np.count_nonzero(first)) * V * esz + int(np.count_nonzero(first & (pos < g))) * 16
+        cb["rows_second"] = int(np.count_nonzero(~first & ((flags & api.SV_ROW_UNREAD) == 0))) * V * esz
         # per-request stage: the deciding rows' logits (read again) and q rows
         cb["request_stage"] = cb["reread"] + (cb["residual"] * V * 4 if has_q else 0)
         per_set.append(cb)
@@ -538,8 +552,10 @@ def main():
     full_bytes = rows * V * esz + (0 if not has_q else positions * (V * 4 + 16))
     rows_ms, rows_n = prof[api.SV_PROFILE_ROWS]
     req_ms, req_n = prof[api.SV_PROFILE_REQUEST]
+    first_ms, first_n = prof[api.SV_PROFILE_ROWS_FIRST]
     rows_s = rows_ms / max(rows_n, 1) * 1e-3
     req_s = req_ms / max(req_n, 1) * 1e-3
+    first_s = first_ms / max(first_n, 1) * 1e-3
     achieved = b["rows_kernel"] / rows_s / 1e9 if rows_n else None
     traffic = measured_traffic()
     logits0, q0, x0, _, _ = sets[0]
@@ -565,9 +581,18 @@ def main():
                      "kernel": "lazy_rows_kernel (per-row pass, two launches per call)",
                      "bytes_per_launch": b["rows_kernel"],
                      "launch_ms_mean": rows_s * 1e3, "launches_timed": rows_n,
-                     "note": "HIP events recorded by the library on the launch stream around the per-row "
-                             "pass (both launches) in the timed region; bytes: the logit rows it read, 16 B per "
-                             "draft row read, its records and statistics (mean over the input sets)"},
+                     "first_launch": {"positions": p1, "ms_mean": first_s * 1e3 if first_n else None,
+                                      "bytes": b["rows_first"],
+                                      "achieved_GBps": b["rows_first"] / first_s / 1e9 if first_n else None},
+                     "second_launch": {"ms_mean": (rows_s - first_s) * 1e3 if first_n and rows_n else None,
+                                       "bytes": b["rows_second"],
+                                       "achieved_GBps": (b["rows_second"] / (rows_s - first_s) / 1e9
+                                                         if first_n and rows_n and rows_s > first_s else None)},
+                     "note": f"HIP events recorded by the library on the launch stream around the per-row "
+                             f"pass (both launches) on one call in {PROFILE_EVERY} of the timed region; bytes: the "
+                             f"logit rows it read, 16 B per draft row read, its records and statistics (mean over "
+                             f"the input sets). first_launch: events around the first launch alone in a loop after "
+                             f"the timed region; second_launch: the difference"},
         "request_stage": {"kernel": "request_kernel (per-request fp64 pass and finish, one launch)",
                           "bytes_per_launch": b["request_stage"],
                           "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,

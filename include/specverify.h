@@ -160,19 +160,27 @@ int spec_verify_stream_read(const void* src, size_t bytes, unsigned long long* w
  * HIP events that the library records on the launch stream right before and
  * right after each launch of a selected kernel.
  *   kernel_mask  bit SV_PROFILE_ROWS: the per-row pass (softmax statistics
- *                and accept test, every mode); bit SV_PROFILE_REQUEST: the
- *                per-request fp64 pass of the default (lazy) mode
+ *                and accept test, every mode; both launches of the default
+ *                mode); bit SV_PROFILE_REQUEST: the per-request stage of the
+ *                default (lazy) mode; bit SV_PROFILE_ROWS_FIRST: the first
+ *                per-row launch of the default mode alone
  *   capacity     launches recorded per kernel, 1 .. 2^20; later ones are not
  * spec_verify_profile_start drops any earlier recording, creates the events
  * and starts recording (SV_ERR_INVALID_ARGUMENT for a bad mask or capacity,
  * SV_ERR_LAUNCH if events cannot be created). spec_verify_profile_stop waits
- * for the recorded events, writes per kernel id (arrays of 2) the summed
+ * for the recorded events, writes per kernel id (arrays of 3) the summed
  * duration in milliseconds and the number of launches recorded, releases the
  * events and stops recording (either pointer may be NULL). Library-wide host
- * state: not for concurrent callers. */
+ * state: not for concurrent callers.
+ * spec_verify_profile_every (after start) records only every `every`-th call
+ * (the first, then each `every` calls later), so that a timed loop carries
+ * few events: an event recorded between two kernels delays the second by
+ * a few microseconds. SV_ERR_INVALID_ARGUMENT for every < 1. */
 #define SV_PROFILE_ROWS 0
 #define SV_PROFILE_REQUEST 1
+#define SV_PROFILE_ROWS_FIRST 2
 int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity);
+int spec_verify_profile_every(int32_t every);
 int spec_verify_profile_stop(double* total_ms, int32_t* launches);
 
 /*

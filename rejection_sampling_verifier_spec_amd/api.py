@@ -15,7 +15,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+# SPECVERIFY_LIB: another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify.so")
 
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
@@ -34,12 +35,13 @@ SV_ROW_ROW_SELECT = 0x4000
 SV_ROW_WHY = {0x10: "accept", 0x20: "fallback", 0x40: "search", 0x80: "margin", 0x100: "forced"}
 SV_PROFILE_ROWS = 0
 SV_PROFILE_REQUEST = 1
+SV_PROFILE_ROWS_FIRST = 2
 
 EXPORTS = ("spec_verify_workspace_size", "spec_verify_status_string", "spec_verify_version",
            "spec_verify_probs", "spec_verify_greedy", "spec_verify_ragged", "spec_verify_selftest_exp2",
            "spec_verify_exp2_error_bound", "spec_verify_profile_start", "spec_verify_profile_stop",
            "spec_verify_probs_filtered", "spec_verify_ragged_filtered", "spec_verify_stream_read",
-           "spec_verify_probs_noalloc")
+           "spec_verify_probs_noalloc", "spec_verify_profile_every")
 SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
@@ -76,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_exp2_error_bound.restype = ctypes.c_double
     lib.spec_verify_profile_start.argtypes = [u32, i32]
     lib.spec_verify_profile_start.restype = ctypes.c_int
+    lib.spec_verify_profile_every.argtypes = [i32]
+    lib.spec_verify_profile_every.restype = ctypes.c_int
     lib.spec_verify_profile_stop.argtypes = [vp, vp]
     lib.spec_verify_profile_stop.restype = ctypes.c_int
     lib.spec_verify_probs.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f64, u32, vp, vp, vp, vp, sz, vp]
@@ -380,24 +384,28 @@ def stream_read(buf, out=None, stream=None):
     return out
 
 
-def profile_start(kernels=(SV_PROFILE_ROWS, SV_PROFILE_REQUEST), capacity=1024):
-    """Start recording HIP events around the given kernels (see the header)."""
+def profile_start(kernels=(SV_PROFILE_ROWS, SV_PROFILE_REQUEST), capacity=1024, every=1):
+    """Start recording HIP events around the given kernels (see the header),
+    on one call in `every`."""
     mask = 0
     for k in kernels:
         mask |= 1 << int(k)
     rc = load().spec_verify_profile_start(mask, int(capacity))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_profile_start")
+    rc = load().spec_verify_profile_every(int(every))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_profile_every")
 
 
 def profile_stop():
     """Stop recording; returns {kernel id: (summed ms, launches)}."""
-    total = (ctypes.c_double * 2)()
-    count = (ctypes.c_int32 * 2)()
+    total = (ctypes.c_double * 3)()
+    count = (ctypes.c_int32 * 3)()
     rc = load().spec_verify_profile_stop(ctypes.cast(total, ctypes.c_void_p), ctypes.cast(count, ctypes.c_void_p))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_profile_stop")
-    return {SV_PROFILE_ROWS: (float(total[0]), int(count[0])), SV_PROFILE_REQUEST: (float(total[1]), int(count[1]))}
+    return {k: (float(total[k]), int(count[k])) for k in (SV_PROFILE_ROWS, SV_PROFILE_REQUEST, SV_PROFILE_ROWS_FIRST)}
 
 
 RECORDS_OFFSET = 256  # the records follow a 256-byte block of counters

@@ -18,16 +18,27 @@ HIPCC_FLAGS = [
 ]
 
 
-def build_library(verbose: bool = False) -> str:
+# host code only: AddressSanitizer and UndefinedBehaviorSanitizer on the host
+# layer (argument checks, workspace layout, launch set-up); the device code is
+# built as usual
+SANITIZE_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-omit-frame-pointer -g".split()
+
+
+def build_library(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I" + INCLUDE, SRC, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-I" + INCLUDE, SRC, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
+    import sys
+
+    if "--sanitize" in sys.argv:
+        print(build_library(verbose=True, out=sys.argv[sys.argv.index("--sanitize") + 1], sanitize=True))
+    else:
+        print(build_library(verbose=True))

@@ -3610,6 +3610,28 @@ int lazy_first_positions(int B, int pm) {
 }
 constexpr int kRowsNTEager = 512;
 
+// Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
+// recorded on the launch stream around the selected kernels. Host state.
+constexpr int kProfileIds = 3;  // SV_PROFILE_ROWS, SV_PROFILE_REQUEST, SV_PROFILE_ROWS_FIRST
+struct Profiler {
+  uint32_t mask = 0;
+  int capacity = 0;
+  int every = 1;                           // record one call in `every`
+  hipEvent_t* ev[kProfileIds] = {};       // per kernel id: [capacity][2] start, stop
+  int used[kProfileIds] = {};
+  int calls[kProfileIds] = {};            // calls seen since the start
+  bool on[kProfileIds] = {};              // the current call is recorded
+};
+Profiler g_prof;
+
+void prof_record(int id, int which, hipStream_t st) {
+  if (!(g_prof.mask & (1u << id))) return;
+  if (which == 0) g_prof.on[id] = (g_prof.calls[id]++ % g_prof.every) == 0 && g_prof.used[id] < g_prof.capacity;
+  if (!g_prof.on[id]) return;
+  (void)hipEventRecord(g_prof.ev[id][2 * g_prof.used[id] + which], st);
+  if (which == 1) ++g_prof.used[id];
+}
+
 template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
 void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
   if constexpr (EAGER) {
@@ -3619,8 +3641,10 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
     // every later row (every draft row of a ragged batch but one per request)
     const int split = lazy_first_positions(a.B, a.pm);
     const int64_t rest = a.cu ? static_cast<int64_t>(a.ndraft) : static_cast<int64_t>(a.B) * (a.pm - split);
+    prof_record(SV_PROFILE_ROWS_FIRST, 0, st);
     hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
                        lds, st, a, split, rest > 0 ? 1 : 0);
+    prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
     if (rest > 0)
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st,
                          a, split, 2);
@@ -3669,22 +3693,6 @@ template <typename LT, bool VEC, bool FILTER>
 void launch_request(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2, hipStream_t st) {
   if (!FILTER && a.q == nullptr) launch_request_modes<LT, VEC, false, false>(a, sel, pa, lds2, st);
   else launch_request_modes<LT, VEC, FILTER, true>(a, sel, pa, lds2, st);
-}
-
-// Benchmark diagnostics (spec_verify_profile_start / _stop): HIP event pairs
-// recorded on the launch stream around the selected kernels. Host state.
-struct Profiler {
-  uint32_t mask = 0;
-  int capacity = 0;
-  hipEvent_t* ev[2] = {nullptr, nullptr};  // per kernel id: [capacity][2] start, stop
-  int used[2] = {0, 0};
-};
-Profiler g_prof;
-
-void prof_record(int id, int which, hipStream_t st) {
-  if (!(g_prof.mask & (1u << id)) || g_prof.used[id] >= g_prof.capacity) return;
-  (void)hipEventRecord(g_prof.ev[id][2 * g_prof.used[id] + which], st);
-  if (which == 1) ++g_prof.used[id];
 }
 
 template <typename LT>
@@ -3903,11 +3911,9 @@ int spec_verify_version(void) { return 3; }
 double spec_verify_exp2_error_bound(void) { return kEpsExp; }
 
 int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity) {
-  if (capacity < 1 || capacity > (1 << 20) || (kernel_mask & ~3u) || !kernel_mask) return SV_ERR_INVALID_ARGUMENT;
-  double t[2];
-  int n[2];
-  spec_verify_profile_stop(t, n);  // drops any earlier recording
-  for (int id = 0; id < 2; ++id) {
+  if (capacity < 1 || capacity > (1 << 20) || (kernel_mask & ~7u) || !kernel_mask) return SV_ERR_INVALID_ARGUMENT;
+  spec_verify_profile_stop(nullptr, nullptr);  // drops any earlier recording
+  for (int id = 0; id < kProfileIds; ++id) {
     if (!(kernel_mask & (1u << id))) continue;
     g_prof.ev[id] = new hipEvent_t[2 * static_cast<size_t>(capacity)];
     for (int i = 0; i < 2 * capacity; ++i) {
@@ -3917,20 +3923,28 @@ int spec_verify_profile_start(uint32_t kernel_mask, int32_t capacity) {
         for (int k = 0; k < i; ++k) (void)hipEventDestroy(g_prof.ev[id][k]);
         delete[] g_prof.ev[id];
         g_prof.ev[id] = nullptr;
-        spec_verify_profile_stop(t, n);
+        spec_verify_profile_stop(nullptr, nullptr);
         return SV_ERR_LAUNCH;
       }
     }
   }
   g_prof.mask = kernel_mask;
   g_prof.capacity = capacity;
-  g_prof.used[0] = g_prof.used[1] = 0;
+  g_prof.every = 1;
+  for (int id = 0; id < kProfileIds; ++id) g_prof.used[id] = g_prof.calls[id] = 0;
+  return SV_OK;
+}
+
+int spec_verify_profile_every(int32_t every) {
+  if (every < 1) return SV_ERR_INVALID_ARGUMENT;
+  g_prof.every = every;
+  for (int id = 0; id < kProfileIds; ++id) g_prof.calls[id] = 0;
   return SV_OK;
 }
 
 int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
   int rc = SV_OK;
-  for (int id = 0; id < 2; ++id) {
+  for (int id = 0; id < kProfileIds; ++id) {
     double sum = 0.0;
     int used = 0;
     if (g_prof.ev[id]) {
@@ -3951,7 +3965,11 @@ int spec_verify_profile_stop(double* total_ms, int32_t* launches) {
   }
   g_prof.mask = 0;
   g_prof.capacity = 0;
-  g_prof.used[0] = g_prof.used[1] = 0;
+  g_prof.every = 1;
+  for (int id = 0; id < kProfileIds; ++id) {
+    g_prof.used[id] = g_prof.calls[id] = 0;
+    g_prof.on[id] = false;
+  }
   return rc;
 }
 

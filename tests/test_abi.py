@@ -173,14 +173,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 def test_profile_argument_validation(lib):
     # rejected before any HIP call: no kernel selected, unknown kernel bit, bad capacity
     assert lib.spec_verify_profile_start(0, 10) == -1
-    assert lib.spec_verify_profile_start(4, 10) == -1
+    assert lib.spec_verify_profile_start(8, 10) == -1
     assert lib.spec_verify_profile_start(1, 0) == -1
     assert lib.spec_verify_profile_start(1, (1 << 20) + 1) == -1
+    assert lib.spec_verify_profile_every(0) == -1
     # nothing recorded: stop reports zeros and touches no device state
-    total = (ctypes.c_double * 2)(7.0, 7.0)
-    count = (ctypes.c_int32 * 2)(7, 7)
+    total = (ctypes.c_double * 3)(7.0, 7.0, 7.0)
+    count = (ctypes.c_int32 * 3)(7, 7, 7)
     assert lib.spec_verify_profile_stop(ctypes.cast(total, ctypes.c_void_p), ctypes.cast(count, ctypes.c_void_p)) == 0
-    assert list(total) == [0.0, 0.0] and list(count) == [0, 0]
+    assert list(total) == [0.0, 0.0, 0.0] and list(count) == [0, 0, 0]
 
 
 def noalloc(lib, **kw):
