@@ -1702,25 +1702,29 @@ __device__ __forceinline__ void head_append_wave(const RawTile<LT, VEC>& r, int 
   }
 }
 
-// head_append_wave for pass 1, which also counts in `cnt2` (per lane) the
-// in-row elements at or above c2 < c; groups of 8 slots without an element
-// at or above c2 are skipped, and the appends run only in groups that hold
-// one at or above c.
+// head_append_wave for pass 1, which also counts in `cnt2` (the wave's
+// count: ballots counted on the scalar unit) the in-row elements at or above
+// c2 < c; groups of 8 slots (their per-lane maxima gm, from the tile's
+// maximum) without an element at or above c2 are skipped, and the appends
+// run only in groups that hold one at or above c.
 template <typename LT, bool VEC>
-__device__ __forceinline__ void head_append_count_wave(const RawTile<LT, VEC>& r, int base, int V, int lane, float c,
-                                                       float c2, uint32_t* dst, int slice, int& cnt, int& cnt2) {
+__device__ __forceinline__ void head_append_count_wave(const RawTile<LT, VEC>& r, const float (&gm)[kLaneElems / 8],
+                                                       int base, int V, int lane, float c, float c2, uint32_t* dst,
+                                                       int slice, int& cnt, int& cnt2) {
   using L = Lay<LT, VEC>;
-  const bool full = base + kTile <= V;
+  const bool full = base + kTile <= V;  // uniform
 #pragma unroll
   for (int g = 0; g < kLaneElems; g += 8) {
-    float gm = r.get(g);
+    if (!__any(gm[g / 8] >= c2)) continue;
+    if (full) {
 #pragma unroll
-    for (int k = g + 1; k < g + 8; ++k) gm = fmaxf(gm, r.get(k));
-    if (!__any(gm >= c2)) continue;
+      for (int k = g; k < g + 8; ++k) cnt2 += static_cast<int>(__popcll(__ballot(r.get(k) >= c2)));
+    } else {
 #pragma unroll
-    for (int k = g; k < g + 8; ++k)
-      cnt2 += ((full || L::index(base, lane, k) < V) && r.get(k) >= c2) ? 1 : 0;
-    if (!__any(gm >= c)) continue;
+      for (int k = g; k < g + 8; ++k)
+        cnt2 += static_cast<int>(__popcll(__ballot(L::index(base, lane, k) < V && r.get(k) >= c2)));
+    }
+    if (!__any(gm[g / 8] >= c)) continue;
 #pragma unroll
     for (int k = g; k < g + 8; ++k) {
       const float v = r.get(k);
@@ -2299,19 +2303,30 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
   float ref = -INFINITY;
   float cut1 = -INFINITY;  // top-k / top-p: pass 1 gathers the head {l >= cut1}
   int hcnt = 0;            // (into per-wave slices, hcnt elements offered by this wave)
-  float cut2 = -INFINITY;  // and counts per lane the elements >= cut2 (hcnt2)
+  float cut2 = -INFINITY;  // and counts per wave the elements >= cut2 (hcnt2)
   int hcnt2 = 0;
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
     // the tile's maximum first: a tile that raises the wave's reference is
     // summed once, against the raised one
     float lm = -INFINITY;
+    float gm[kLaneElems / 8];  // (top-k / top-p: the maxima of the lane's groups of 8 slots)
+    if constexpr (FILTER) {
 #pragma unroll
-    for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, r.get(k));
+      for (int g = 0; g < kLaneElems; g += 8) {
+        gm[g / 8] = r.get(g);
+#pragma unroll
+        for (int k = g + 1; k < g + 8; ++k) gm[g / 8] = fmaxf(gm[g / 8], r.get(k));
+        lm = fmaxf(lm, gm[g / 8]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, r.get(k));
+    }
     if (__any(lm > ref)) ref = fmaxf(ref, wave_max(lm));
     if constexpr (FILTER) {
       if (__any(lm >= cut2))
-        head_append_count_wave<LT, VEC>(r, base, V, lane, cut1, cut2, fsp->head + wave * (kHeadCap / kWaves),
+        head_append_count_wave<LT, VEC>(r, gm, base, V, lane, cut1, cut2, fsp->head + wave * (kHeadCap / kWaves),
                                         kHeadCap / kWaves, hcnt, hcnt2);
     }
     float es = 0.f, ea = 0.f;
@@ -2384,7 +2399,6 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     // maximum of the first tiles
     if (lane == 0) sh.wref[wave] = ref;
     if constexpr (FILTER) {
-      hcnt2 = wave_sum_i(hcnt2);
       if (lane == 0) {
         fsp->wcnt[wave] = hcnt;
         fsp->wcnt2[wave] = hcnt2;
