@@ -593,7 +593,8 @@ def main():
                              f"logit rows it read, 16 B per draft row read, its records and statistics (mean over "
                              f"the input sets). first_launch: events around the first launch alone in a loop after "
                              f"the timed region; second_launch: the difference"},
-        "request_stage": {"kernel": "request_kernel (per-request fp64 pass and finish, one launch)",
+        "request_stage": {"kernel": "request_kernel (per-request fp64 slice pass, then the finish; both in one "
+                                    "launch when one slice per request fills the chip)",
                           "bytes_per_launch": b["request_stage"],
                           "launch_ms_mean": req_s * 1e3 if req_n else None, "launches_timed": req_n,
                           "achieved_GBps": b["request_stage"] / req_s / 1e9 if req_n else None},
