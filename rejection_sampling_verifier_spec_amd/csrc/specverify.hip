@@ -2705,12 +2705,20 @@ __device__ __forceinline__ void exp2_table_init(double* tab) {
 // can take only one scalar operand, so two uniform constants in one fma would
 // otherwise be copied into VGPRs at every use; as compile-time constants the
 // compiler keeps or rematerialises them without holding VGPRs.
+// The two fmas whose other constant operand is already scalar take theirs
+// from a vector register held for the whole pass (scale_v, c4_v: the asm
+// keeps the compiler from folding them back into constants), so no constant
+// is copied at each use.
 struct Exp2Consts {
   double rnd, scale, inv_scale, lo, c1, c2, c3, c4;
+  double scale_v, c4_v;
 };
 __device__ __forceinline__ Exp2Consts exp2_consts_load() {
-  return Exp2Consts{6755399441055744.0, kExp2Scale, kExp2InvScale, -1100.0, 0.6931471805599453, 0.2402265069591007,
-                    0.05550410866482158, 0.009618129107628477};
+  Exp2Consts c{6755399441055744.0, kExp2Scale, kExp2InvScale, -1100.0, 0.6931471805599453, 0.2402265069591007,
+               0.05550410866482158, 0.009618129107628477, kExp2Scale, 0.009618129107628477};
+  asm volatile("" : "+v"(c.scale_v));
+  asm volatile("" : "+v"(c.c4_v));
+  return c;
 }
 
 // exp2_neg of N arguments at once, in phases (all table reads, then all
@@ -2725,14 +2733,14 @@ __device__ __forceinline__ void exp2_negN(const double (&a)[N], const double* __
 #pragma unroll
   for (int k = 0; k < N; ++k) {
     const double ak = fmax(a[k], C.lo);
-    const double t = fma(ak, C.scale, kRnd);
+    const double t = fma(ak, C.scale_v, kRnd);
     r[k] = fma(t - kRnd, C.inv_scale, ak);
     J[k] = __double2loint(t);
     tv[k] = tab[J[k] & (kExp2Tab - 1)];
   }
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    double p = fma(c4, r[k], c3);
+    double p = fma(C.c4_v, r[k], c3);
     p = fma(p, r[k], c2);
     p = fma(p, r[k], c1);
     p = fma(p, r[k], 1.0);
