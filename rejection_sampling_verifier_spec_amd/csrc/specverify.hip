@@ -468,32 +468,14 @@ struct Task {
 __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__ cu, int B, int gamma,
                                             int ndraft);
 
-// Lazy mode. First launch (tasks == nullptr): block blk takes position
-// blk / B of request b = blk % B (all first drafts, then all second drafts,
-// ...). Second launch: block blk takes task blk of the list the first launch
-// wrote ({request, position}, request by request), if there is one.
-__device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restrict__ cu, int B, int gamma,
-                                                 int ndraft, const int2* __restrict__ tasks, int ntasks) {
+// Lazy mode: the row of position i of request b (invalid when the request's
+// offsets are, or when i is past its bonus row).
+__device__ __forceinline__ Task lazy_task(int b, int i, const int32_t* __restrict__ cu, int B, int gamma,
+                                          int ndraft) {
   Task t;
   t.valid = true;
-  if (tasks) {
-    if (blk >= ntasks) {
-      t.valid = false;
-      return t;
-    }
-    const int2 tk = tasks[blk];
-    t.b = tk.x;
-    t.i = tk.y;
-    // entries come from the first launch; any other value (a workspace that
-    // was not zero-filled, a list left by an interrupted call) is no task
-    if (static_cast<unsigned>(t.b) >= static_cast<unsigned>(B) || t.i < 0) {
-      t.valid = false;
-      return t;
-    }
-  } else {
-    t.b = blk % B;
-    t.i = blk / B;
-  }
+  t.b = b;
+  t.i = i;
   int d0, d1;
   if (cu) {
     d0 = cu[t.b];
@@ -512,6 +494,25 @@ __device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restr
   t.trow = static_cast<int64_t>(d0) + t.i + t.b;
   t.srow = static_cast<int64_t>(d1) + t.b;
   return t;
+}
+
+// Lazy mode. First launch (tasks == nullptr): block blk takes position
+// blk / B of request b = blk % B (all first drafts, then all second drafts,
+// ...). Second launch: block blk takes task blk of the list the first launch
+// wrote ({request, position}, request by request), if there is one.
+__device__ __forceinline__ Task decode_task_lazy(int blk, const int32_t* __restrict__ cu, int B, int gamma,
+                                                 int ndraft, const int2* __restrict__ tasks, int ntasks) {
+  if (tasks) {
+    Task t;
+    t.valid = false;
+    if (blk >= ntasks) return t;
+    const int2 tk = tasks[blk];
+    // entries come from the first launch; any other value (a workspace that
+    // was not zero-filled, a list left by an interrupted call) is no task
+    if (static_cast<unsigned>(tk.x) >= static_cast<unsigned>(B) || tk.y < 0) return t;
+    return lazy_task(tk.x, tk.y, cu, B, gamma, ndraft);
+  }
+  return lazy_task(blk % B, blk / B, cu, B, gamma, ndraft);
 }
 
 __device__ __forceinline__ Task decode_task(int blk, const int32_t* __restrict__ cu, int B, int gamma,
@@ -599,6 +600,7 @@ struct RowShared {
   int skip;        // lazy mode: an earlier position of the request is a certain rejection
   int last;        // lazy mode: this block is the last of the first launch to finish
   int mark_old;    // lazy mode: the values this block's mark atomics returned (stored to wait for them)
+  int2 qtask;      // lazy mode, self-listed second launch: this block's {request, position}, or {-1, 0}
   int wcount[16];  // lazy mode: per-wave counts of the survivor list
   float wmax[16];  // per-wave maxima (blocks of up to 1024 threads)
   float wref[16];  // per-wave final references of pass 1 (the row max is their maximum)
@@ -2594,19 +2596,87 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
   if (threadIdx.x == 0) a.surv_n[0] = base;
 }
 
+// The second launch without a list (see kSelfListMaxReads): every block derives the same list from the marks the first
+// launch left (its survivors, request by request, in request order) and takes
+// entry blockIdx.x, so the first launch ends with its last row instead of
+// counting its blocks and listing serially. The later rows of every request
+// that did not survive are recorded unread by the block that owns the
+// request (b mod the grid). Raises made in this launch (positions >= p1)
+// never change a request's survival, so any value a block reads agrees.
+template <int NT>
+__device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kW = NT / 64;
+  const int k = blockIdx.x;
+  if (threadIdx.x == 0) sh.qtask = make_int2(-1, 0);
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += NT) {
+    const int b = b0 + static_cast<int>(threadIdx.x);
+    int cnt = 0;
+    int d0 = 0;
+    if (b < a.B) {
+      int d1;
+      if (a.cu) {
+        d0 = a.cu[b];
+        d1 = a.cu[b + 1];
+      } else {
+        d0 = b * a.gamma;
+        d1 = d0 + a.gamma;
+      }
+      const bool ok = !a.cu || (d0 >= 0 && d1 >= d0 && d1 <= a.ndraft);
+      const int g = d1 - d0;
+      const bool keep = ok && g >= p1 &&
+                        __hip_atomic_load(a.mark + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= kMarkBase - p1;
+      if (keep) {
+        cnt = g + 1 - p1;
+      } else if (ok && b % static_cast<int>(gridDim.x) == k) {
+        for (int i = p1; i <= g; ++i)
+          a.ws[static_cast<int64_t>(d0) + b + i] = make_int2(-1, static_cast<int>(kRowUnread));
+      }
+    }
+    // offsets: exclusive scan of the counts over the block (lanes, then waves)
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) sh.wcount[wave] = incl;
+    __syncthreads();
+    int off = base + incl - cnt;
+    for (int w = 0; w < wave; ++w) off += sh.wcount[w];
+    if (cnt > 0 && k >= off && k < off + cnt) sh.qtask = make_int2(b, p1 + (k - off));
+    for (int w = 0; w < kW; ++w) base += sh.wcount[w];
+    __syncthreads();
+  }
+  const int2 e = sh.qtask;
+  if (e.x < 0) {
+    Task t;
+    t.valid = false;
+    return t;
+  }
+  return lazy_task(e.x, e.y, a.cu, a.B, a.gamma, a.ndraft);
+}
+
 // (FILTER: at least four waves per SIMD, two blocks per CU as without it;
 // the rare radix-select path of the threshold may then spill)
 template <typename LT, bool VEC, int NT, bool FILTER>
 __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
   // phase 0: first launch, alone; 1: first launch, a second follows (its last
-  // block lists the tasks); 2: second launch
+  // block lists the tasks); 2: second launch, from that list; 3: first
+  // launch, a second follows that lists for itself; 4: that second launch
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
   __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
-  const bool second = phase == 2;
-  const Task t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, second ? a.tasks : nullptr,
-                                  second ? a.surv_n[0] : 0);
+  const bool second = phase == 2 || phase == 4;
+  Task t;
+  if constexpr (!FILTER) {
+    if (phase == 4) t = self_listed_task<NT>(a, p1, sh);
+  }
+  if (FILTER || phase != 4)
+    t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, phase == 2 ? a.tasks : nullptr,
+                         phase == 2 ? a.surv_n[0] : 0);
   bool read = t.valid;
   // The request's mark starts at zero in every call: its position-0 block (in
   // the first launch) clears it before anything else. Blocks of the first
@@ -3604,6 +3674,13 @@ size_t ws_bytes(int64_t rows) { return 256 + align256(static_cast<size_t>(rows) 
 constexpr int kRowsNTLazy = 512;
 constexpr int kRaggedFirstMax = 4;  // ragged batches: most positions in the first lazy launch
 constexpr int kLazyBlocksPerCU = 2;      // lazy per-row kernel: 512-thread blocks resident per CU
+// Most mark reads (requests x blocks of the second launch) for which every
+// block of the second lazy launch derives the task list itself: each block,
+// the empty ones too, reads every request's mark, so beyond this the first
+// launch's last block lists the tasks instead (measured: the headline batch,
+// 256 x 1280, and the ragged one, 512 x 2307, gain about 1%; one-hot drafts
+// at B = 1024, 1024 x 4096, lose 6%)
+constexpr int64_t kSelfListMaxReads = int64_t{1} << 21;
 
 // Compute units of the current device (cached per device; 256 if the query
 // fails). Callers on several host threads may fill an entry at the same time:
@@ -3663,13 +3740,16 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
     // every later row (every draft row of a ragged batch but one per request)
     const int split = lazy_first_positions(a.B, a.pm);
     const int64_t rest = a.cu ? static_cast<int64_t>(a.ndraft) : static_cast<int64_t>(a.B) * (a.pm - split);
+    // the second launch lists for itself when every block's pass over the
+    // marks stays cheap (without top-k / top-p)
+    const bool self = !FILTER && static_cast<int64_t>(a.B) * rest <= kSelfListMaxReads;
     prof_record(SV_PROFILE_ROWS_FIRST, 0, st);
     hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
-                       lds, st, a, split, rest > 0 ? 1 : 0);
+                       lds, st, a, split, rest > 0 ? (self ? 3 : 1) : 0);
     prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
     if (rest > 0)
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st,
-                         a, split, 2);
+                         a, split, self ? 4 : 2);
   }
 }
 

@@ -207,6 +207,25 @@ def test_both_lazy_launches_all_requests(B):
     gh.compare(w, gh.run_gpu_filtered(w, 20, 0.9), label=f"B={B} filtered", filt=(20, 0.9))
 
 
+def test_second_launch_listed_both_ways():
+    """The second per-row launch takes its tasks from a list the first
+    launch's last block writes, or (when requests x second-launch blocks is
+    at most 2^21) lists them itself in every block. B = 1100 with four
+    positions per request (p1 = 1: 1100 x 3300 reads) takes the first way,
+    its first 200 requests (p1 = 2: 200 x 400) the second; q rows, one-hot
+    drafts and the ragged layout, every request compared with the oracle."""
+    gh = _gh()
+    w = make_dense_custom(77, B=1100, gamma=3, V=1024, dtype="bf16", temperature=1.0, q_sigma=0.3)
+    assert 1100 * (1100 * 3) > (1 << 21)
+    for name, ww in (("B=1100", w), ("B=200", make_dense_custom(77, B=200, gamma=3, V=1024, dtype="bf16",
+                                                                  temperature=1.0, q_sigma=0.3))):
+        gh.compare(ww, gh.run_gpu(ww), label=f"{name} q rows")
+        wo = dict(ww, draft_probs=None)
+        gh.compare(wo, gh.run_gpu(wo), label=f"{name} one-hot")
+        wr = dense_as_ragged(ww)
+        gh.compare(wr, gh.run_gpu(wr), label=f"{name} ragged")
+
+
 def test_ragged_long_requests_over_both_launches():
     """A ragged batch of 300 requests with 0 to 24 drafts each and drafts
     close to the target (most accepted), so that the second per-row launch
