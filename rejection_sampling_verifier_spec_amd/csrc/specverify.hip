@@ -2883,6 +2883,7 @@ struct RawChunk<uint16_t, true> {
   uint4 l;
   float4 q0, q1;
   int i0;
+  __device__ __forceinline__ uint32_t word(int i) const { return i == 0 ? l.x : i == 1 ? l.y : i == 2 ? l.z : l.w; }
   __device__ __forceinline__ void load(const uint16_t* __restrict__ lrow, const float* __restrict__ qrow, int V,
                                        int base, int lane, int c, bool has_q) {
     i0 = Lay<uint16_t, true>::index(base, lane, 8 * c);
@@ -3024,9 +3025,35 @@ __device__ __forceinline__ void load8qf(const float* __restrict__ q, int V, int 
 // whether tile j of a row of V elements reaches past its end
 __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j == nt - 1 && j * kTile + kTile > V; }
 
-struct ReqShared {
+constexpr int kPassNT = 256;       // threads per block of the per-request kernel
+constexpr int kPassWaves = kPassNT / 64;
+
+// Memo of the fp64 pass for bf16 logits: e(l) = 2^((l - m) s) of one row for
+// every bf16 value l with 2^-10 <= |l| < 2^6 (16 binades of 128 codes, both
+// signs: 4096 entries, 32 KB of LDS), each computed by the same fma and
+// exp2_neg as the direct path, so a looked-up e equals the computed one bit
+// for bit. Entry of code c: (c & 0x7fff) - kMemoLo, plus kMemoHalf when the
+// sign bit is set. A bf16 row holds at most 65536 distinct values and the
+// bulk of a logit row lies in these binades, so a block builds the table once
+// per row (4096 exp2) and then reads one entry per element instead of
+// evaluating the exp2; groups holding a value outside the range (tiny or large
+// magnitudes, inf, NaN) take the direct path.
+constexpr int kMemoHalf = 16 * 128;
+constexpr int kMemoN = 2 * kMemoHalf;
+constexpr uint32_t kMemoLo = (127u - 10u) << 7;  // bf16 magnitude code of 2^-10
+template <typename LT, bool VEC>
+constexpr bool kMemo = VEC && std::is_same_v<LT, uint16_t>;
+
+// The memo and the finish's crossing-tile weights are never live together
+// (the pass ends at a barrier before the finish, and every pass rebuilds the
+// memo), so they share the LDS.
+template <bool MEMO>
+struct ReqSharedT {
   double part[4];  // per-wave partial sums (an undecided tile)
-  double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see finish_row)
+  union {
+    double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see finish_row)
+    double memo[MEMO ? kMemoN : kTile];
+  };
   int first;    // first row not yet accepted
   int nund;     // tiles with undecided elements
   int cross, lastpos;
@@ -3035,6 +3062,41 @@ struct ReqShared {
   int token;
   int pad;
 };
+
+// Memo entries of the two bf16 values packed in w (low half first), as two
+// 16-bit fields; the 16-bit offsets from kMemoLo are or-ed into `miss`, where
+// any bit of 0xf800 in a half marks a value outside the memo (its entry is
+// then some other in-range one, replaced by the direct path).
+__device__ __forceinline__ uint32_t memo_index2(uint32_t w, uint32_t& miss) {
+  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  const u16x2 lo = {static_cast<unsigned short>(kMemoLo), static_cast<unsigned short>(kMemoLo)};
+  const uint32_t off = __builtin_bit_cast(uint32_t, mag - lo);
+  miss |= off;
+  return (off & 0x07ff07ffu) | ((w >> 4) & 0x08000800u);  // sign bit 15 -> entry bit 11
+}
+
+// Build the memo of one row (every thread of the block takes part; the caller
+// waits at a barrier before reading it). With MASK, values below tau are 0.
+template <bool MASK>
+__device__ __forceinline__ void memo_build(double* memo, double s, double nms, float tau,
+                                           const double* __restrict__ tab, const Exp2Consts& C) {
+  static_assert(kMemoN % (kExpW * kPassNT) == 0, "whole rounds of the block");
+  for (int i0 = threadIdx.x; i0 < kMemoN; i0 += kExpW * kPassNT) {
+    double ar[kExpW], e[kExpW];
+#pragma unroll
+    for (int k = 0; k < kExpW; ++k) {
+      const uint32_t i = static_cast<uint32_t>(i0 + k * kPassNT);
+      const uint32_t code = ((i / kMemoHalf) << 15) | (kMemoLo + i % kMemoHalf);
+      float l = __uint_as_float(code << 16);
+      if constexpr (MASK) l = l < tau ? -INFINITY : l;
+      ar[k] = fma(static_cast<double>(l), s, nms);
+    }
+    exp2_negN<kExpW>(ar, tab, C, e);
+#pragma unroll
+    for (int k = 0; k < kExpW; ++k) memo[i0 + k * kPassNT] = e[k];
+  }
+}
 
 // The fp64 pass of one row over tiles j = j0, j0 + step, ... < j1, one tile
 // per wave at a time, in four chunks of 8 elements per lane; a ring of four
@@ -3047,7 +3109,8 @@ template <typename LT, bool VEC, bool MASK>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
                               const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
-                              float tau) {
+                              float tau, double* memo) {
+  constexpr bool MEMO = kMemo<LT, VEC>;
   const int lane = threadIdx.x & 63;
   const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
   using Chunk = RawChunk<LT, VEC>;
@@ -3063,13 +3126,32 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
 #pragma unroll
     for (int h = 0; h < 8; h += kExpW) {
       double ar[kExpW], e[kExpW];
+      auto direct = [&]() {
 #pragma unroll
-      for (int k = 0; k < kExpW; ++k) {
-        float l = ring[slot].template get_l<PD>(h + k, V);
-        if constexpr (MASK) l = l < tau ? -INFINITY : l;
-        ar[k] = fma(static_cast<double>(l), s, nms);
+        for (int k = 0; k < kExpW; ++k) {
+          float l = ring[slot].template get_l<PD>(h + k, V);
+          if constexpr (MASK) l = l < tau ? -INFINITY : l;
+          ar[k] = fma(static_cast<double>(l), s, nms);
+        }
+        exp2_negN<kExpW>(ar, tab, C, e);
+      };
+      if constexpr (MEMO) {
+        if constexpr (!PD) {
+          static_assert(kExpW == 4, "the memo lookup takes two words of two bf16 values");
+          uint32_t miss = 0;
+          const uint32_t i01 = memo_index2(ring[slot].word(h >> 1), miss);
+          const uint32_t i23 = memo_index2(ring[slot].word((h >> 1) + 1), miss);
+          e[0] = memo[i01 & 0xffffu];
+          e[1] = memo[i01 >> 16];
+          e[2] = memo[i23 & 0xffffu];
+          e[3] = memo[i23 >> 16];
+          if (__builtin_amdgcn_ballot_w64((miss & 0xf800f800u) != 0u)) direct();  // rare; same values elsewhere
+        } else {
+          direct();
+        }
+      } else {
+        direct();
       }
-      exp2_negN<kExpW>(ar, tab, C, e);
 #pragma unroll
       for (int k = 0; k < kExpW; ++k) es += e[k];
       if (draft) {  // uniform; the element's side by a 0/1 factor
@@ -3102,10 +3184,23 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     und = 0;
   };
   int j = j0;
-  if (j >= j1) return;
-  load(0, j, 0);
-  load(1, j, 1);
-  load(2, j, 2);
+  if constexpr (MEMO) {
+    // the first loads go out before the memo is built (every thread of the
+    // block builds it and waits at the barrier, with or without tiles)
+    if (j < j1) {
+      load(0, j, 0);
+      load(1, j, 1);
+      load(2, j, 2);
+    }
+    memo_build<MASK>(memo, s, nms, tau, tab, C);
+    __syncthreads();
+    if (j >= j1) return;
+  } else {
+    if (j >= j1) return;
+    load(0, j, 0);
+    load(1, j, 1);
+    load(2, j, 2);
+  }
   for (; j < j1; j += step) {
     const int jn = j + step < j1 ? j + step : j;
     if (base_partial(j, nt, V)) {
@@ -3148,8 +3243,6 @@ __device__ __forceinline__ bool request_range(const ProbsArgs& a, int b, int& d0
   return true;
 }
 
-constexpr int kPassNT = 256;       // threads per block of the per-request kernel
-constexpr int kPassWaves = kPassNT / 64;
 constexpr int kMaxSlices = 16;     // most blocks per request
 static_assert(kPassWaves == 4, "the finish's in-tile search maps 16 scan lanes to each of four waves");
 
@@ -3178,7 +3271,8 @@ struct PassArrays {  // per request: [B][nt] tile sums of its deciding row (the 
 // request's outputs, and the function returns false.
 template <typename LT, bool VEC, bool FILTER>
 __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int d0, int d1, int n, double* rbuf,
-                           BlockScratchT<kPassNT>& sc, ReqShared& rs, const double* __restrict__ tab,
+                           BlockScratchT<kPassNT>& sc, ReqSharedT<kMemo<LT, VEC>>& rs,
+                           const double* __restrict__ tab,
                            const Exp2Consts& C) {
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
@@ -3433,7 +3527,7 @@ __global__ __launch_bounds__(kPassNT, (MODE == kReqFinish ? 1 : request_blocks_p
 request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
   extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
   __shared__ BlockScratchT<kPassNT> sc;
-  __shared__ ReqShared rs;
+  __shared__ ReqSharedT<kMemo<LT, VEC>> rs;
   __shared__ double tab[kExp2Tab];
   const int b = MODE == kReqPass ? blockIdx.x / slices : blockIdx.x;
   const int sl = MODE == kReqPass ? blockIdx.x % slices : 0;
@@ -3469,11 +3563,13 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
         const int per = (nt + slices - 1) / slices;
         const int j0 = min(nt, sl * per), j1 = min(nt, j0 + per);
         fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
-                                       kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w));
+                                       kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w),
+                                       rs.memo);
         return;
       } else {
         fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, wave, nt,
-                                       kPassWaves, tab, C, rbuf, rbuf + nt, rbuf + 2 * nt, static_cast<float>(st.w));
+                                       kPassWaves, tab, C, rbuf, rbuf + nt, rbuf + 2 * nt, static_cast<float>(st.w),
+                                       rs.memo);
       }
     }
     if constexpr (MODE != kReqPass) {

@@ -626,6 +626,40 @@ def test_negative_infinity_padding(dtype):
     gh.compare(w, gh.run_gpu_filtered(w, 30, 0.9), label=f"-inf padding {dtype} filtered", filt=(30, 0.9))
 
 
+def test_bf16_values_outside_the_common_binades():
+    """bf16 rows whose values fall outside 2^-10 <= |l| < 2^6 (the binades the
+    fp64 pass keeps per-row values of): exact zeros, tiny magnitudes, large
+    ones up to 2^8, -inf, rows made only of such values, and rows where they
+    are scattered among ordinary ones; with q rows, one-hot drafts and
+    top-k / top-p, all compared with the oracle."""
+    from rejection_sampling_verifier_spec_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    gh = _gh()
+    w = make_dense_custom(43, B=16, gamma=3, V=5000, dtype="bf16", temperature=1.0)
+    rng = np.random.default_rng(44)
+    l = w["logits"]
+    shape = l.shape
+    pick = rng.random(shape)
+    sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32)
+    tiny = (sign * 2.0 ** rng.uniform(-40, -10.5, shape)).astype(np.float32)
+    large = (sign * 2.0 ** rng.uniform(6, 8, shape)).astype(np.float32)
+    l = np.where(pick < 0.01, 0.0, l)
+    l = np.where((pick >= 0.01) & (pick < 0.03), tiny, l)
+    l = np.where((pick >= 0.03) & (pick < 0.04), large, l)
+    l = np.where((pick >= 0.04) & (pick < 0.045), -np.inf, l)
+    l[0] = tiny[0]  # request 0: only tiny magnitudes
+    l[1] = np.where(rng.random(l[1].shape) < 0.5, large[1], tiny[1])  # request 1: none in the common binades
+    l[2, :, ::7] = 0.0
+    l = l.astype(np.float32)
+    w["logits_bits"] = f32_to_bf16_bits(l)
+    w["logits"] = bf16_bits_to_f32(w["logits_bits"])
+    gh.compare(w, gh.run_gpu(w), label="outside the common binades")
+    wo = dict(w, draft_probs=None)
+    gh.compare(wo, gh.run_gpu(wo), label="outside the common binades, one-hot")
+    gh.compare(w, gh.run_gpu_filtered(w, 40, 0.95), label="outside the common binades, filtered", filt=(40, 0.95))
+    wr = dict(w, temperature=0.3)
+    gh.compare(wr, gh.run_gpu(wr), label="outside the common binades, T=0.3")
+
+
 def test_out_of_range_draft_token_is_rejected():
     gh = _gh()
     w = make_dense_custom(10, B=4, gamma=2, V=1000, dtype="f32", temperature=1.0)
