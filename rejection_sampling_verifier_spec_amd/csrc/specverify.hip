@@ -2234,10 +2234,11 @@ __device__ void row_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
   dZt = dZ;
 }
 
-// Returns (thread 0 of a lazy-mode block) the value its mark raise returned,
-// or 0: the caller consumes it later, so that the atomic's round trip
-// overlaps the rest of the row's work.
-template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false>
+// Returns (thread 0 of a lazy-mode block) the value its mark raise returned
+// (RET_MARK), or 0: the caller consumes it later, so that the atomic's round
+// trip overlaps the rest of the row's work. Without RET_MARK the raise returns
+// nothing and the block never waits for it.
+template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false, bool RET_MARK = false>
 __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
                                          RowShared& sh,
                                          std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr) {
@@ -2493,11 +2494,16 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     // the certified Z interval in fp64 units (or {0, inf} when there is none)
     if (tid == 0) {
       const uint32_t f = sh.uncertain ? kRowUndecided : ((is_draft && accepted) ? kRowAccepted : kRowDeferred);
-      // a certain rejection raises the request's mark; the returned value goes
-      // back to the caller, which stores it (waiting for the atomic) before
-      // the first launch's count
-      if (is_draft && f == kRowDeferred)
-        mark_ret = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a certain rejection raises the request's mark; with RET_MARK the
+      // returned value goes back to the caller, which stores it (waiting for
+      // the atomic) before the first launch's count; otherwise the atomic
+      // returns nothing (the block's slot is not held for its round trip)
+      if (is_draft && f == kRowDeferred) {
+        if constexpr (RET_MARK)
+          mark_ret = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          (void)__hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (f != kRowAccepted) {
         double z = 0.0, dz = INFINITY;
         if (Z > 0.0 && Z < INFINITY && dZ < Z && m != -INFINITY) {
@@ -2660,11 +2666,14 @@ __device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
 
 // (FILTER: at least four waves per SIMD, two blocks per CU as without it;
 // the rare radix-select path of the threshold may then spill)
-template <typename LT, bool VEC, int NT, bool FILTER>
+template <typename LT, bool VEC, int NT, bool FILTER, bool LIST>
 __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
   // phase 0: first launch, alone; 1: first launch, a second follows (its last
   // block lists the tasks); 2: second launch, from that list; 3: first
-  // launch, a second follows that lists for itself; 4: that second launch
+  // launch, a second follows that lists for itself; 4: that second launch.
+  // LIST: built for phase 1 (the mark atomics return their values, which the
+  // count waits for); otherwise they return nothing and no block waits for
+  // their round trips.
   extern __shared__ float dyn[];
   __shared__ BlockScratchT<NT> sc;
   __shared__ RowShared sh;
@@ -2688,8 +2697,12 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
   // below: the clear has been performed before the count is issued; the
   // result is consumed only then, so the round trip overlaps the row)
   int mark_ret = 0;
-  if (!second && t.valid && t.i == 0 && threadIdx.x == 0)
-    mark_ret = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!second && t.valid && t.i == 0 && threadIdx.x == 0) {
+    if constexpr (LIST)
+      mark_ret = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (second && t.valid && t.i > 0) {
     if (threadIdx.x == 0)
       sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
@@ -2699,8 +2712,8 @@ __global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs
       read = false;
     }
   }
-  if (read) mark_ret ^= probs_row<LT, VEC, NT, false, FILTER>(a, t, dyn, sc, sh, &fsh);
-  if (phase != 1) return;
+  if (read) mark_ret ^= probs_row<LT, VEC, NT, false, FILTER, LIST>(a, t, dyn, sc, sh, &fsh);
+  if (!LIST || phase != 1) return;
   if (threadIdx.x == 0) sh.mark_old = mark_ret;  // waits for this thread's mark atomics
   // first launch: the last block to finish lists the tasks of the second launch
   // reads. Marks and the count are device-scope atomics; every mark update
@@ -3839,13 +3852,18 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
     // the second launch lists for itself when every block's pass over the
     // marks stays cheap (without top-k / top-p)
     const bool self = !FILTER && static_cast<int64_t>(a.B) * rest <= kSelfListMaxReads;
+    const int phase1 = rest > 0 ? (self ? 3 : 1) : 0;
     prof_record(SV_PROFILE_ROWS_FIRST, 0, st);
-    hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(a.B) * split), dim3(NT),
-                       lds, st, a, split, rest > 0 ? (self ? 3 : 1) : 0);
+    if (phase1 == 1)
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, true>), dim3(static_cast<unsigned>(a.B) * split),
+                         dim3(NT), lds, st, a, split, phase1);
+    else
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false>), dim3(static_cast<unsigned>(a.B) * split),
+                         dim3(NT), lds, st, a, split, phase1);
     prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
     if (rest > 0)
-      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER>), dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st,
-                         a, split, self ? 4 : 2);
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false>), dim3(static_cast<unsigned>(rest)), dim3(NT),
+                         lds, st, a, split, self ? 4 : 2);
   }
 }
 
