@@ -119,6 +119,9 @@ enum sv_status {
  * largest logits) could not decide it: */
 #define SV_ROW_HEAD2 0x2000u       /* from a second, larger or smaller, gathered head */
 #define SV_ROW_ROW_SELECT 0x4000u  /* from a radix select over the whole row */
+/* lazy mode, one-hot drafts (no q rows) with bf16 logits: */
+#define SV_ROW_TILE_SUMS 0x8000u   /* rejected (or bonus) row whose fp64 tile sums the per-row pass kept (the
+                                      per-request stage does not read its logits again) */
 
 /* Bytes of workspace needed for `num_target_rows` target rows (dense:
  * num_requests * (gamma + 1); ragged: num_draft_tokens + num_requests) of

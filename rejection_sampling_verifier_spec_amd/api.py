@@ -32,6 +32,7 @@ SV_ROW_UNDECIDED = 0x800
 SV_ROW_UNREAD = 0x1000
 SV_ROW_HEAD2 = 0x2000
 SV_ROW_ROW_SELECT = 0x4000
+SV_ROW_TILE_SUMS = 0x8000
 SV_ROW_WHY = {0x10: "accept", 0x20: "fallback", 0x40: "search", 0x80: "margin", 0x100: "forced"}
 SV_PROFILE_ROWS = 0
 SV_PROFILE_REQUEST = 1

@@ -441,6 +441,27 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// The same sum by DPP row moves on the two 32-bit halves (no lane-index
+// registers, no LDS), the four row totals then added in a fixed order: every
+// lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+__device__ __forceinline__ double wave_sum_d_dpp(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x124>(v);
+  v += dpp_d<0x128>(v);
+  return ((lane_d(v, 0) + lane_d(v, 16)) + lane_d(v, 32)) + lane_d(v, 48);
+}
+
 // Inclusive scan over the 64 lanes (lane order), fixed association.
 __device__ __forceinline__ double wave_scan_incl_d(double v) {
   const int lane = threadIdx.x & 63;
@@ -589,6 +610,7 @@ struct ProbsArgs {
   int* xdone;     // the list's per-row finished-tile counters (zeroed when a row is listed)
   double4* rstat; // lazy mode: {m, Z, sum e|a|} of deferred rows
   int* mark;      // lazy mode, per request: kMarkBase - (first position known to be a certain rejection), or 0
+  double* rsum;   // lazy mode, one-hot drafts with bf16 logits: [rows][nt] fp64 tile sums of the rows not accepted
   int pm;         // lazy mode: most positions of the first launch (all of a dense batch)
   int2* tasks;    // lazy mode: {request, position} of the rows the second launch takes (count at surv_n)
   int* surv_n;    // lazy mode: [0] the task count, [16] the first launch's finished-block counter
@@ -718,6 +740,7 @@ constexpr uint32_t kRowUnread = SV_ROW_UNREAD;
 constexpr uint32_t kRowHead2 = SV_ROW_HEAD2;
 constexpr uint32_t kRowRowSelect = SV_ROW_ROW_SELECT;
 constexpr uint32_t kRowUndecided = SV_ROW_UNDECIDED;
+constexpr uint32_t kRowTileSums = SV_ROW_TILE_SUMS;
 constexpr uint32_t kFlagLazy = 0x80000000u;    // internal: set by the host for the lazy mode
 constexpr uint32_t kFlagFilter = 0x40000000u;  // internal: lazy mode with top-k / top-p
 constexpr int kMarkBase = 1 << 30;              // lazy mode: per-request mark = kMarkBase - position
@@ -2664,92 +2687,6 @@ __device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
   return lazy_task(e.x, e.y, a.cu, a.B, a.gamma, a.ndraft);
 }
 
-// (FILTER: at least four waves per SIMD, two blocks per CU as without it;
-// the rare radix-select path of the threshold may then spill)
-template <typename LT, bool VEC, int NT, bool FILTER, bool LIST>
-__global__ __launch_bounds__(NT, FILTER ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
-  // phase 0: first launch, alone; 1: first launch, a second follows (its last
-  // block lists the tasks); 2: second launch, from that list; 3: first
-  // launch, a second follows that lists for itself; 4: that second launch.
-  // LIST: built for phase 1 (the mark atomics return their values, which the
-  // count waits for); otherwise they return nothing and no block waits for
-  // their round trips.
-  extern __shared__ float dyn[];
-  __shared__ BlockScratchT<NT> sc;
-  __shared__ RowShared sh;
-  __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
-  const bool second = phase == 2 || phase == 4;
-  Task t;
-  if constexpr (!FILTER) {
-    if (phase == 4) t = self_listed_task<NT>(a, p1, sh);
-  }
-  if (FILTER || phase != 4)
-    t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, phase == 2 ? a.tasks : nullptr,
-                         phase == 2 ? a.surv_n[0] : 0);
-  bool read = t.valid;
-  // The request's mark starts at zero in every call: its position-0 block (in
-  // the first launch) clears it before anything else. Blocks of the first
-  // launch therefore never read marks (its rows start in one round anyway);
-  // a mark raised there before the clear is lost, which only leaves a row to
-  // be read that could have been skipped. The second launch and the task
-  // list read marks after the first launch has completed.
-  // (a returning exchange whose result is stored before this block's count
-  // below: the clear has been performed before the count is issued; the
-  // result is consumed only then, so the round trip overlaps the row)
-  int mark_ret = 0;
-  if (!second && t.valid && t.i == 0 && threadIdx.x == 0) {
-    if constexpr (LIST)
-      mark_ret = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      __hip_atomic_store(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (second && t.valid && t.i > 0) {
-    if (threadIdx.x == 0)
-      sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
-    __syncthreads();
-    if (sh.skip) {
-      if (threadIdx.x == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowUnread));
-      read = false;
-    }
-  }
-  if (read) mark_ret ^= probs_row<LT, VEC, NT, false, FILTER, LIST>(a, t, dyn, sc, sh, &fsh);
-  if (!LIST || phase != 1) return;
-  if (threadIdx.x == 0) sh.mark_old = mark_ret;  // waits for this thread's mark atomics
-  // first launch: the last block to finish lists the tasks of the second launch
-  // reads. Marks and the count are device-scope atomics; every mark update
-  // (the clear above, a raise in probs_row) is a returning atomic whose result
-  // thread 0 stores above (so it has been performed) before that block's count
-  // is issued, and the last block reads the marks with device-scope atomic
-  // loads after its own count has returned, behind an acquire fence. No
-  // block needs a release fence (a cache write-back) of its own.
-  __syncthreads();
-  if (threadIdx.x == 0)
-    sh.last = __hip_atomic_fetch_add(a.surv_n + 16, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!sh.last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  list_survivors<NT>(a, p1, sh);
-  if (threadIdx.x == 0) a.surv_n[16] = 0;  // ready for the next call
-}
-
-// ----------------------------------------------------------------------------
-// lazy mode, phase 2: one block per request decides the request in fp64.
-//
-// The rows are taken in order; an accepted row passes. The first row that is
-// not (certainly rejected, or with an accept test the bound could not settle)
-// gets one fp64 pass over its logits and q: per tile, the sum E_j of
-// e_k = 2^((l_k - m) log2(e) / T) and the part of the residual sum that the
-// certified Z interval [zlo, zhi] of the fast pass already decides: P_j and
-// Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
-// every Z in the interval, and whether any element is left undecided. Then
-// Z = sum_j E_j; an undecided accept test is settled exactly (an accepted row
-// passes, and the next row is taken); W_j = P_j / Z - Q_j, the tiles with
-// undecided elements summed again with Z; residual mass <= 1e-8 falls back to
-// p; the tile search and the in-tile search draw the token in fp64. If every
-// draft is accepted, the bonus row is sampled from p the same way. The block
-// then writes the request's outputs.
-
 constexpr int kExpW = 4;  // exps in flight per lane in the fp64 pass
 constexpr int kExp2Bits = 8;                  // table index bits
 constexpr int kExp2Tab = 1 << kExp2Bits;      // 2^(j/256), j = 0..255 (2 KB of LDS)
@@ -2830,6 +2767,278 @@ __device__ __forceinline__ void exp2_negN(const double (&a)[N], const double* __
     e[k] = ldexp(p * tv[k], J[k] >> kExp2Bits);
   }
 }
+
+// Memo of the fp64 sums for bf16 logits: e(l) = 2^((l - m) s) of one row for
+// every bf16 value l with 2^-10 <= |l| < 2^6 (16 binades of 128 codes, both
+// signs: 4096 entries, 32 KB of LDS), each computed by the same fma and
+// exp2_neg as the direct path, so a looked-up e equals the computed one bit
+// for bit. Entry of code c: (c & 0x7fff) - kMemoLo, plus kMemoHalf when the
+// sign bit is set. A bf16 row holds at most 65536 distinct values and the
+// bulk of a logit row lies in these binades, so a block builds the table once
+// per row (4096 exp2) and then reads one entry per element instead of
+// evaluating the exp2; groups holding a value outside the range (tiny or large
+// magnitudes, inf, NaN) take the direct path.
+constexpr int kMemoHalf = 16 * 128;
+constexpr int kMemoN = 2 * kMemoHalf;
+constexpr uint32_t kMemoLo = (127u - 10u) << 7;  // bf16 magnitude code of 2^-10
+template <typename LT, bool VEC>
+constexpr bool kMemo = VEC && std::is_same_v<LT, uint16_t>;
+
+// Memo entries of the two bf16 values packed in w (low half first), as two
+// 16-bit fields; the 16-bit offsets from kMemoLo are or-ed into `miss`, where
+// any bit of 0xf800 in a half marks a value outside the memo (its entry is
+// then some other in-range one, replaced by the direct path).
+__device__ __forceinline__ uint32_t memo_index2(uint32_t w, uint32_t& miss) {
+  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+  const u16x2 lo = {static_cast<unsigned short>(kMemoLo), static_cast<unsigned short>(kMemoLo)};
+  const uint32_t off = __builtin_bit_cast(uint32_t, mag - lo);
+  miss |= off;
+  return (off & 0x07ff07ffu) | ((w >> 4) & 0x08000800u);  // sign bit 15 -> entry bit 11
+}
+
+// Build the memo of one row (every thread of the block takes part; the caller
+// waits at a barrier before reading it). With MASK, values below tau are 0.
+template <int NT, bool MASK>
+__device__ __forceinline__ void memo_build(double* memo, double s, double nms, float tau,
+                                           const double* __restrict__ tab, const Exp2Consts& C) {
+  static_assert(kMemoN % (kExpW * NT) == 0, "whole rounds of the block");
+  for (int i0 = threadIdx.x; i0 < kMemoN; i0 += kExpW * NT) {
+    double ar[kExpW], e[kExpW];
+#pragma unroll
+    for (int k = 0; k < kExpW; ++k) {
+      const uint32_t i = static_cast<uint32_t>(i0 + k * NT);
+      const uint32_t code = ((i / kMemoHalf) << 15) | (kMemoLo + i % kMemoHalf);
+      float l = __uint_as_float(code << 16);
+      if constexpr (MASK) l = l < tau ? -INFINITY : l;
+      ar[k] = fma(static_cast<double>(l), s, nms);
+    }
+    exp2_negN<kExpW>(ar, tab, C, e);
+#pragma unroll
+    for (int k = 0; k < kExpW; ++k) memo[i0 + k * NT] = e[k];
+  }
+}
+
+
+// One-hot drafts with bf16 logits (no q rows; the lazy mode without top-k /
+// top-p): the per-row pass sums the row in fp64 itself, e_k = 2^((l_k - A) s)
+// with A the block maximum of the first tiles (the anchor, carried as the
+// row's m), through the per-row memo (values outside its binades by the
+// direct fp64 exp2), so that the per-request stage never reads the row
+// again: with q = onehot(x) the residual is p without x's element, which the
+// tile sums E_j give. Z = sum_j E_j and the accept test p(x) = e_x / Z are
+// taken in fp64 (nothing left to certify); a row that is not accepted keeps
+// its E_j in the workspace (SV_ROW_TILE_SUMS). A row whose anchor or Z is
+// not finite and positive (all -inf first tiles, a value far above the
+// anchor) takes the general body.
+template <int NT, bool RET_MARK>
+__device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc, RowShared& sh,
+                               double* memo, double* tab) {
+  constexpr int kWaves = NT / 64;
+  using Raw = RawTile<uint16_t, true>;
+  const int V = a.V;
+  const int nt = (V + kTile - 1) / kTile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* __restrict__ lrow = static_cast<const uint16_t*>(a.logits) + t.trow * static_cast<int64_t>(V);
+  const bool is_draft = t.drow >= 0;
+  const int64_t x = is_draft ? a.x[t.drow] : -1;
+  const bool x_ok = is_draft && x >= 0 && x < V;
+  const float lx = x_ok ? to_float(lrow[x]) : -INFINITY;
+  const float u_acc = is_draft ? a.u[t.trow] : 0.f;
+  double* E = reinterpret_cast<double*>(dyn);  // [nt] (the dynamic LDS holds 4 nt floats)
+  auto load = [&](Raw& r, int j) {
+    if (j * kTile + kTile > V) r.load_padded(lrow, V, j * kTile, lane);  // -inf past the end
+    else r.load_full(lrow, j * kTile, lane);
+  };
+  exp2_table_init(tab);
+  Raw ra, rb;
+  int j = wave;
+  float lm = -INFINITY;
+  if (j < nt) {
+    load(ra, j);
+#pragma unroll
+    for (int k = 0; k < kLaneElems; ++k) lm = fmaxf(lm, ra.get(k));
+    lm = wave_max(lm);
+    if (j + kWaves < nt) load(rb, j + kWaves);  // in flight while the memo is built
+  }
+  if (lane == 0) sh.wmax[wave] = lm;
+  __syncthreads();  // (also publishes tab)
+  float A = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) A = fmaxf(A, sh.wmax[w]);
+  if (A > -INFINITY && A < INFINITY) {
+  const double s = a.s64;
+  const double nms = -(static_cast<double>(A) * s);
+  const Exp2Consts C = exp2_consts_load();
+  memo_build<NT, false>(memo, s, nms, 0.f, tab, C);
+  __syncthreads();
+  auto tile_sum = [&](const Raw& r) {
+    double es = 0.0;
+#pragma unroll
+    for (int w4 = 0; w4 < 16; w4 += 2) {  // the lane's 16 words, two at a time (four values)
+      const uint4& q0 = r.d[w4 >> 2];
+      const uint32_t w0 = (w4 & 3) == 0 ? q0.x : q0.z;
+      const uint32_t w1 = (w4 & 3) == 0 ? q0.y : q0.w;
+      uint32_t miss = 0;
+      const uint32_t i01 = memo_index2(w0, miss), i23 = memo_index2(w1, miss);
+      double e[4] = {memo[i01 & 0xffffu], memo[i01 >> 16], memo[i23 & 0xffffu], memo[i23 >> 16]};
+      if (__builtin_amdgcn_ballot_w64((miss & 0xf800f800u) != 0u)) {  // rare; same values elsewhere
+        const double ar[4] = {fma(static_cast<double>(__uint_as_float(w0 << 16)), s, nms),
+                              fma(static_cast<double>(__uint_as_float(w0 & 0xffff0000u)), s, nms),
+                              fma(static_cast<double>(__uint_as_float(w1 << 16)), s, nms),
+                              fma(static_cast<double>(__uint_as_float(w1 & 0xffff0000u)), s, nms)};
+        exp2_negN<4>(ar, tab, C, e);
+      }
+      es += (e[0] + e[1]) + (e[2] + e[3]);
+    }
+    return wave_sum_d_dpp(es);
+  };
+  // tiles wave, wave + kWaves, ...: ra holds the current one, rb the next
+  // (its loads in flight), the one after goes into ra once ra is summed
+  if (j < nt) {
+    while (true) {
+      const double ta = tile_sum(ra);
+      if (lane == 0) E[j] = ta;
+      if (j + 2 * kWaves < nt) load(ra, j + 2 * kWaves);
+      j += kWaves;
+      if (j >= nt) break;
+      const double tb = tile_sum(rb);
+      if (lane == 0) E[j] = tb;
+      if (j + 2 * kWaves < nt) load(rb, j + 2 * kWaves);
+      j += kWaves;
+      if (j >= nt) break;
+    }
+  }
+  __syncthreads();
+  double zl = 0.0;
+  for (int q = tid; q < nt; q += NT) zl += E[q];
+  const double Z = block_sum<NT>(zl, sc);
+  if (Z > 0.0 && Z < INFINITY) {
+  if (tid == 0) {
+    int accepted = 0;
+    if (x_ok) {
+      const double px = exp2_neg(fma(static_cast<double>(lx), s, nms), tab) / Z;
+      accepted = (px > 0.0 && static_cast<double>(u_acc) <= px) ? 1 : 0;  // q(x) = 1
+    }
+    sh.accepted = accepted;
+  }
+  __syncthreads();
+  const bool accepted = sh.accepted != 0;
+  int mark_ret = 0;
+  if (!accepted) {
+    double* rs = a.rsum + t.trow * static_cast<int64_t>(nt);
+    for (int q = tid; q < nt; q += NT) rs[q] = E[q];
+  }
+  if (tid == 0) {
+    const uint32_t f = accepted ? kRowAccepted : (kRowDeferred | kRowTileSums);
+    if (is_draft && !accepted) {  // a certain rejection raises the request's mark
+      if constexpr (RET_MARK)
+        mark_ret = __hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        (void)__hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!accepted) a.rstat[t.trow] = make_double4(static_cast<double>(A), Z, 0.0, -static_cast<double>(INFINITY));
+    a.ws[t.trow] = make_int2(-1, static_cast<int>(f));
+  }
+  return mark_ret;
+  }  // Z finite and positive
+  }  // anchor finite
+  __syncthreads();  // the general body reuses the shared state
+  return probs_row<uint16_t, true, NT, false, false, RET_MARK>(a, t, dyn, sc, sh);
+}
+
+// (FILTER: at least four waves per SIMD, two blocks per CU as without it;
+// the rare radix-select path of the threshold may then spill)
+template <typename LT, bool VEC, int NT, bool FILTER, bool LIST, bool ONEHOT = false>
+__global__ __launch_bounds__(NT, (FILTER || ONEHOT) ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
+  // phase 0: first launch, alone; 1: first launch, a second follows (its last
+  // block lists the tasks); 2: second launch, from that list; 3: first
+  // launch, a second follows that lists for itself; 4: that second launch.
+  // LIST: built for phase 1 (the mark atomics return their values, which the
+  // count waits for); otherwise they return nothing and no block waits for
+  // their round trips. ONEHOT: bf16 rows of a batch with one-hot drafts, summed
+  // in fp64 through the memo (onehot_memo_row).
+  static_assert(!ONEHOT || (std::is_same_v<LT, uint16_t> && VEC && !FILTER), "one-hot memo rows: bf16, no filter");
+  extern __shared__ float dyn[];
+  __shared__ double memo_s[ONEHOT ? kMemoN : 1];
+  __shared__ double tab_s[ONEHOT ? kExp2Tab : 1];
+  __shared__ BlockScratchT<NT> sc;
+  __shared__ RowShared sh;
+  __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
+  const bool second = phase == 2 || phase == 4;
+  Task t;
+  if constexpr (!FILTER) {
+    if (phase == 4) t = self_listed_task<NT>(a, p1, sh);
+  }
+  if (FILTER || phase != 4)
+    t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, phase == 2 ? a.tasks : nullptr,
+                         phase == 2 ? a.surv_n[0] : 0);
+  bool read = t.valid;
+  // The request's mark starts at zero in every call: its position-0 block (in
+  // the first launch) clears it before anything else. Blocks of the first
+  // launch therefore never read marks (its rows start in one round anyway);
+  // a mark raised there before the clear is lost, which only leaves a row to
+  // be read that could have been skipped. The second launch and the task
+  // list read marks after the first launch has completed.
+  // (a returning exchange whose result is stored before this block's count
+  // below: the clear has been performed before the count is issued; the
+  // result is consumed only then, so the round trip overlaps the row)
+  int mark_ret = 0;
+  if (!second && t.valid && t.i == 0 && threadIdx.x == 0) {
+    if constexpr (LIST)
+      mark_ret = __hip_atomic_exchange(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(a.mark + t.b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (second && t.valid && t.i > 0) {
+    if (threadIdx.x == 0)
+      sh.skip = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > kMarkBase - t.i;
+    __syncthreads();
+    if (sh.skip) {
+      if (threadIdx.x == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowUnread));
+      read = false;
+    }
+  }
+  if (read) {
+    if constexpr (ONEHOT) mark_ret ^= onehot_memo_row<NT, LIST>(a, t, dyn, sc, sh, memo_s, tab_s);
+    else mark_ret ^= probs_row<LT, VEC, NT, false, FILTER, LIST>(a, t, dyn, sc, sh, &fsh);
+  }
+  if (!LIST || phase != 1) return;
+  if (threadIdx.x == 0) sh.mark_old = mark_ret;  // waits for this thread's mark atomics
+  // first launch: the last block to finish lists the tasks of the second launch
+  // reads. Marks and the count are device-scope atomics; every mark update
+  // (the clear above, a raise in probs_row) is a returning atomic whose result
+  // thread 0 stores above (so it has been performed) before that block's count
+  // is issued, and the last block reads the marks with device-scope atomic
+  // loads after its own count has returned, behind an acquire fence. No
+  // block needs a release fence (a cache write-back) of its own.
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sh.last = __hip_atomic_fetch_add(a.surv_n + 16, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!sh.last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  list_survivors<NT>(a, p1, sh);
+  if (threadIdx.x == 0) a.surv_n[16] = 0;  // ready for the next call
+}
+
+// ----------------------------------------------------------------------------
+// lazy mode, phase 2: one block per request decides the request in fp64.
+//
+// The rows are taken in order; an accepted row passes. The first row that is
+// not (certainly rejected, or with an accept test the bound could not settle)
+// gets one fp64 pass over its logits and q: per tile, the sum E_j of
+// e_k = 2^((l_k - m) log2(e) / T) and the part of the residual sum that the
+// certified Z interval [zlo, zhi] of the fast pass already decides: P_j and
+// Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
+// every Z in the interval, and whether any element is left undecided. Then
+// Z = sum_j E_j; an undecided accept test is settled exactly (an accepted row
+// passes, and the next row is taken); W_j = P_j / Z - Q_j, the tiles with
+// undecided elements summed again with Z; residual mass <= 1e-8 falls back to
+// p; the tile search and the in-tile search draw the token in fp64. If every
+// draft is accepted, the bonus row is sampled from p the same way. The block
+// then writes the request's outputs.
 
 // Chunk c (0..3) of a lane's part of the tile at `base`: the lane's elements
 // k = 8c .. 8c + 7 in the tile layout (see Lay), as fp32 logits (-inf past the
@@ -3041,22 +3250,6 @@ __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j ==
 constexpr int kPassNT = 256;       // threads per block of the per-request kernel
 constexpr int kPassWaves = kPassNT / 64;
 
-// Memo of the fp64 pass for bf16 logits: e(l) = 2^((l - m) s) of one row for
-// every bf16 value l with 2^-10 <= |l| < 2^6 (16 binades of 128 codes, both
-// signs: 4096 entries, 32 KB of LDS), each computed by the same fma and
-// exp2_neg as the direct path, so a looked-up e equals the computed one bit
-// for bit. Entry of code c: (c & 0x7fff) - kMemoLo, plus kMemoHalf when the
-// sign bit is set. A bf16 row holds at most 65536 distinct values and the
-// bulk of a logit row lies in these binades, so a block builds the table once
-// per row (4096 exp2) and then reads one entry per element instead of
-// evaluating the exp2; groups holding a value outside the range (tiny or large
-// magnitudes, inf, NaN) take the direct path.
-constexpr int kMemoHalf = 16 * 128;
-constexpr int kMemoN = 2 * kMemoHalf;
-constexpr uint32_t kMemoLo = (127u - 10u) << 7;  // bf16 magnitude code of 2^-10
-template <typename LT, bool VEC>
-constexpr bool kMemo = VEC && std::is_same_v<LT, uint16_t>;
-
 // The memo and the finish's crossing-tile weights are never live together
 // (the pass ends at a barrier before the finish, and every pass rebuilds the
 // memo), so they share the LDS.
@@ -3075,41 +3268,6 @@ struct ReqSharedT {
   int token;
   int pad;
 };
-
-// Memo entries of the two bf16 values packed in w (low half first), as two
-// 16-bit fields; the 16-bit offsets from kMemoLo are or-ed into `miss`, where
-// any bit of 0xf800 in a half marks a value outside the memo (its entry is
-// then some other in-range one, replaced by the direct path).
-__device__ __forceinline__ uint32_t memo_index2(uint32_t w, uint32_t& miss) {
-  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
-  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
-  const u16x2 lo = {static_cast<unsigned short>(kMemoLo), static_cast<unsigned short>(kMemoLo)};
-  const uint32_t off = __builtin_bit_cast(uint32_t, mag - lo);
-  miss |= off;
-  return (off & 0x07ff07ffu) | ((w >> 4) & 0x08000800u);  // sign bit 15 -> entry bit 11
-}
-
-// Build the memo of one row (every thread of the block takes part; the caller
-// waits at a barrier before reading it). With MASK, values below tau are 0.
-template <bool MASK>
-__device__ __forceinline__ void memo_build(double* memo, double s, double nms, float tau,
-                                           const double* __restrict__ tab, const Exp2Consts& C) {
-  static_assert(kMemoN % (kExpW * kPassNT) == 0, "whole rounds of the block");
-  for (int i0 = threadIdx.x; i0 < kMemoN; i0 += kExpW * kPassNT) {
-    double ar[kExpW], e[kExpW];
-#pragma unroll
-    for (int k = 0; k < kExpW; ++k) {
-      const uint32_t i = static_cast<uint32_t>(i0 + k * kPassNT);
-      const uint32_t code = ((i / kMemoHalf) << 15) | (kMemoLo + i % kMemoHalf);
-      float l = __uint_as_float(code << 16);
-      if constexpr (MASK) l = l < tau ? -INFINITY : l;
-      ar[k] = fma(static_cast<double>(l), s, nms);
-    }
-    exp2_negN<kExpW>(ar, tab, C, e);
-#pragma unroll
-    for (int k = 0; k < kExpW; ++k) memo[i0 + k * kPassNT] = e[k];
-  }
-}
 
 // The fp64 pass of one row over tiles j = j0, j0 + step, ... < j1, one tile
 // per wave at a time, in four chunks of 8 elements per lane; a ring of four
@@ -3205,7 +3363,7 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
       load(1, j, 1);
       load(2, j, 2);
     }
-    memo_build<MASK>(memo, s, nms, tau, tab, C);
+    memo_build<kPassNT, MASK>(memo, s, nms, tau, tab, C);
     __syncthreads();
     if (j >= j1) return;
   } else {
@@ -3329,7 +3487,8 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
       const double qx = x_ok ? (onehot ? 1.0 : static_cast<double>(qrow[x])) : 0.0;
       if (x_ok && px > 0.0 && static_cast<double>(a.u[trow]) * qx <= px) {
         if (tid == 0)
-          a.ws[trow] = make_int2(-1, static_cast<int>(kRowAccepted | rflags | (f0 & (kRowHead2 | kRowRowSelect))));
+          a.ws[trow] = make_int2(
+              -1, static_cast<int>(kRowAccepted | rflags | (f0 & (kRowHead2 | kRowRowSelect | kRowTileSums))));
         __syncthreads();
         return true;
       }
@@ -3500,7 +3659,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
     }
     if (lane == 0) {
       sel.nacc[b] = n;
-      a.ws[trow] = make_int2(token, static_cast<int>(rflags | (f0 & (kRowHead2 | kRowRowSelect))));
+      a.ws[trow] = make_int2(token, static_cast<int>(rflags | (f0 & (kRowHead2 | kRowRowSelect | kRowTileSums))));
     }
     return false;
   }
@@ -3558,14 +3717,24 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
   int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &rs.first);  // (its barriers also publish tab)
   const Exp2Consts C = exp2_consts_load();
   for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
-    if (MODE == kReqFinish && guard == 0) {
+    const int64_t trow = t0 + n;
+    if (static_cast<uint32_t>(a.ws[trow].y) & kRowTileSums) {
+      // one-hot drafts with bf16 logits: the per-row pass kept the row's fp64
+      // tile sums (relative to the m it recorded); no q, so P and Q are 0
+      if constexpr (MODE == kReqPass) return;
+      const double* src = a.rsum + trow * static_cast<int64_t>(nt);
+      for (int j = tid; j < nt; j += kPassNT) {
+        rbuf[j] = src[j];
+        rbuf[nt + j] = 0.0;
+        rbuf[2 * nt + j] = 0.0;
+      }
+    } else if (MODE == kReqFinish && guard == 0) {
       for (int j = tid; j < nt; j += kPassNT) {
         rbuf[j] = pa.E[o + j];
         rbuf[nt + j] = pa.P[o + j];
         rbuf[2 * nt + j] = pa.Q[o + j];
       }
     } else {
-      const int64_t trow = t0 + n;
       const bool draft = n < g;
       const double4 st = a.rstat[trow];
       const double zhi = (st.y + st.z) * (1.0 + kZSlack), zlo = (st.y - st.z) * (1.0 - kZSlack);
@@ -3854,6 +4023,21 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
     const bool self = !FILTER && static_cast<int64_t>(a.B) * rest <= kSelfListMaxReads;
     const int phase1 = rest > 0 ? (self ? 3 : 1) : 0;
     prof_record(SV_PROFILE_ROWS_FIRST, 0, st);
+    if constexpr (kMemo<LT, VEC> && !FILTER) {
+      if (a.q == nullptr) {  // one-hot drafts: rows summed in fp64 through the memo
+        if (phase1 == 1)
+          hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, false, true, true>),
+                             dim3(static_cast<unsigned>(a.B) * split), dim3(NT), lds, st, a, split, phase1);
+        else
+          hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, false, false, true>),
+                             dim3(static_cast<unsigned>(a.B) * split), dim3(NT), lds, st, a, split, phase1);
+        prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
+        if (rest > 0)
+          hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, false, false, true>), dim3(static_cast<unsigned>(rest)),
+                             dim3(NT), lds, st, a, split, self ? 4 : 2);
+        return;
+      }
+    }
     if (phase1 == 1)
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, true>), dim3(static_cast<unsigned>(a.B) * split),
                          dim3(NT), lds, st, a, split, phase1);
@@ -3892,7 +4076,9 @@ template <typename LT, bool VEC, bool FILTER, bool HASQ>
 void launch_request_modes(const ProbsArgs& a, const SelectArgs& sel, const PassArrays& pa, size_t lds2,
                           hipStream_t st) {
   const int nt = (a.V + kTile - 1) / kTile;
-  const int sl = request_slices(a.B, nt, request_blocks_per_cu<LT, VEC, HASQ>());
+  // (one-hot drafts with bf16 logits: the per-row pass kept the deciding
+  // rows' tile sums, and one block per request only finishes)
+  const int sl = (!HASQ && kMemo<LT, VEC>) ? 1 : request_slices(a.B, nt, request_blocks_per_cu<LT, VEC, HASQ>());
   if (sl == 1) {
     hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqFused>), dim3(static_cast<unsigned>(a.B)),
                        dim3(kPassNT), lds2, st, a, sel, pa, 1);
@@ -4031,6 +4217,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.top_p = filter ? fa.top_p : 1.0;
     p.rstat = reinterpret_cast<double4*>(wsb + wl.rstat);
     p.mark = reinterpret_cast<int*>(wsb + wl.mark);
+    p.rsum = reinterpret_cast<double*>(wsb + wl.etile);
     p.tasks = reinterpret_cast<int2*>(wsb + wl.surv);
     p.surv_n = reinterpret_cast<int*>(wsb + wl.count + 128);
 

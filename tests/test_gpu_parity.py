@@ -660,6 +660,34 @@ def test_bf16_values_outside_the_common_binades():
     gh.compare(wr, gh.run_gpu(wr), label="outside the common binades, T=0.3")
 
 
+def test_onehot_bf16_rows_summed_by_the_per_row_pass():
+    """One-hot drafts with bf16 logits: the per-row pass sums every row it
+    reads in fp64 against an anchor (the maximum of the block's first tiles)
+    and keeps the tile sums of the rows it does not accept
+    (SV_ROW_TILE_SUMS), so the per-request stage only finishes. Rows that
+    cannot be summed that way take the general per-row body: every value of
+    the first tiles -inf (request 0), and at T = 0.05 one value so far above
+    the anchor that the fp64 sum overflows (request 1; at T = 1 it does not).
+    Compared with the oracle on every request."""
+    from rejection_sampling_verifier_spec_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    gh = _gh()
+    B, g, V = 16, 3, 40000
+    for T in (1.0, 0.05):
+        w = make_dense_custom(47, B=B, gamma=g, V=V, dtype="bf16", temperature=T, q_kind="onehot")
+        l = w["logits"].copy()
+        l[0, :, :16384] = -np.inf
+        l[1, :, 30000] = 120.0
+        w["logits_bits"] = f32_to_bf16_bits(l)
+        w["logits"] = bf16_bits_to_f32(w["logits_bits"])
+        out, nacc, _, rec = gpu = gh.run_gpu(w)
+        gh.compare(w, gpu, label=f"one-hot rows summed per row, T={T}")
+        flags = rec[:, 1].reshape(B, g + 1)
+        for b in range(B):
+            kept = (int(flags[b, int(nacc[b])]) & api.SV_ROW_TILE_SUMS) != 0
+            general = b == 0 or (b == 1 and T == 0.05)
+            assert kept != general, (T, b, hex(int(flags[b, int(nacc[b])])))
+
+
 def test_out_of_range_draft_token_is_rejected():
     gh = _gh()
     w = make_dense_custom(10, B=4, gamma=2, V=1000, dtype="f32", temperature=1.0)
