@@ -2838,13 +2838,22 @@ __device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, Bl
   using Raw = RawTile<uint16_t, true>;
   const int V = a.V;
   const int nt = (V + kTile - 1) / kTile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* __restrict__ lrow = static_cast<const uint16_t*>(a.logits) + t.trow * static_cast<int64_t>(V);
-  const bool is_draft = t.drow >= 0;
-  const int64_t x = is_draft ? a.x[t.drow] : -1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: tile indices and their tests too)
+  // the task is the block's (a second launch takes it from LDS): uniform, so
+  // that the row's address stays in scalar registers
+  auto uni64 = [](int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const int64_t trow = uni64(t.trow), drow = uni64(t.drow);
+  const uint16_t* __restrict__ lrow = static_cast<const uint16_t*>(a.logits) + trow * static_cast<int64_t>(V);
+  const bool is_draft = drow >= 0;
+  const int64_t x = is_draft ? a.x[drow] : -1;
   const bool x_ok = is_draft && x >= 0 && x < V;
   const float lx = x_ok ? to_float(lrow[x]) : -INFINITY;
-  const float u_acc = is_draft ? a.u[t.trow] : 0.f;
+  const float u_acc = is_draft ? a.u[trow] : 0.f;
   double* E = reinterpret_cast<double*>(dyn);  // [nt] (the dynamic LDS holds 4 nt floats)
   auto load = [&](Raw& r, int j) {
     if (j * kTile + kTile > V) r.load_padded(lrow, V, j * kTile, lane);  // -inf past the end
@@ -2926,7 +2935,7 @@ __device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, Bl
   const bool accepted = sh.accepted != 0;
   int mark_ret = 0;
   if (!accepted) {
-    double* rs = a.rsum + t.trow * static_cast<int64_t>(nt);
+    double* rs = a.rsum + trow * static_cast<int64_t>(nt);
     for (int q = tid; q < nt; q += NT) rs[q] = E[q];
   }
   if (tid == 0) {
@@ -2937,8 +2946,8 @@ __device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, Bl
       else
         (void)__hip_atomic_fetch_max(a.mark + t.b, kMarkBase - t.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (!accepted) a.rstat[t.trow] = make_double4(static_cast<double>(A), Z, 0.0, -static_cast<double>(INFINITY));
-    a.ws[t.trow] = make_int2(-1, static_cast<int>(f));
+    if (!accepted) a.rstat[trow] = make_double4(static_cast<double>(A), Z, 0.0, -static_cast<double>(INFINITY));
+    a.ws[trow] = make_int2(-1, static_cast<int>(f));
   }
   return mark_ret;
   }  // Z finite and positive
