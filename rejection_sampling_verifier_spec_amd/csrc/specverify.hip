@@ -2276,7 +2276,7 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
   float* M = dyn + nt;      // running max when the tile was summed (>= every element of the tile)
   float* W = dyn + 2 * nt;  // tile sums of max(0, p - q)
   float* EA = dyn + 3 * nt; // tile sums of e |a| (a = the exp argument), for the error bound
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + t.trow * static_cast<int64_t>(V);
   const bool is_draft = t.drow >= 0;
@@ -2982,6 +2982,21 @@ __global__ __launch_bounds__(NT, (FILTER || ONEHOT) ? 4 : 1) void lazy_rows_kern
   if (FILTER || phase != 4)
     t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, phase == 2 ? a.tasks : nullptr,
                          phase == 2 ? a.surv_n[0] : 0);
+  // the task is the block's (uniform): keep it in scalar registers
+  {
+    auto uni64 = [](int64_t v) {
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+      return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    };
+    t.b = __builtin_amdgcn_readfirstlane(t.b);
+    t.g = __builtin_amdgcn_readfirstlane(t.g);
+    t.i = __builtin_amdgcn_readfirstlane(t.i);
+    t.trow = uni64(t.trow);
+    t.drow = uni64(t.drow);
+    t.srow = uni64(t.srow);
+    t.valid = __builtin_amdgcn_readfirstlane(t.valid ? 1 : 0) != 0;
+  }
   bool read = t.valid;
   // The request's mark starts at zero in every call: its position-0 block (in
   // the first launch) clears it before anything else. Blocks of the first
