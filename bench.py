@@ -293,8 +293,10 @@ def call_bytes(rec, nacc, V, esz, has_q, gamma=None, cu=None):
     """Bytes one call reads, from its row records: `unique` counts every
     input element once (the logit rows the per-row pass read, the q rows of
     the replacement draws, 16 B of token, q(x) and uniform per draft row
-    read); `reread` the logit rows the per-request stage reads again (the
-    deciding rows). Returns a dict with the row counts."""
+    read); `reread` the logits the per-request stage reads again: each
+    request's deciding row, or only the 2048-element tile the draw falls in
+    when the per-row pass kept the row's tile sums (SV_ROW_TILE_SUMS: one-hot
+    drafts with bf16 logits). Returns a dict with the row counts."""
     import numpy as np
 
     flags = rec[:, 1].astype(np.int64)
@@ -311,7 +313,13 @@ def call_bytes(rec, nacc, V, esz, has_q, gamma=None, cu=None):
     rows_read = int(np.count_nonzero(read))
     drafts_read = int(np.count_nonzero(read & draft))
     unique = rows_read * V * esz + drafts_read * 16 + (resid * V * 4 if has_q else 0)
-    reread = (resid + bonus) * V * esz
+    nacc64 = np.asarray(nacc).astype(np.int64)
+    if cu is None:
+        deciding = np.arange(B) * (gamma + 1) + nacc64
+    else:
+        deciding = cu[:-1].astype(np.int64) + np.arange(B) + nacc64
+    kept = (flags[deciding] & 0x8000) != 0  # SV_ROW_TILE_SUMS
+    reread = int(np.where(kept, min(V, 2048), V).sum()) * esz
     needed = int(np.sum(nacc + 1)) * V * esz + (resid * V * 4 if has_q else 0)
     return dict(unique=unique, reread=reread, rows_read=rows_read, drafts_read=drafts_read, residual=resid,
                 bonus=bonus, rows=rows, needed=needed)
