@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lazy_rows_kernel_peaked_bf16_b256_g7_v128256_traffic.txt")
+SPEC_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "probs_rows_kernel_speculative_peaked_bf16_b256_g7_v128256_traffic.txt")
 
 
 def source_sha256() -> str:
@@ -50,21 +51,21 @@ def source_sha256() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per call of the per-row pass (both launches) from the
-    committed rocprofv3 summary, or None when it is missing or was taken on
-    another source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(path=TRAFFIC_FILE, keys=("rows_kernel_hbm_bytes_per_call",)):
+    """HBM bytes per call of the given kernels (default: the per-row pass,
+    both launches) from a committed rocprofv3 summary, or None when it is
+    missing or was taken on another source."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("source_sha256") != source_sha256():
         return None
     try:
-        return float(vals["rows_kernel_hbm_bytes_per_call"])
+        return sum(float(vals[k]) for k in keys)
     except (KeyError, ValueError):
         return None
 
@@ -436,9 +437,15 @@ def measure_speculative(steps, sets, T, ws, stream, esz, V):
     wall = time_calls(call, sets, steps)
     B, g = sets[0][2].shape
     nbytes = B * (g + 1) * V * esz + B * g * (V * 4 + 16)
+    # the bytes its kernels move (rocprofv3 summary of this source, or None):
+    # every logit row is read twice, once for Z and once with q for the
+    # residual tile sums, which need Z
+    moved = measured_traffic(SPEC_TRAFFIC_FILE, ("eager_rows_kernel_hbm_bytes_per_call",
+                                                 "exact_kernel_hbm_bytes_per_call"))
     return {"flags": api.SV_FLAG_ALL_RESIDUALS, "steps": steps, "input_sets": NSETS, "ms_per_call": wall * 1e3,
             "positions_per_s": B * g / wall, "unique_bytes_per_call": nbytes, "achieved_GBps": nbytes / wall / 1e9,
-            "frac_of_hbm_peak": nbytes / wall / 1e9 / HBM_PEAK_GBS}
+            "frac_of_hbm_peak": nbytes / wall / 1e9 / HBM_PEAK_GBS, "measured_hbm_bytes_per_call": moved,
+            "measured_GBps_over_call": None if moved is None else moved / wall / 1e9}
 
 
 def main():

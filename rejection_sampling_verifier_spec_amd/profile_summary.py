@@ -31,7 +31,8 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRC = os.path.join(ROOT, "rejection_sampling_verifier_spec_amd", "csrc", "specverify.hip")
 
-FAMILIES = {"rows": "lazy_rows_kernel", "request": "request_kernel", "copy": "copyBuffer"}
+FAMILIES = {"rows": "lazy_rows_kernel", "request": "request_kernel", "eager_rows": "probs_rows_kernel",
+            "exact": "exact_kernel", "greedy": "greedy_rows_kernel", "copy": "copyBuffer"}
 CLOCK_MHZ = 2400.0  # MI355X engine clock for the utilisation figures
 SIMDS = 1024        # 256 compute units x 4 SIMDs
 
@@ -80,7 +81,7 @@ def cmd_stats(args) -> None:
         durs = collections.defaultdict(list)
         for r in csv.DictReader(open(traces[0])):
             f = family(r["Kernel_Name"])
-            if f in ("rows", "request"):
+            if f is not None and f != "copy":
                 durs[(f, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))].append(
                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         lines += ["", "# per launch (family, grid threads, block threads): dispatches, median / mean us"]
