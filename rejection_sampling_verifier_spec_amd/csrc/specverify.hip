@@ -1130,22 +1130,22 @@ __global__ __launch_bounds__(kNT) void exact_kernel(ProbsArgs a, ExactArgs e, Se
     __syncthreads();  // every thread is done with `last` of the previous item
     if (r.t.valid) exact_item<LT>(a, e, r, pos, j0, sc);
     if (threadIdx.x == 0) {
-      __threadfence();  // release this item's tile sums
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release this item's tile sums
       last = atomicAdd(&e.done[pos], 1) == per_row - 1;
     }
     __syncthreads();
     if (!last) continue;
-    __threadfence();  // acquire every tile sum of the row
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire every tile sum of the row
     if (r.t.valid) exact_finish_row<LT>(a, e, r, pos, xtile, sc, sh);
     if (threadIdx.x == 0) {
       e.done[pos] = 0;
-      __threadfence();  // release the row's record
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release the row's record
       last = atomicAdd(e.finished, 1) == n - 1;
     }
     __syncthreads();
     if (!last) continue;
     // the last listed row is done: select every request that holds a listed row
-    __threadfence();  // acquire every record
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire every record
     for (int p = threadIdx.x; p < n; p += kNT) {
       const ExactRow rr = exact_row_info(a, e, p);
       if (rr.t.valid) select_request(sel, rr.t.b, false);
