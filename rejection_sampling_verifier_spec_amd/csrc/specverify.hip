@@ -462,6 +462,42 @@ __device__ __forceinline__ double wave_sum_d_dpp(double v) {
   return ((lane_d(v, 0) + lane_d(v, 16)) + lane_d(v, 32)) + lane_d(v, 48);
 }
 
+// Inclusive scan over the 64 lanes in lane order by DPP: a shift-and-add scan
+// within each 16-lane row (shifts 1, 2, 4, 8; lanes past the row's start
+// read 0), then the earlier rows' totals added in a fixed order. Every lane's
+// result is deterministic; no LDS traffic.
+template <int N>
+__device__ __forceinline__ double dpp_shr_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x110 + N, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x110 + N, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_scan_incl_d_dpp(double v) {
+  v += dpp_shr_d<1>(v);
+  v += dpp_shr_d<2>(v);
+  v += dpp_shr_d<4>(v);
+  v += dpp_shr_d<8>(v);
+  const double t0 = lane_d(v, 15), t1 = lane_d(v, 31), t2 = lane_d(v, 47);
+  const int lane = threadIdx.x & 63;
+  if (lane < 16) return v;
+  const double t01 = t0 + t1;
+  return v + (lane < 32 ? t0 : lane < 48 ? t01 : t01 + t2);
+}
+// Sum over the block by DPP wave sums, then the waves' sums in a fixed order.
+template <int NT>
+__device__ double block_sum_dpp(double v, BlockScratchT<NT>& s) {
+  constexpr int kWaves = NT / 64;
+  v = wave_sum_d_dpp(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s.d[wave] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) r += s.d[w];
+  __syncthreads();
+  return r;
+}
+
 // Inclusive scan over the 64 lanes (lane order), fixed association.
 __device__ __forceinline__ double wave_scan_incl_d(double v) {
   const int lane = threadIdx.x & 63;
@@ -3499,7 +3535,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
     for (int j = tid; j < nt; j += kPassNT) W[j] = P[j] < 0.0 ? -1.0 : 0.0;  // -1: undecided elements
     double zl = 0.0;
     for (int j = tid; j < nt; j += kPassNT) zl += E[j];
-    const double Z = block_sum<kPassNT>(zl, sc);
+    const double Z = block_sum_dpp<kPassNT>(zl, sc);
     const double iz = 1.0 / Z;
 
     uint32_t rflags = undecided ? (kRowExact | kWhyAccept) : 0u;
@@ -3569,8 +3605,8 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
     const int jlo = min(nt, lane * tp), jhi = min(nt, jlo + tp);
     double tv = 0.0;
     for (int j = jlo; j < jhi; ++j) tv += tile_val(j);
-    double incl = wave_scan_incl_d(tv);
-    double total = __shfl(incl, 63);
+    double incl = wave_scan_incl_d_dpp(tv);
+    double total = lane_d(incl, 63);
     if (mode == 1) {
       rflags |= kRowResidual;
       if (total <= kFallbackMass) {  // residual mass too small: sample from p
@@ -3578,8 +3614,8 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
         rflags |= kRowFallback;
         tv = 0.0;
         for (int j = jlo; j < jhi; ++j) tv += tile_val(j);
-        incl = wave_scan_incl_d(tv);
-        total = __shfl(incl, 63);
+        incl = wave_scan_incl_d_dpp(tv);
+        total = lane_d(incl, 63);
       }
     }
     const double tau = u_smp * total;
@@ -3614,7 +3650,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
       double pl = 0.0;
       for (int j = jlo; j < jhi; ++j)
         if (j < jt) pl += tile_val(j);
-      pb = wave_sum_d(pl);
+      pb = wave_sum_d_dpp(pl);
     }
     // in-tile search: scan lane l (of wave 0) owns the 32 consecutive elements
     // jt*kTile + 32 l + (0..31). The four waves compute the tile's weights
@@ -3650,7 +3686,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
     double ls = 0.0;
 #pragma unroll 8
     for (int i = 0; i < 32; ++i) ls += rs.wbuf[i * 64 + lane];
-    const double lincl = wave_scan_incl_d(ls);
+    const double lincl = wave_scan_incl_d_dpp(ls);
     const double tl = tau - pb;
     int tok = -1, lastpos = -1;
     {
@@ -3737,6 +3773,14 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
   const int g = d1 - d0;
   const int64_t t0 = static_cast<int64_t>(d0) + b;
   const int64_t o = static_cast<int64_t>(b) * nt;
+  // the finish's first tile sums (they do not depend on the open row): their
+  // loads go out before the row search and the table
+  double pf[3] = {0.0, 0.0, 0.0};
+  if (MODE == kReqFinish && tid < nt) {
+    pf[0] = pa.E[o + tid];
+    pf[1] = pa.P[o + tid];
+    pf[2] = pa.Q[o + tid];
+  }
   exp2_table_init(tab);
   int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &rs.first);  // (its barriers also publish tab)
   const Exp2Consts C = exp2_consts_load();
@@ -3754,9 +3798,10 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
       }
     } else if (MODE == kReqFinish && guard == 0) {
       for (int j = tid; j < nt; j += kPassNT) {
-        rbuf[j] = pa.E[o + j];
-        rbuf[nt + j] = pa.P[o + j];
-        rbuf[2 * nt + j] = pa.Q[o + j];
+        const bool mine = j == tid;
+        rbuf[j] = mine ? pf[0] : pa.E[o + j];
+        rbuf[nt + j] = mine ? pf[1] : pa.P[o + j];
+        rbuf[2 * nt + j] = mine ? pf[2] : pa.Q[o + j];
       }
     } else {
       const bool draft = n < g;
