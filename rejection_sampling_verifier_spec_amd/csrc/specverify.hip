@@ -3399,11 +3399,11 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     }
   };
   auto flush = [&](int jj) {
-    const double te = wave_sum_d(es);
+    const double te = wave_sum_d_dpp(es);
     double tp = 0.0, tq = 0.0;
     if (draft) {
-      tp = wave_sum_d(ps);
-      tq = wave_sum_d(qs);
+      tp = wave_sum_d_dpp(ps);
+      tq = wave_sum_d_dpp(qs);
     }
     const bool tu = und != 0;
     if (lane == 0) {
