@@ -359,15 +359,15 @@ __device__ double block_sum(double v, BlockScratchT<NT>& s) {
   return r;
 }
 
-// Two fixed-order block sums with one pair of barriers.
+__device__ __forceinline__ double wave_sum_d_dpp(double v);
+
+// Two fixed-order block sums with one pair of barriers (DPP wave sums, then
+// the waves' sums in order).
 template <int NT>
 __device__ void block_sum2(double v, double w, BlockScratchT<NT>& s, double& rv, double& rw) {
   constexpr int kWaves = NT / 64;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    v += __shfl_xor(v, o);
-    w += __shfl_xor(w, o);
-  }
+  v = wave_sum_d_dpp(v);
+  w = wave_sum_d_dpp(w);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     s.d[wave] = v;
@@ -2957,7 +2957,7 @@ __device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, Bl
   __syncthreads();
   double zl = 0.0;
   for (int q = tid; q < nt; q += NT) zl += E[q];
-  const double Z = block_sum<NT>(zl, sc);
+  const double Z = block_sum_dpp<NT>(zl, sc);
   if (Z > 0.0 && Z < INFINITY) {
   if (tid == 0) {
     int accepted = 0;
