@@ -498,6 +498,18 @@ __device__ double block_sum_dpp(double v, BlockScratchT<NT>& s) {
   return r;
 }
 
+// Inclusive integer scan over the 64 lanes by DPP (as wave_scan_incl_d_dpp).
+__device__ __forceinline__ int wave_scan_incl_i_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  const int lane = threadIdx.x & 63;
+  return v + (lane < 16 ? 0 : lane < 32 ? t0 : lane < 48 ? t0 + t1 : t0 + t1 + t2);
+}
+
 // Inclusive scan over the 64 lanes (lane order), fixed association.
 __device__ __forceinline__ double wave_scan_incl_d(double v) {
   const int lane = threadIdx.x & 63;
@@ -2644,12 +2656,7 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
       }
     }
     // offsets: exclusive scan of the counts over the block (lanes, then waves)
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
+    const int incl = wave_scan_incl_i_dpp(cnt);
     if (lane == 63) sh.wcount[wave] = incl;
     __syncthreads();
     int off = base + incl - cnt;
@@ -2700,12 +2707,7 @@ __device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
       }
     }
     // offsets: exclusive scan of the counts over the block (lanes, then waves)
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
+    const int incl = wave_scan_incl_i_dpp(cnt);
     if (lane == 63) sh.wcount[wave] = incl;
     __syncthreads();
     int off = base + incl - cnt;
@@ -3320,7 +3322,6 @@ struct ReqSharedT {
     double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see finish_row)
     double memo[MEMO ? kMemoN : kTile];
   };
-  int first;    // first row not yet accepted
   int nund;     // tiles with undecided elements
   int cross, lastpos;
   int tile;
@@ -3450,17 +3451,17 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
 }
 
 // The request's first row >= start whose own accept test did not pass (g if
-// none), found by the whole block; uniform (scalar) on return.
+// none), found by every wave alike (a ballot over 64 rows at a time: no LDS,
+// no barrier); uniform on return.
 template <int NT>
-__device__ __forceinline__ int first_open_row(const int2* __restrict__ ws, int64_t t0, int start, int g, int* slot) {
-  if (threadIdx.x == 0) *slot = g;
-  __syncthreads();
-  for (int i = start + static_cast<int>(threadIdx.x); i < g; i += NT)
-    if (!(static_cast<uint32_t>(ws[t0 + i].y) & kRowAccepted)) atomicMin(slot, i);
-  __syncthreads();
-  const int n = __builtin_amdgcn_readfirstlane(*slot);
-  __syncthreads();
-  return n;
+__device__ __forceinline__ int first_open_row(const int2* __restrict__ ws, int64_t t0, int start, int g) {
+  const int lane = threadIdx.x & 63;
+  for (int i0 = start; i0 < g; i0 += 64) {
+    const int i = i0 + lane;
+    const uint64_t open = __ballot(i < g && !(static_cast<uint32_t>(ws[t0 + i].y) & kRowAccepted));
+    if (open) return i0 + __ffsll(static_cast<unsigned long long>(open)) - 1;
+  }
+  return g;
 }
 
 __device__ __forceinline__ bool request_range(const ProbsArgs& a, int b, int& d0, int& d1) {
@@ -3782,7 +3783,8 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
     pf[2] = pa.Q[o + tid];
   }
   exp2_table_init(tab);
-  int n = first_open_row<kPassNT>(a.ws, t0, 0, g, &rs.first);  // (its barriers also publish tab)
+  __syncthreads();  // (publishes tab)
+  int n = first_open_row<kPassNT>(a.ws, t0, 0, g);
   const Exp2Consts C = exp2_consts_load();
   for (int guard = 0; guard <= g; ++guard) {  // at most g + 1 rows are taken
     const int64_t trow = t0 + n;
@@ -3826,7 +3828,7 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
     if constexpr (MODE != kReqPass) {
       __syncthreads();
       if (!finish_row<LT, VEC, FILTER>(a, sel, b, d0, d1, n, rbuf, sc, rs, tab, C)) return;
-      n = first_open_row<kPassNT>(a.ws, t0, n + 1, g, &rs.first);
+      n = first_open_row<kPassNT>(a.ws, t0, n + 1, g);
     }
   }
 }
