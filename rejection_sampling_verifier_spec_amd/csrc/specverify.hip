@@ -3312,16 +3312,11 @@ __device__ __forceinline__ bool base_partial(int j, int nt, int V) { return j ==
 constexpr int kPassNT = 256;       // threads per block of the per-request kernel
 constexpr int kPassWaves = kPassNT / 64;
 
-// The memo and the finish's crossing-tile weights are never live together
-// (the pass ends at a barrier before the finish, and every pass rebuilds the
-// memo), so they share the LDS.
+// Shared state of the per-request kernel; the memo only with bf16 logits.
 template <bool MEMO>
 struct ReqSharedT {
-  double part[4];  // per-wave partial sums (an undecided tile)
-  union {
-    double wbuf[kTile];  // the crossing tile's weights, scan-lane-major (see finish_row)
-    double memo[MEMO ? kMemoN : kTile];
-  };
+  double part[4];  // per-wave partial sums (an undecided tile; the in-tile scan's wave totals)
+  double memo[MEMO ? kMemoN : 1];
   int nund;     // tiles with undecided elements
   int cross, lastpos;
   int tile;
@@ -3653,20 +3648,20 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
         if (j < jt) pl += tile_val(j);
       pb = wave_sum_d_dpp(pl);
     }
-    // in-tile search: scan lane l (of wave 0) owns the 32 consecutive elements
-    // jt*kTile + 32 l + (0..31). The four waves compute the tile's weights
-    // once, lane (w, l') the 8 elements of scan lane 16 w + l' / 4 from
-    // 8 (l' % 4), into LDS (weight i of scan lane l at wbuf[i 64 + l]); wave 0
-    // then sums and scans them in token order.
+    // in-tile search: lane l of wave w computes the weights of elements
+    // jt*kTile + 8 (64 w + l) + (0..7), so the block holds the tile in token
+    // order (wave-major, then lane); each wave scans its quarter (DPP), the
+    // waves' totals are added in order, and every lane finds the crossing
+    // among its own eight (the block minimum of the lanes' finds).
+    double w8[8];
+    const int k0 = jt * kTile + 8 * (64 * wave + lane);
     {
-      const int L = 16 * wave + (lane >> 2), h = lane & 3;
-      const int kc = jt * kTile + 32 * L + 8 * h;
       float lv[8], qv[8];
-      load8f<LT, VEC>(lrow, V, kc, lv);
-      load8qf<VEC>(mode == 1 ? qrow : nullptr, V, kc, qv);
+      load8f<LT, VEC>(lrow, V, k0, lv);
+      load8qf<VEC>(mode == 1 ? qrow : nullptr, V, k0, qv);
       if (mode == 1 && onehot) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qv[k] = kc + k == hot ? 1.f : 0.f;
+        for (int k = 0; k < 8; ++k) qv[k] = k0 + k == hot ? 1.f : 0.f;
       }
 #pragma unroll
       for (int g4 = 0; g4 < 8; g4 += kExpW) {
@@ -3677,40 +3672,43 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
 #pragma unroll
         for (int k = 0; k < kExpW; ++k) {
           const double p = e[k] * iz;
-          rs.wbuf[(8 * h + g4 + k) * 64 + L] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[g4 + k])) : p;
+          w8[g4 + k] = mode == 1 ? fmax(0.0, p - static_cast<double>(qv[g4 + k])) : p;
         }
       }
+    }
+    double s8 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s8 += w8[k];
+    const double lincl = wave_scan_incl_d_dpp(s8);
+    if (lane == 63) rs.part[wave] = lincl;
+    if (tid == 0) {
+      rs.cross = 0x7fffffff;
+      rs.lastpos = -1;
+    }
+    __syncthreads();
+    double c = 0.0;
+    for (int w = 0; w < wave; ++w) c += rs.part[w];
+    c += lincl - s8;
+    const double tl = tau - pb;
+    {
+      int tok = -1, lastpos = -1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        c += w8[k];
+        if (w8[k] > 0.0) {
+          lastpos = k0 + k;
+          if (tok < 0 && c >= tl) tok = k0 + k;
+        }
+      }
+      const uint64_t hit = __ballot(tok >= 0);
+      if (hit && lane == __ffsll(static_cast<unsigned long long>(hit)) - 1) atomicMin(&rs.cross, tok);
+      int lp = lastpos;
+      for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+      if (lane == 0 && lp >= 0) atomicMax(&rs.lastpos, lp);
     }
     __syncthreads();
     if (wave != 0) return false;
-    const int k0 = jt * kTile + 32 * lane;
-    double ls = 0.0;
-#pragma unroll 8
-    for (int i = 0; i < 32; ++i) ls += rs.wbuf[i * 64 + lane];
-    const double lincl = wave_scan_incl_d_dpp(ls);
-    const double tl = tau - pb;
-    int tok = -1, lastpos = -1;
-    {
-      double c = lincl - ls;
-#pragma unroll 8
-      for (int i = 0; i < 32; ++i) {
-        const double w = rs.wbuf[i * 64 + lane];
-        c += w;
-        if (w > 0.0) {
-          lastpos = k0 + i;
-          if (tok < 0 && c >= tl) tok = k0 + i;
-        }
-      }
-    }
-    int token;
-    const uint64_t thit = __ballot(tok >= 0);
-    if (thit) {
-      token = __shfl(tok, __ffsll(static_cast<unsigned long long>(thit)) - 1);
-    } else {
-      int lp = lastpos;
-      for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
-      token = lp >= 0 ? lp : jt * kTile;
-    }
+    const int token = rs.cross != 0x7fffffff ? rs.cross : (rs.lastpos >= 0 ? rs.lastpos : jt * kTile);
     // ---- outputs of the request
     for (int i = lane; i <= g; i += 64) {
       int64_t o = -1;
