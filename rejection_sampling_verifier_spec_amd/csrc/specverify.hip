@@ -317,10 +317,65 @@ __device__ __forceinline__ float lane_f(float v, int l) {
 // by 4 and 8 within the row; every lane ends with its row's total. The four
 // row totals are then combined in a fixed order, so every lane of the wave
 // holds the same, deterministic result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x124>(v);
+  v += dpp_i<0x128>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x124>(v));
+  v = min(v, dpp_i<0x128>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x124>(v));
+  v = max(v, dpp_i<0x128>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// 64-bit integer sums and inclusive scans (lane order) by DPP moves of the
+// two halves; integer sums are exact in any order.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(dpp_i<CTRL>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  v += dpp_u64<0xB1>(v);
+  v += dpp_u64<0x4E>(v);
+  v += dpp_u64<0x124>(v);
+  v += dpp_u64<0x128>(v);
+  return (lane_u64(v, 0) + lane_u64(v, 16)) + (lane_u64(v, 32) + lane_u64(v, 48));
+}
+__device__ __forceinline__ unsigned long long wave_scan_incl_u64(unsigned long long v) {
+  // within each 16-lane row: shifts right by 1, 2, 4, 8 (lanes before the
+  // row's start read 0), then the earlier rows' totals
+  v += dpp_u64<0x111>(v);
+  v += dpp_u64<0x112>(v);
+  v += dpp_u64<0x114>(v);
+  v += dpp_u64<0x118>(v);
+  const unsigned long long t0 = lane_u64(v, 15), t1 = lane_u64(v, 31), t2 = lane_u64(v, 47);
+  const int lane = threadIdx.x & 63;
+  return v + (lane < 16 ? 0ull : lane < 32 ? t0 : lane < 48 ? t0 + t1 : t0 + t1 + t2);
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);
@@ -1578,12 +1633,7 @@ __device__ void pick_count(FilterShared& fs, uint32_t kk) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) c[r] = fs.cnt[255 - 4 * lane - r];
   const uint32_t ls = (c[0] + c[1]) + (c[2] + c[3]);
-  uint32_t incl = ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = static_cast<uint32_t>(wave_scan_incl_i_dpp(static_cast<int>(ls)));
   const uint32_t excl = incl - ls;
   if (excl < kk && incl >= kk) {  // exactly one lane
     uint32_t cum = excl;
@@ -1618,13 +1668,10 @@ __device__ void level_take(FilterShared& fs, int t) {
       et = ev;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ma += __shfl_xor(ma, o);
-    ea += __shfl_xor(ea, o);
-    mt += __shfl_xor(mt, o);
-    et += __shfl_xor(et, o);
-  }
+  ma = wave_sum_u64(ma);
+  ea = wave_sum_u64(ea);
+  mt = wave_sum_u64(mt);
+  et = wave_sum_u64(et);
   if (lane == 0) {
     fs.m_above = ma;
     fs.e_above = ea;
@@ -1894,8 +1941,7 @@ __device__ int gather_head(const LT* __restrict__ lrow, int V, const float (&cut
   int ok_from = kRungs;  // first rung that fits this wave
 #pragma unroll
   for (int i = kRungs - 1; i >= 0; --i) {
-    int c = cnt[i];
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    const int c = wave_sum_i(cnt[i]);
     if (c <= kSlice && ok_from == i + 1) ok_from = i;
   }
   if (lane == 0) fs.wcnt[wave] = ok_from;
@@ -1986,12 +2032,7 @@ __device__ void pick_head_mass(FilterShared& fs, double C, double tlo, double th
     mv[r] = fs.mass[255 - 4 * lane - r];
     ls += mv[r];
   }
-  unsigned long long im = ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(im, o);
-    if (lane >= o) im += y;
-  }
+  const unsigned long long im = wave_scan_incl_u64(ls);
   unsigned long long cm = im - ls;
   int hat = 256, und = 256;
 #pragma unroll
@@ -2002,11 +2043,8 @@ __device__ void pick_head_mass(FilterShared& fs, double C, double tlo, double th
     if (v >= thi) hat = min(hat, t);
     else if (v >= tlo) und = min(und, t);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    hat = min(hat, __shfl_xor(hat, o));
-    und = min(und, __shfl_xor(und, o));
-  }
+  hat = wave_min_i(hat);
+  und = wave_min_i(und);
   if (lane == 0) fs.pos = (und < hat || hat >= 256) ? -1 : hat;
 }
 
@@ -2055,7 +2093,7 @@ __device__ bool decide_head(const ProbsArgs& a, const LT* __restrict__ lrow, flo
   unsigned long long zpart = 0;
   for (int i = tid; i < n; i += NT)
     if (fs.head[i] >= klo) zpart += fs.hfix[i];
-  for (int o = 32; o > 0; o >>= 1) zpart += __shfl_xor(zpart, o);
+  zpart = wave_sum_u64(zpart);
   if ((tid & 63) == 0) fs.m_at = 0;
   __syncthreads();
   if ((tid & 63) == 0) atomicAdd(&fs.m_at, zpart);
@@ -3639,8 +3677,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
       jt = __shfl(jt, src);
       pb = __shfl(pb, src);
     } else {
-      int jl = jlast;
-      for (int o = 32; o > 0; o >>= 1) jl = max(jl, __shfl_xor(jl, o));
+      const int jl = wave_max_i(jlast);
       jt = jl >= 0 ? jl : 0;
       // prefix before the last positive tile
       double pl = 0.0;
@@ -3702,8 +3739,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
       }
       const uint64_t hit = __ballot(tok >= 0);
       if (hit && lane == __ffsll(static_cast<unsigned long long>(hit)) - 1) atomicMin(&rs.cross, tok);
-      int lp = lastpos;
-      for (int o = 32; o > 0; o >>= 1) lp = max(lp, __shfl_xor(lp, o));
+      const int lp = wave_max_i(lastpos);
       if (lane == 0 && lp >= 0) atomicMax(&rs.lastpos, lp);
     }
     __syncthreads();
