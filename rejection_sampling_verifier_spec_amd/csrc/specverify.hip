@@ -3370,11 +3370,11 @@ struct ReqSharedT {
 // P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
 // interval leaves an element undecided (LDS or global, indexed by tile). With
 // MASK, logits below tau (outside the top-k / top-p kept set) count as -inf.
-template <typename LT, bool VEC, bool MASK>
+template <typename LT, bool VEC, bool MASK, bool SPLIT = false>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
                               const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
-                              float tau, double* memo) {
+                              float tau, double* memo, double (*cpart)[4][3] = nullptr, int (*cund)[4] = nullptr) {
   constexpr bool MEMO = kMemo<LT, VEC>;
   const int lane = threadIdx.x & 63;
   const double nms = -(m * s);  // e_k = 2^(l_k s - m s): the common rounding of m s cancels in p
@@ -3448,6 +3448,57 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     es = ps = qs = 0.0;
     und = 0;
   };
+  if constexpr (SPLIT) {
+    // a slice of fewer tiles than waves (at most 3): wave w takes chunk w of
+    // each of the slice's tiles [j0, j1), all loads at once; the tiles' sums
+    // are the four waves' partial sums added in wave order
+    const int w = threadIdx.x >> 6, nl = j1 - j0;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      if (t < nl) load(t, j0 + t, w);
+    if constexpr (MEMO) {
+      memo_build<kPassNT, MASK>(memo, s, nms, tau, tab, C);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t < nl) {
+        if (base_partial(j0 + t, nt, V)) compute(t, std::true_type{});
+        else compute(t, std::false_type{});
+        const double te = wave_sum_d_dpp(es);
+        double tp = 0.0, tq = 0.0;
+        if (draft) {
+          tp = wave_sum_d_dpp(ps);
+          tq = wave_sum_d_dpp(qs);
+        }
+        if (lane == 0) {
+          cpart[t][w][0] = te;
+          cpart[t][w][1] = tp;
+          cpart[t][w][2] = tq;
+          cund[t][w] = und != 0 ? 1 : 0;
+        }
+        es = ps = qs = 0.0;
+        und = 0;
+      }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < nl) {
+      double te = 0.0, tp = 0.0, tq = 0.0;
+      int tu = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        te += cpart[t][v][0];
+        tp += cpart[t][v][1];
+        tq += cpart[t][v][2];
+        tu |= cund[t][v];
+      }
+      E[j0 + t] = te;
+      P[j0 + t] = tu ? -1.0 : tp;
+      Q[j0 + t] = tq;
+    }
+    return;
+  }
   int j = j0;
   if constexpr (MEMO) {
     // the first loads go out before the memo is built (every thread of the
@@ -3766,19 +3817,26 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
 // certified Z interval [zlo, zhi] of the per-row pass already decides: P_j
 // and Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
 // every Z in the interval (P_j = -1: an element left undecided) - then
-// finish_row. One kernel template, three ways to launch it:
+// finish_row. One kernel template, four ways to launch it:
 //   kReqFused:  one block per request does the whole row into LDS and the
 //               finish (when the requests alone fill the chip's block slots);
 //   kReqPass:   `slices` blocks per request, each a slice of the row's tiles,
 //               the sums to device memory (plain stores: the finish is a
 //               launch of its own);
-//   kReqFinish: one block per request reads the sums into LDS and finishes.
+//   kReqFinish: one block per request reads the sums into LDS and finishes;
+//   kReqPassSplit: as kReqPass for slices of fewer tiles than the block's
+//               waves (small batches): each tile's chunks spread over the
+//               waves, their sums added in wave order.
 // A later open row (an undecided accept test that turned out accepted, rare)
 // gets its whole pass from the finishing block alone, in LDS.
 // HASQ = false (one-hot drafts, no q rows): every deciding row needs only its
 // tile sums of e, and the kernel is built without the residual's per-element
 // work (fewer registers, more waves per SIMD).
-enum RequestMode { kReqFused = 0, kReqPass = 1, kReqFinish = 2 };
+enum RequestMode { kReqFused = 0, kReqPass = 1, kReqFinish = 2, kReqPassSplit = 3 };
+// dynamic LDS of kReqPassSplit: per tile (at most 3) and wave, E, P, Q, then
+// whether the wave's chunk left an element undecided
+constexpr int kSplitParts = 3 * kPassWaves * 3;
+constexpr size_t kSplitLds = kSplitParts * sizeof(double) + 3 * kPassWaves * sizeof(int);
 
 // Blocks of the per-request kernel resident per compute unit, the register
 // budget its pass builds are held to: three with bf16 logits and q rows (at
@@ -3792,17 +3850,18 @@ constexpr int request_blocks_per_cu() {
 template <typename LT, bool VEC, bool FILTER, bool HASQ, int MODE>
 __global__ __launch_bounds__(kPassNT, (MODE == kReqFinish ? 1 : request_blocks_per_cu<LT, VEC, HASQ>())) void
 request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
+  constexpr bool kSlicePass = MODE == kReqPass || MODE == kReqPassSplit;
   extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
   __shared__ BlockScratchT<kPassNT> sc;
   __shared__ ReqSharedT<kMemo<LT, VEC>> rs;
   __shared__ double tab[kExp2Tab];
-  const int b = MODE == kReqPass ? blockIdx.x / slices : blockIdx.x;
-  const int sl = MODE == kReqPass ? blockIdx.x % slices : 0;
+  const int b = kSlicePass ? blockIdx.x / slices : blockIdx.x;
+  const int sl = kSlicePass ? blockIdx.x % slices : 0;
   const int V = a.V, nt = (V + kTile - 1) / kTile;
   const int tid = threadIdx.x, wave = tid >> 6;
   int d0, d1;
   if (!request_range(a, b, d0, d1)) {
-    if (MODE != kReqPass && tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
+    if (!kSlicePass && tid == 0) sel.nacc[b] = 0;  // invalid offsets: nothing emitted
     return;
   }
   const int g = d1 - d0;
@@ -3825,7 +3884,7 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
     if (static_cast<uint32_t>(a.ws[trow].y) & kRowTileSums) {
       // one-hot drafts with bf16 logits: the per-row pass kept the row's fp64
       // tile sums (relative to the m it recorded); no q, so P and Q are 0
-      if constexpr (MODE == kReqPass) return;
+      if constexpr (kSlicePass) return;
       const double* src = a.rsum + trow * static_cast<int64_t>(nt);
       for (int j = tid; j < nt; j += kPassNT) {
         rbuf[j] = src[j];
@@ -3846,12 +3905,19 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
       const LT* __restrict__ lrow = static_cast<const LT*>(a.logits) + trow * static_cast<int64_t>(V);
       const float* __restrict__ qrow =
           (HASQ && draft && a.q) ? a.q + static_cast<int64_t>(d0 + n) * V : nullptr;
-      if constexpr (MODE == kReqPass) {
+      if constexpr (kSlicePass) {
         const int per = (nt + slices - 1) / slices;
         const int j0 = min(nt, sl * per), j1 = min(nt, j0 + per);
-        fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
-                                       kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o, static_cast<float>(st.w),
-                                       rs.memo);
+        if constexpr (MODE == kReqPassSplit)  // (the host launches it when per < kPassWaves)
+          fp64_row_pass<LT, VEC, FILTER, true>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0,
+                                               min(j1, j0 + kPassWaves - 1), kPassWaves, tab, C, pa.E + o,
+                                               pa.P + o, pa.Q + o, static_cast<float>(st.w), rs.memo,
+                                               reinterpret_cast<double(*)[4][3]>(rbuf),
+                                               reinterpret_cast<int(*)[4]>(rbuf + kSplitParts));
+        else
+          fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0 + wave, j1,
+                                         kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o,
+                                         static_cast<float>(st.w), rs.memo);
         return;
       } else {
         fp64_row_pass<LT, VEC, FILTER>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, wave, nt,
@@ -3859,7 +3925,7 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
                                        rs.memo);
       }
     }
-    if constexpr (MODE != kReqPass) {
+    if constexpr (!kSlicePass) {
       __syncthreads();
       if (!finish_row<LT, VEC, FILTER>(a, sel, b, d0, d1, n, rbuf, sc, rs, tab, C)) return;
       n = first_open_row<kPassNT>(a.ws, t0, n + 1, g);
@@ -4189,9 +4255,14 @@ void launch_request_modes(const ProbsArgs& a, const SelectArgs& sel, const PassA
                        dim3(kPassNT), lds2, st, a, sel, pa, 1);
     return;
   }
-  hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPass>),
-                     dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), 0, st, a, sel, pa,
-                     sl);
+  if ((nt + sl - 1) / sl < kPassWaves)  // slices of fewer tiles than waves
+    hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPassSplit>),
+                       dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), kSplitLds, st, a,
+                       sel, pa, sl);
+  else
+    hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPass>),
+                       dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), 0, st, a, sel,
+                       pa, sl);
   hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqFinish>), dim3(static_cast<unsigned>(a.B)),
                      dim3(kPassNT), lds2, st, a, sel, pa, 1);
 }
