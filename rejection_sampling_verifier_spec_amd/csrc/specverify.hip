@@ -719,10 +719,12 @@ struct ProbsArgs {
   int* surv_n;    // lazy mode: [0] the task count, [16] the first launch's finished-block counter
   int top_k;      // filtered lazy mode: keep the top_k largest logits (with ties); off unless 0 < top_k < V
   double top_p;   // filtered lazy mode: keep the smallest top set of mass >= top_p; off when >= 1
+  int cus;        // the device's compute units
 };
 
 struct RowShared {
   int skip;        // lazy mode: an earlier position of the request is a certain rejection
+  int stop;        // lazy mode, second launch: that became known while the row was read
   int last;        // lazy mode: this block is the last of the first launch to finish
   int mark_old;    // lazy mode: the values this block's mark atomics returned (stored to wait for them)
   int2 qtask;      // lazy mode, self-listed second launch: this block's {request, position}, or {-1, 0}
@@ -2347,10 +2349,18 @@ __device__ void row_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
 // (RET_MARK), or 0: the caller consumes it later, so that the atomic's round
 // trip overlaps the rest of the row's work. Without RET_MARK the raise returns
 // nothing and the block never waits for it.
-template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false, bool RET_MARK = false>
+//
+// STOP (the second launch of the lazy mode) with stop_on, for a row after
+// its request's first position: the row stops as soon as an earlier
+// position of its request is known to be a certain rejection (its mark
+// raised during this launch; the first launch cleared the marks before),
+// and is recorded as not read.
+template <typename LT, bool VEC, int NT, bool EAGER, bool FILTER = false, bool RET_MARK = false, bool STOP = false>
 __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, float* dyn, BlockScratchT<NT>& sc,
                                          RowShared& sh,
-                                         std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr) {
+                                         std::conditional_t<FILTER, FilterShared, NoFilterShared>* fsp = nullptr,
+                                         bool stop_on = false) {
+  const bool can_stop = STOP && stop_on && t.i > 0;
   static_assert(!(EAGER && FILTER), "top-k / top-p run in the lazy mode only");
   constexpr int kWaves = NT / 64;
   using L = Lay<LT, VEC>;
@@ -2487,6 +2497,7 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     } else if (lane == 0) {
       sh.wmax[wave] = -INFINITY;
     }
+    if (STOP && tid == 0) sh.stop = 0;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ref = fmaxf(ref, sh.wmax[w]);
@@ -2494,18 +2505,31 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
       cut1 = ref - kHeadH1 / s;
       cut2 = cut1 - kCount2 / s;
     }
+    // (can_stop) each wave loads the request's mark at every step (one
+    // request for the wave) and tests the value it loaded the step before,
+    // whose round trip the step's tile overlapped
+    int mk = 0;
+    bool halted = false;
+    auto stopped = [&]() {
+      halted = __builtin_amdgcn_readfirstlane(mk) > kMarkBase - t.i;
+      mk = __hip_atomic_load(a.mark + t.b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return halted;
+    };
     if (j < nt) {
       while (true) {
         rb.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
         tile1(ra, j);
         j += kWaves;
         if (j >= nt) break;
+        if (can_stop && stopped()) break;
         ra.load(lrow, V, min(j + kWaves, nt - 1) * kTile, lane);
         tile1(rb, j);
         j += kWaves;
         if (j >= nt) break;
+        if (can_stop && stopped()) break;
       }
     }
+    if (can_stop && halted && lane == 0) sh.stop = 1;
     // the wave's final reference is the largest M_j of its tiles (every raise
     // sets it to the raising tile's M_j); a wave without tiles holds the block
     // maximum of the first tiles
@@ -2522,6 +2546,10 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     }
   }
   __syncthreads();
+  if (can_stop && sh.stop) {  // (uniform: no wave writes it after the barrier)
+    if (tid == 0) a.ws[t.trow] = make_int2(-1, static_cast<int>(kRowUnread));
+    return 0;
+  }
 
   // Row max m, c_m = fl(-m s) and Z = sum_j S_j exp2(c_m - c_j) in e-units.
   // The c_j cancel exactly, so Z approximates 2^D sum_k 2^((l_k - m) s) with
@@ -2714,7 +2742,7 @@ __device__ void list_survivors(const ProbsArgs& a, int p1, RowShared& sh) {
 // request (b mod the grid). Raises made in this launch (positions >= p1)
 // never change a request's survival, so any value a block reads agrees.
 template <int NT>
-__device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
+__device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh, int& ntask) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kW = NT / 64;
   const int k = blockIdx.x;
@@ -2754,6 +2782,7 @@ __device__ Task self_listed_task(const ProbsArgs& a, int p1, RowShared& sh) {
     for (int w = 0; w < kW; ++w) base += sh.wcount[w];
     __syncthreads();
   }
+  ntask = base;
   const int2 e = sh.qtask;
   if (e.x < 0) {
     Task t;
@@ -3034,7 +3063,7 @@ __device__ int onehot_memo_row(const ProbsArgs& a, const Task& t, float* dyn, Bl
 
 // (FILTER: at least four waves per SIMD, two blocks per CU as without it;
 // the rare radix-select path of the threshold may then spill)
-template <typename LT, bool VEC, int NT, bool FILTER, bool LIST, bool ONEHOT = false>
+template <typename LT, bool VEC, int NT, bool FILTER, bool LIST, bool ONEHOT = false, bool STOP = false>
 __global__ __launch_bounds__(NT, (FILTER || ONEHOT) ? 4 : 1) void lazy_rows_kernel(ProbsArgs a, int p1, int phase) {
   // phase 0: first launch, alone; 1: first launch, a second follows (its last
   // block lists the tasks); 2: second launch, from that list; 3: first
@@ -3052,8 +3081,9 @@ __global__ __launch_bounds__(NT, (FILTER || ONEHOT) ? 4 : 1) void lazy_rows_kern
   __shared__ std::conditional_t<FILTER, FilterShared, NoFilterShared> fsh;
   const bool second = phase == 2 || phase == 4;
   Task t;
+  int ntask = 0;  // (second launch) rows it holds
   if constexpr (!FILTER) {
-    if (phase == 4) t = self_listed_task<NT>(a, p1, sh);
+    if (phase == 4) t = self_listed_task<NT>(a, p1, sh, ntask);
   }
   if (FILTER || phase != 4)
     t = decode_task_lazy(blockIdx.x, a.cu, a.B, a.gamma, a.ndraft, phase == 2 ? a.tasks : nullptr,
@@ -3101,7 +3131,13 @@ __global__ __launch_bounds__(NT, (FILTER || ONEHOT) ? 4 : 1) void lazy_rows_kern
   }
   if (read) {
     if constexpr (ONEHOT) mark_ret ^= onehot_memo_row<NT, LIST>(a, t, dyn, sc, sh, memo_s, tab_s);
-    else mark_ret ^= probs_row<LT, VEC, NT, false, FILTER, LIST>(a, t, dyn, sc, sh, &fsh);
+    else {
+      // (rows stop early only when the launch holds more rows than the chip
+      // has compute units: then some units run two, and a row found
+      // unneeded would otherwise set the launch's end)
+      if (STOP && phase == 2) ntask = a.surv_n[0];
+      mark_ret ^= probs_row<LT, VEC, NT, false, FILTER, LIST, STOP>(a, t, dyn, sc, sh, &fsh, ntask > a.cus);
+    }
   }
   if (!LIST || phase != 1) return;
   if (threadIdx.x == 0) sh.mark_old = mark_ret;  // waits for this thread's mark atomics
@@ -4216,9 +4252,9 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false>), dim3(static_cast<unsigned>(a.B) * split),
                          dim3(NT), lds, st, a, split, phase1);
     prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
-    if (rest > 0)
-      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false>), dim3(static_cast<unsigned>(rest)), dim3(NT),
-                         lds, st, a, split, self ? 4 : 2);
+    if (rest > 0)  // (rows that stop when an earlier position turns out a certain rejection)
+      hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false, false, !FILTER>),
+                         dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st, a, split, self ? 4 : 2);
   }
 }
 
@@ -4398,6 +4434,7 @@ int verify_common(const void* logits, int dtype, const float* q, const int64_t* 
     p.surv_n = reinterpret_cast<int*>(wsb + wl.count + 128);
 
     p.pm = cu ? kRaggedFirstMax : gamma + 1;
+    p.cus = device_cus();
     p.xcount = xcount;
     p.xlist = reinterpret_cast<ExactEntry*>(wsb + wl.list);
     p.xdone = reinterpret_cast<int*>(wsb + wl.done);
