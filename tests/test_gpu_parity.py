@@ -73,13 +73,19 @@ def test_peaked_bf16_full_every_request(seed):
     gpu = gh.run_gpu(w)
     gh.compare_all(w, gpu, label=f"peaked full s{seed}")
     # properties at full size: accepted prefix equals the drafts, padding, ranges
-    out, nacc, _, _ = gpu
+    out, nacc, _, rec = gpu
     g = w["gamma"]
+    flags = rec[:, 1].reshape(w["B"], g + 1)
     for b in range(w["B"]):
         n = int(nacc[b])
         assert 0 <= n <= g
         assert np.array_equal(out[b, :n], w["draft_tokens"][b, :n])
         assert 0 <= out[b, n] < w["V"] and np.all(out[b, n + 1:] == -1)
+        # rows not read (skipped, or stopped mid-row in the second launch,
+        # which at this size holds more rows than the chip has compute
+        # units) lie after the request's deciding row; rows up to it were read
+        unread = np.nonzero(flags[b] & api.SV_ROW_UNREAD)[0]
+        assert len(unread) == 0 or unread.min() > n
 
 
 @pytest.mark.parametrize("seed", SEEDS)
