@@ -3437,19 +3437,20 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
         exp2_negN<kExpW>(ar, tab, C, e);
       };
       if constexpr (MEMO) {
-        if constexpr (!PD) {
-          static_assert(kExpW == 4, "the memo lookup takes two words of two bf16 values");
-          uint32_t miss = 0;
-          const uint32_t i01 = memo_index2(ring[slot].word(h >> 1), miss);
-          const uint32_t i23 = memo_index2(ring[slot].word((h >> 1) + 1), miss);
-          e[0] = memo[i01 & 0xffffu];
-          e[1] = memo[i01 >> 16];
-          e[2] = memo[i23 & 0xffffu];
-          e[3] = memo[i23 >> 16];
-          if (__builtin_amdgcn_ballot_w64((miss & 0xf800f800u) != 0u)) direct();  // rare; same values elsewhere
-        } else {
-          direct();
-        }
+        static_assert(kExpW == 4, "the memo lookup takes two words of two bf16 values");
+        uint32_t miss = 0;
+        const uint32_t i01 = memo_index2(ring[slot].word(h >> 1), miss);
+        const uint32_t i23 = memo_index2(ring[slot].word((h >> 1) + 1), miss);
+        // (the row's last tile: bf16 rows hold a multiple of 8 values, so a
+        // lane's chunk lies wholly inside the row or wholly past its end;
+        // one past the end adds nothing and misses nothing)
+        const bool in = !PD || ring[slot].i0 < V;
+        if (!in) miss = 0;
+        e[0] = in ? memo[i01 & 0xffffu] : 0.0;
+        e[1] = in ? memo[i01 >> 16] : 0.0;
+        e[2] = in ? memo[i23 & 0xffffu] : 0.0;
+        e[3] = in ? memo[i23 >> 16] : 0.0;
+        if (__builtin_amdgcn_ballot_w64((miss & 0xf800f800u) != 0u)) direct();  // rare; same values elsewhere
       } else {
         direct();
       }
