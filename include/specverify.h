@@ -112,8 +112,9 @@ enum sv_status {
 #define SV_ROW_DEFERRED 0x400u     /* lazy mode: rejected (or bonus) row whose token was not needed (not drawn) */
 #define SV_ROW_UNDECIDED 0x800u    /* lazy mode: accept test left to the per-request fp64 pass, which did not
                                       need this row (an earlier row was rejected) */
-#define SV_ROW_UNREAD 0x1000u      /* lazy mode: row after a position already known to be a certain
-                                      rejection: not needed, its logits were not read */
+#define SV_ROW_UNREAD 0x1000u      /* lazy mode: row after a position known to be a certain rejection: not
+                                      needed, its logits not read (or not read to the end: a row of the
+                                      second per-row launch stops once that becomes known) */
 /* top-k / top-p (the *_filtered entry points): how the row's threshold was
  * found when the head gathered during the first pass over the row (its
  * largest logits) could not decide it: */
