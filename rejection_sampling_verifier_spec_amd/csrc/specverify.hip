@@ -1539,9 +1539,9 @@ constexpr float kHeadH1 = 12.f;
 constexpr int kHeadFix = 50;  // fraction bits of the head masses: kHeadCap terms <= 1 stay below 2^63
 constexpr int kRungs = 4;
 __constant__ float kRungBelow[kRungs] = {48.f, 32.f, 16.f, 8.f};
-// pass 1 also counts, per wave, the elements at or above c2 = c1 - kCount2 / s:
-// with top-k on and pass 1's head too small, a second head at c2 that fits
-// and holds k elements is gathered in one sweep (no count sweep)
+// with top-k on and pass 1's head too small, a second head at
+// c2 = c1 - kCount2 / s is gathered in one sweep (it holds the top-k set
+// when it holds k elements; an overflow of its slices falls to the rungs)
 constexpr float kCount2 = 8.f;
 __constant__ float kRungAbove[kRungs] = {0.25f, 0.5f, 0.75f, 1.f};
 
@@ -1557,9 +1557,8 @@ struct FilterShared {
   uint32_t head[kHeadCap];              // keys of the head elements
   unsigned long long hfix[kHeadCap];    // their masses 2^((l - m) s64) as fixed point (kHeadFix bits)
   int wcnt[16];                         // per-wave counts
-  int wcnt2[16];                        // pass 1: per-wave counts of the elements >= cut2
   float cut1;                           // pass 1's head cutoff
-  float cut2;                           // pass 1's counted cutoff (cut1 - kCount2 / s)
+  float cut2;                           // the second head's cutoff (cut1 - kCount2 / s)
   int ik, ip;                           // head indices: end of tau_k's tie group, top-p crossing
   int amb;                              // top-p: first tie-group end within the bound of the target
   double zk;                            // exact Z_K (head sum) when top-k is on
@@ -1824,28 +1823,16 @@ __device__ __forceinline__ void head_append_wave(const RawTile<LT, VEC>& r, int 
   }
 }
 
-// head_append_wave for pass 1, which also counts in `cnt2` (the wave's
-// count: ballots counted on the scalar unit) the in-row elements at or above
-// c2 < c; groups of 8 slots (their per-lane maxima gm, from the tile's
-// maximum) without an element at or above c2 are skipped, and the appends
-// run only in groups that hold one at or above c.
+// head_append_wave for pass 1: groups of 8 slots (their per-lane maxima gm)
+// without an element at or above c are skipped.
 template <typename LT, bool VEC>
-__device__ __forceinline__ void head_append_count_wave(const RawTile<LT, VEC>& r, const float (&gm)[kLaneElems / 8],
-                                                       int base, int V, int lane, float c, float c2, uint32_t* dst,
-                                                       int slice, int& cnt, int& cnt2) {
+__device__ __forceinline__ void head_append_groups_wave(const RawTile<LT, VEC>& r, const float (&gm)[kLaneElems / 8],
+                                                        int base, int V, int lane, float c, uint32_t* dst, int slice,
+                                                        int& cnt) {
   using L = Lay<LT, VEC>;
   const bool full = base + kTile <= V;  // uniform
 #pragma unroll
   for (int g = 0; g < kLaneElems; g += 8) {
-    if (!__any(gm[g / 8] >= c2)) continue;
-    if (full) {
-#pragma unroll
-      for (int k = g; k < g + 8; ++k) cnt2 += static_cast<int>(__popcll(__ballot(r.get(k) >= c2)));
-    } else {
-#pragma unroll
-      for (int k = g; k < g + 8; ++k)
-        cnt2 += static_cast<int>(__popcll(__ballot(L::index(base, lane, k) < V && r.get(k) >= c2)));
-    }
     if (!__any(gm[g / 8] >= c)) continue;
 #pragma unroll
     for (int k = g; k < g + 8; ++k) {
@@ -2167,22 +2154,12 @@ __device__ int head_threshold(const ProbsArgs& a, const LT* __restrict__ lrow, f
                                double& dZt) {
   const int n1 = compact_slices<NT>(fs);  // pass 1's slices (> kHeadCap: one overflowed)
   if (n1 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n1, fs, sc, tau, Zt, dZt)) return 1;
-  // top-k on and pass 1's head too small: the head at pass 1's counted cutoff
-  // when it fits every wave's slice and holds k elements (the top-k set, and
-  // so the top-p crossing within it, lie at or above that cutoff)
+  // top-k on and pass 1's head too small: the head at the second cutoff (when
+  // it fits every wave's slice and holds k elements, the top-k set, and so
+  // the top-p crossing within it, lie at or above that cutoff)
   if (n1 <= kHeadCap && a.top_k > 0 && a.top_k < a.V) {
-    constexpr int kSlice = kHeadCap / (NT / 64);
-    int tot = 0;
-    bool fits = true;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      fits = fits && fs.wcnt2[w] <= kSlice;
-      tot += fs.wcnt2[w];
-    }
-    if (fits && tot >= a.top_k) {
-      const int n2 = gather_at<LT, VEC, NT>(lrow, a.V, fs.cut2, fs);
-      if (n2 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt)) return 2;
-    }
+    const int n2 = gather_at<LT, VEC, NT>(lrow, a.V, fs.cut2, fs);
+    if (n2 <= kHeadCap && decide_head<LT, VEC, NT>(a, lrow, m, shift, Zp, dZp, n2, fs, sc, tau, Zt, dZt)) return 2;
   }
   // a head of its own: below pass 1's cutoff when that head was too small
   // (the crossing or the k-th element lay below it), above it when it overflowed
@@ -2425,8 +2402,6 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
   float ref = -INFINITY;
   float cut1 = -INFINITY;  // top-k / top-p: pass 1 gathers the head {l >= cut1}
   int hcnt = 0;            // (into per-wave slices, hcnt elements offered by this wave)
-  float cut2 = -INFINITY;  // and counts per wave the elements >= cut2 (hcnt2)
-  int hcnt2 = 0;
   auto tile1 = [&](const Raw& r, int j) {
     const int base = j * kTile;
     // the tile's maximum first: a tile that raises the wave's reference is
@@ -2447,9 +2422,9 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     }
     if (__any(lm > ref)) ref = fmaxf(ref, wave_max(lm));
     if constexpr (FILTER) {
-      if (__any(lm >= cut2))
-        head_append_count_wave<LT, VEC>(r, gm, base, V, lane, cut1, cut2, fsp->head + wave * (kHeadCap / kWaves),
-                                        kHeadCap / kWaves, hcnt, hcnt2);
+      if (__any(lm >= cut1))
+        head_append_groups_wave<LT, VEC>(r, gm, base, V, lane, cut1, fsp->head + wave * (kHeadCap / kWaves),
+                                         kHeadCap / kWaves, hcnt);
     }
     float es = 0.f, ea = 0.f;
     const bool special = base + kTile > V || (xmask >= base && xmask < base + kTile);  // uniform
@@ -2503,7 +2478,6 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     for (int w = 0; w < kWaves; ++w) ref = fmaxf(ref, sh.wmax[w]);
     if constexpr (FILTER) {
       cut1 = ref - kHeadH1 / s;
-      cut2 = cut1 - kCount2 / s;
     }
     // (can_stop) each wave loads the request's mark at every step (one
     // request for the wave) and tests the value it loaded the step before,
@@ -2537,11 +2511,10 @@ __device__ __forceinline__ int probs_row(const ProbsArgs& a, const Task& t, floa
     if constexpr (FILTER) {
       if (lane == 0) {
         fsp->wcnt[wave] = hcnt;
-        fsp->wcnt2[wave] = hcnt2;
       }
       if (tid == 0) {
         fsp->cut1 = cut1;
-        fsp->cut2 = cut2;
+        fsp->cut2 = cut1 - kCount2 / s;
       }
     }
   }
