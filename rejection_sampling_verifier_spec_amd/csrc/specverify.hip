@@ -4226,7 +4226,7 @@ void launch_rows(const ProbsArgs& a, int64_t rows, size_t lds, hipStream_t st) {
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false>), dim3(static_cast<unsigned>(a.B) * split),
                          dim3(NT), lds, st, a, split, phase1);
     prof_record(SV_PROFILE_ROWS_FIRST, 1, st);
-    if (rest > 0)  // (rows that stop when an earlier position turns out a certain rejection)
+    if (rest > 0)  // (without top-k / top-p, rows that stop once an earlier position is a certain rejection)
       hipLaunchKernelGGL((lazy_rows_kernel<LT, VEC, NT, FILTER, false, false, !FILTER>),
                          dim3(static_cast<unsigned>(rest)), dim3(NT), lds, st, a, split, self ? 4 : 2);
   }
