@@ -3379,7 +3379,7 @@ struct ReqSharedT {
 // P_j, with P_j = -1 (impossible otherwise) marking a tile in which the Z
 // interval leaves an element undecided (LDS or global, indexed by tile). With
 // MASK, logits below tau (outside the top-k / top-p kept set) count as -inf.
-template <typename LT, bool VEC, bool MASK, bool SPLIT = false>
+template <typename LT, bool VEC, bool MASK, bool SPLIT = false, bool TAIL = false>
 __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restrict__ qrow, int V, int nt, double m,
                               double s, double zhi, double zlo, bool draft, int j0, int j1, int step,
                               const double* __restrict__ tab, const Exp2Consts& C, double* E, double* P, double* Q,
@@ -3458,22 +3458,22 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     es = ps = qs = 0.0;
     und = 0;
   };
-  if constexpr (SPLIT) {
-    // a slice of fewer tiles than waves (at most 3): wave w takes chunk w of
-    // each of the slice's tiles [j0, j1), all loads at once; the tiles' sums
-    // are the four waves' partial sums added in wave order
-    const int w = threadIdx.x >> 6, nl = j1 - j0;
+  // chunk w (the wave) of each tile in [a0, a1), at most 3 tiles, all loads
+  // at once; the tiles' sums are the four waves' partial sums added in wave
+  // order (LDS partials, one barrier; every wave of the block takes part)
+  auto split_tiles = [&](int a0, int a1, auto build) {
+    const int w = threadIdx.x >> 6, nl = a1 - a0;
 #pragma unroll
     for (int t = 0; t < 3; ++t)
-      if (t < nl) load(t, j0 + t, w);
-    if constexpr (MEMO) {
+      if (t < nl) load(t, a0 + t, w);
+    if constexpr (MEMO && decltype(build)::value) {
       memo_build<kPassNT, MASK>(memo, s, nms, tau, tab, C);
       __syncthreads();
     }
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       if (t < nl) {
-        if (base_partial(j0 + t, nt, V)) compute(t, std::true_type{});
+        if (base_partial(a0 + t, nt, V)) compute(t, std::true_type{});
         else compute(t, std::false_type{});
         const double te = wave_sum_d_dpp(es);
         double tp = 0.0, tq = 0.0;
@@ -3503,10 +3503,52 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
         tq += cpart[t][v][2];
         tu |= cund[t][v];
       }
-      E[j0 + t] = te;
-      P[j0 + t] = tu ? -1.0 : tp;
-      Q[j0 + t] = tq;
+      E[a0 + t] = te;
+      P[a0 + t] = tu ? -1.0 : tp;
+      Q[a0 + t] = tq;
     }
+  };
+  // whole tiles j, j + stp, ... < jend of one wave (the first tile's first
+  // three chunks already loaded)
+  auto run = [&](int j, int jend, int stp) {
+    for (; j < jend; j += stp) {
+      const int jn = j + stp < jend ? j + stp : j;
+      if (base_partial(j, nt, V)) {
+        load(3, j, 3); compute(0, std::true_type{});
+        load(0, jn, 0); compute(1, std::true_type{});
+        load(1, jn, 1); compute(2, std::true_type{});
+        load(2, jn, 2); compute(3, std::true_type{});
+      } else {
+        load(3, j, 3); compute(0, std::false_type{});
+        load(0, jn, 0); compute(1, std::false_type{});
+        load(1, jn, 1); compute(2, std::false_type{});
+        load(2, jn, 2); compute(3, std::false_type{});
+      }
+      flush(j);
+    }
+  };
+  if constexpr (SPLIT) {  // a slice of fewer tiles than waves
+    split_tiles(j0, j1, std::true_type{});
+    return;
+  }
+  if constexpr (TAIL) {
+    // a slice [j0, j1): its whole rounds of four tiles one tile per wave,
+    // then the last (j1 - j0) mod 4 tiles by chunks over the four waves, so
+    // that no wave takes a tile more than the others
+    const int w = threadIdx.x >> 6;
+    const int jm = j0 + kPassWaves * ((j1 - j0) / kPassWaves);
+    const int jw = j0 + w;
+    if (jw < jm) {
+      load(0, jw, 0);
+      load(1, jw, 1);
+      load(2, jw, 2);
+    }
+    if constexpr (MEMO) {
+      memo_build<kPassNT, MASK>(memo, s, nms, tau, tab, C);
+      __syncthreads();
+    }
+    run(jw, jm, kPassWaves);
+    if (jm < j1) split_tiles(jm, j1, std::false_type{});  // (uniform)
     return;
   }
   int j = j0;
@@ -3527,21 +3569,7 @@ __device__ void fp64_row_pass(const LT* __restrict__ lrow, const float* __restri
     load(1, j, 1);
     load(2, j, 2);
   }
-  for (; j < j1; j += step) {
-    const int jn = j + step < j1 ? j + step : j;
-    if (base_partial(j, nt, V)) {
-      load(3, j, 3); compute(0, std::true_type{});
-      load(0, jn, 0); compute(1, std::true_type{});
-      load(1, jn, 1); compute(2, std::true_type{});
-      load(2, jn, 2); compute(3, std::true_type{});
-    } else {
-      load(3, j, 3); compute(0, std::false_type{});
-      load(0, jn, 0); compute(1, std::false_type{});
-      load(1, jn, 1); compute(2, std::false_type{});
-      load(2, jn, 2); compute(3, std::false_type{});
-    }
-    flush(j);
-  }
+  run(j, j1, step);
 }
 
 // The request's first row >= start whose own accept test did not pass (g if
@@ -3827,7 +3855,7 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
 // certified Z interval [zlo, zhi] of the per-row pass already decides: P_j
 // and Q_j, the sums of e_k and of q_k over the elements with e_k / Z > q_k for
 // every Z in the interval (P_j = -1: an element left undecided) - then
-// finish_row. One kernel template, four ways to launch it:
+// finish_row. One kernel template, five ways to launch it:
 //   kReqFused:  one block per request does the whole row into LDS and the
 //               finish (when the requests alone fill the chip's block slots);
 //   kReqPass:   `slices` blocks per request, each a slice of the row's tiles,
@@ -3836,13 +3864,16 @@ __device__ bool finish_row(const ProbsArgs& a, const SelectArgs& sel, int b, int
 //   kReqFinish: one block per request reads the sums into LDS and finishes;
 //   kReqPassSplit: as kReqPass for slices of fewer tiles than the block's
 //               waves (small batches): each tile's chunks spread over the
-//               waves, their sums added in wave order.
+//               waves, their sums added in wave order;
+//   kReqPassTail: as kReqPass when the slices take more than one round of
+//               the chip's block slots: the slice's last (tiles mod 4) tiles
+//               spread by chunks over the waves in the same way.
 // A later open row (an undecided accept test that turned out accepted, rare)
 // gets its whole pass from the finishing block alone, in LDS.
 // HASQ = false (one-hot drafts, no q rows): every deciding row needs only its
 // tile sums of e, and the kernel is built without the residual's per-element
 // work (fewer registers, more waves per SIMD).
-enum RequestMode { kReqFused = 0, kReqPass = 1, kReqFinish = 2, kReqPassSplit = 3 };
+enum RequestMode { kReqFused = 0, kReqPass = 1, kReqFinish = 2, kReqPassSplit = 3, kReqPassTail = 4 };
 // dynamic LDS of kReqPassSplit: per tile (at most 3) and wave, E, P, Q, then
 // whether the wave's chunk left an element undecided
 constexpr int kSplitParts = 3 * kPassWaves * 3;
@@ -3860,7 +3891,7 @@ constexpr int request_blocks_per_cu() {
 template <typename LT, bool VEC, bool FILTER, bool HASQ, int MODE>
 __global__ __launch_bounds__(kPassNT, (MODE == kReqFinish ? 1 : request_blocks_per_cu<LT, VEC, HASQ>())) void
 request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
-  constexpr bool kSlicePass = MODE == kReqPass || MODE == kReqPassSplit;
+  constexpr bool kSlicePass = MODE == kReqPass || MODE == kReqPassSplit || MODE == kReqPassTail;
   extern __shared__ double rbuf[];  // [nt] each: E_j, P_j, Q_j, W_j; then [nt] int: undecided tile list
   __shared__ BlockScratchT<kPassNT> sc;
   __shared__ ReqSharedT<kMemo<LT, VEC>> rs;
@@ -3918,7 +3949,13 @@ request_kernel(ProbsArgs a, SelectArgs sel, PassArrays pa, int slices) {
       if constexpr (kSlicePass) {
         const int per = (nt + slices - 1) / slices;
         const int j0 = min(nt, sl * per), j1 = min(nt, j0 + per);
-        if constexpr (MODE == kReqPassSplit)  // (the host launches it when per < kPassWaves)
+        if constexpr (MODE == kReqPassTail)
+          fp64_row_pass<LT, VEC, FILTER, false, true>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0,
+                                                      j1, kPassWaves, tab, C, pa.E + o, pa.P + o, pa.Q + o,
+                                                      static_cast<float>(st.w), rs.memo,
+                                                      reinterpret_cast<double(*)[4][3]>(rbuf),
+                                                      reinterpret_cast<int(*)[4]>(rbuf + kSplitParts));
+        else if constexpr (MODE == kReqPassSplit)  // (the host launches it when per < kPassWaves)
           fp64_row_pass<LT, VEC, FILTER, true>(lrow, qrow, V, nt, st.x, a.s64, zhi, zlo, qrow != nullptr, j0,
                                                min(j1, j0 + kPassWaves - 1), kPassWaves, tab, C, pa.E + o,
                                                pa.P + o, pa.Q + o, static_cast<float>(st.w), rs.memo,
@@ -4267,6 +4304,12 @@ void launch_request_modes(const ProbsArgs& a, const SelectArgs& sel, const PassA
   }
   if ((nt + sl - 1) / sl < kPassWaves)  // slices of fewer tiles than waves
     hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPassSplit>),
+                       dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), kSplitLds, st, a,
+                       sel, pa, sl);
+  else if (static_cast<int64_t>(a.B) * sl > static_cast<int64_t>(request_blocks_per_cu<LT, VEC, HASQ>()) * device_cus())
+    // more than one round of the chip's block slots: a block that ends late
+    // delays the next round's start, so no wave of it takes a tile more
+    hipLaunchKernelGGL((request_kernel<LT, VEC, FILTER, HASQ, kReqPassTail>),
                        dim3(static_cast<unsigned>(a.B) * static_cast<unsigned>(sl)), dim3(kPassNT), kSplitLds, st, a,
                        sel, pa, sl);
   else
